@@ -1,0 +1,67 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and require that
+the pin suite rejects every one of them: a dropped term, a wrong sign, index
+or operand must not survive the pins."""
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+import oracle_pins as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attention.py")
+
+MUTANTS = {
+    "diagonal-exclusive": ("visible = j[None, :] <= pos[:, None]", "visible = j[None, :] < pos[:, None]"),
+    "gqa-interleaved": ("h = g * grp + hh", "h = hh * hkv + g"),
+    "slot-off-by-one": ("off = j % BLOCK", "off = (j + 1) % BLOCK"),
+    "block-index-wrong": ("blk = np.asarray(bt_row)[j // BLOCK]", "blk = np.asarray(bt_row)[j // (2 * BLOCK)]"),
+    "v-layout-token-major": ("v = v_pool[blk, kv_head, :, off]", "v = v_pool[blk, kv_head, :, :].reshape(len(j), -1)[:, :k_pool.shape[-1]]"),
+    "scale-dropped": ("scores = scale * (qf[:, h, :] @ kk.T)", "scores = (qf[:, h, :] @ kk.T)"),
+    "k-v-swapped": ("scores = scale * (qf[:, h, :] @ kk.T)", "scores = scale * (qf[:, h, :] @ vv.T)"),
+    "no-normalisation": ("o[has] = (w[has] @ vv) / l[has, None]", "o[has] = (w[has] @ vv)"),
+    "lse-drops-max": ("lse[sel, h] = np.where(has, m_safe + np.log(", "lse[sel, h] = np.where(has, np.log("),
+    "position-from-seq-len": ("pos = q_start[s] + (r_glob - row_off[s])",
+                              "pos = (np.asarray(b.seq_len)[s] - q_len[s]) + (r_glob - row_off[s])"),
+    "merge-unshifted-weights": ("w = np.where(np.isfinite(pl), np.exp(pl - top_safe[None]), 0.0)",
+                                "w = np.where(np.isfinite(pl), np.exp(pl), 0.0)"),
+    "merge-weights-unnormalised": ("coef = np.where(has[None], w / np.where(has, tot, 1.0)[None], 0.0)",
+                                   "coef = np.where(has[None], w, 0.0)"),
+    "partition-lower-bound-open": ("visible &= (j[None, :] >= key_lo[s])", "visible &= (j[None, :] > key_lo[s])"),
+}
+
+
+def _load_mutant(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {name}"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    mod = _load_mutant(name, old, new)
+    failures = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(mod.attend)
+        except Exception as e:          # noqa: BLE001 - any failure counts as caught
+            failures.append(pin.__name__)
+    try:
+        P.pin_split_merge(mod)
+    except Exception:                   # noqa: BLE001
+        failures.append("pin_split_merge")
+    assert failures, f"mutant {name} survived every pin"
+
+
+def test_unmutated_copy_passes():
+    src = open(SRC).read()
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(src, "<copy>", "exec"), mod.__dict__)
+    for pin in P.ALL_PINS:
+        pin(mod.attend)
+    P.pin_split_merge(mod)
