@@ -1,0 +1,218 @@
+"""Benchmark of libpmattn on one MI355X.
+
+Default workload: decode over a paged GQA KV pool, one Llama-3-8B-shaped layer
+(64 sequences, context lengths uniform in [512, 4096], 32 query / 8 kv heads,
+head_dim 128, bf16, 16-token blocks, random non-contiguous block tables).
+``--config N`` selects one of the five synthetic workloads instead
+(1 tiny fp32, 2 decode, 3 few-shot shared prefix, 4 mixed chunk, 5 long decode).
+
+One step = one ``pmattn_forward`` of the whole batch (tile tasks + merge) with
+inputs resident in HBM; the plan is built once per batch on the host (as a
+serving loop reuses it for every layer) and its host time is reported apart.
+Before each timed step a 512 MiB scratch write evicts L2 and the MALL, so KV
+blocks come from HBM; HIP events on the launch stream bracket the tasks pass
+and the merge pass of every step.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV GB/s + prefill/verify TFLOP/s (% roofline), paged mixed attention"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+FP32_PEAK_TFS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(batch, work, min_seconds=10.0):
+    """Time the fp64 oracle on the same batch (whole batch, repeated until
+    ``min_seconds`` of CPU work); returns a dict in the metric's unit."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    runs = []
+    t_end = time.perf_counter() + min_seconds
+    while True:
+        t0 = time.perf_counter()
+        oracle.attend(batch)
+        runs.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end and len(runs) >= 2:
+            break
+    t = statistics.median(runs)
+    bound = "hbm" if work["flop"] / work["bytes"] < 100 else "mfma"
+    if bound == "hbm":
+        val, unit = work["bytes"] / t / 1e9, "GB/s"
+    else:
+        val, unit = work["flop"] / t / 1e12, "TFLOP/s"
+    return dict(value=val, unit=unit, cores=int(threads), kind="oracle",
+                sample=f"whole batch ({batch.num_seqs} sequences, {batch.num_rows} rows), "
+                       f"{len(runs)} runs of {t:.2f} s median, numpy fp64 (BLAS threads={threads}; "
+                       f"exp single-threaded); host os.cpu_count()={os.cpu_count()}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--num-kv-splits", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import prefix_shared_paged_pmattn_amd as pm
+    import workloads as wl
+
+    t0 = time.perf_counter()
+    b = wl.config(args.config)
+    if args.num_kv_splits is not None:
+        b = b.replace(num_kv_splits=args.num_kv_splits)
+    work = wl.algorithmic_work(b)
+    log(f"[bench] generated {b.name} in {time.perf_counter() - t0:.1f}s: rows={b.num_rows} "
+        f"blocks={b.num_pool_blocks} unique_kv_tokens={work['unique_kv_tokens']} flop={work['flop']:.4g} "
+        f"bytes={work['bytes']:.4g}")
+
+    dev = torch.device("cuda:0")
+    if b.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)  # noqa: E731
+        et = torch.bfloat16
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+        et = torch.float32
+    q = conv(b.q).to(dev)
+    kp = conv(b.k_pool).to(dev)
+    vp = conv(b.v_pool).to(dev)
+    bt = torch.from_numpy(b.block_table).to(dev)
+    out = torch.empty((b.num_rows, b.num_q_heads, b.head_dim), dtype=et, device=dev)
+    lse = torch.empty((b.num_rows, b.num_q_heads), dtype=torch.float32, device=dev)
+
+    def make_plan():
+        return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table,
+                       num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
+                       num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
+                       scale=b.scale, num_kv_splits=b.num_kv_splits)
+
+    plan_times = []
+    for _ in range(20):
+        t = time.perf_counter()
+        p = make_plan()
+        plan_times.append(time.perf_counter() - t)
+    plan_us = statistics.median(plan_times) * 1e6
+    tabs = p.tables()
+    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    p.upload(ws, stream)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    # Validate every tensor once through the binding, then call the two C-ABI
+    # passes with pre-marshalled arguments so that host overhead stays far
+    # below the GPU time of a step (the stream never waits for the host).
+    pm.forward_tasks(p, q, kp, vp, bt, out, lse, ws, stream)
+    pm.forward_merge(p, out, lse, ws, stream)
+    import ctypes
+    lib = pm._lib.load()
+    vptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    c_args = (p.handle, vptr(q), vptr(kp), vptr(vp), vptr(bt), vptr(out), vptr(lse), vptr(ws),
+              ws.numel(), ctypes.c_void_p(int(stream.cuda_stream)))
+    m_args = (p.handle, vptr(out), vptr(lse), vptr(ws), ws.numel(),
+              ctypes.c_void_p(int(stream.cuda_stream)))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.pmattn_forward_tasks(*c_args)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= lib.pmattn_forward_merge(*m_args)
+        if ev is not None:
+            ev[2].record(stream)
+        if st:
+            raise RuntimeError(lib.pmattn_last_error().decode())
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            scratch.zero_()
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        if not args.no_flush:
+            scratch.zero_()
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    t_task = [e[0].elapsed_time(e[1]) for e in evs]    # ms
+    t_merge = [e[1].elapsed_time(e[2]) for e in evs]
+    t_step = [e[0].elapsed_time(e[2]) for e in evs]
+    ms_step = statistics.mean(t_step)
+    ms_task = statistics.mean(t_task)
+    log(f"[bench] plan {plan_us:.1f} us host; items={tabs['items'].shape[0]} "
+        f"classes={tabs['class_rows'].tolist()} merge_rows={tabs['merge_rows'].shape[0]} "
+        f"ws={p.workspace_bytes} B")
+    log(f"[bench] step ms mean {ms_step:.4f} median {statistics.median(t_step):.4f} "
+        f"p10 {np.percentile(t_step, 10):.4f} p90 {np.percentile(t_step, 90):.4f}; "
+        f"tasks {ms_task:.4f} merge {statistics.mean(t_merge):.4f}; wall incl. flush "
+        f"{wall / args.steps * 1e3:.4f} ms/step")
+
+    flop_bound = work["flop"] / work["bytes"] > 315   # above the MI355X ridge point
+    if flop_bound:
+        value = work["flop"] / (ms_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = work["flop"] / (ms_task * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFS if b.dtype == "bf16" else FP32_PEAK_TFS
+        roof = dict(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak,
+                    traffic=None)
+    else:
+        value = work["bytes"] / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = work["bytes"] / (ms_task * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=achieved / HBM_PEAK_GBS, traffic=None)
+    log(f"[bench] value {value:.1f} {unit}; dominant kernel (tasks pass) {achieved:.1f} {roof['unit']} "
+        f"= {100 * roof['frac']:.1f}% of {roof['bound']} peak")
+
+    res = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype=b.dtype, data="synthetic",
+               config=dict(workload=b.name, num_seqs=b.num_seqs, query_rows=b.num_rows,
+                           q_heads=b.num_q_heads, kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                           block_size=16, kv_splits=b.num_kv_splits or "auto",
+                           unique_kv_bytes=work["kv_bytes_unique"],
+                           logical_kv_bytes=work["kv_bytes_logical"], flop=work["flop"],
+                           algorithmic_bytes=work["bytes"], cache_flush_between_steps=not args.no_flush),
+               roofline=roof, plan_host_us=plan_us, tasks_ms=ms_task,
+               merge_ms=statistics.mean(t_merge))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(b, work)
+        log(f"[bench] cpu baseline {res['cpu_baseline']['value']:.3f} {res['cpu_baseline']['unit']}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,240 @@
+/*
+ * pmattn.h - C ABI of libpmattn: attention over a paged KV block pool whose
+ * prefix blocks may be shared by several requests, for one mixed batch of
+ * prefill-chunk, decode and speculative-verify query rows, on AMD gfx950.
+ *
+ * What is computed (per query row r of sequence s at absolute position
+ * pos = q_start[s] + (r - first row of s), per query head h with kv head
+ * g = h / (Hq / Hkv)):
+ *
+ *     out[r][h] = sum_j softmax_j(scale * q[r][h] . K_s[j]) * V_s[j],   j = 0..pos
+ *     lse[r][h] = ln sum_j exp(scale * q[r][h] . K_s[j])
+ *
+ * where K_s[j] / V_s[j] are logical key j of sequence s, found in physical
+ * block block_table[s][j / 16] at slot j % 16.
+ *
+ * Sources (the pages this library implements):
+ *  - XY-Serve pith review ("Tackling the Dynamicity in a Production LLM
+ *    Serving System with SOTA Optimizations via Hybrid Prefill/Decode/Verify
+ *    Scheduling on Efficient Meta-kernels"), "What carries the argument" and
+ *    "Core claim": one matmul-softmax-matmul meta-kernel over tile tasks
+ *    listed in tables, for prefill, decode and verify tokens alike, with
+ *    PagedAttention-style block caches, chunked prefill and prefix caching;
+ *    "Editorial extensions": row-wise mask control instead of separate code
+ *    paths; "Assumptions & free parameters": online softmax equals softmax,
+ *    padded entries do not affect the output, block-table/radix-tree reuse
+ *    keeps K/V semantics; Figure 3: the QK and SV GEMM shapes; Figure 8:
+ *    linear speculative drafts; Figure 11: masked tiles are skipped and decode
+ *    is matrix-vector work.
+ *  - SGLang pith review ("SGLang: Efficient Execution of Structured Language
+ *    Model Programs"), "Core claim": RadixAttention reuses KV caches across
+ *    requests, so block tables of different requests name the same blocks.
+ *  - XY-Serve review reference list: "Flash-Decoding for long-context
+ *    inference" (split the KV range, merge partial results by log-sum-exp).
+ *
+ * Memory layouts (all row-major, no padding between elements):
+ *  - q, out     [R][Hq][d]         R = sum of q_len; rows of sequence s are
+ *                                  contiguous, sequences in descriptor order.
+ *  - k_pool     [num_blocks][Hkv][16][d]   token-major inside a block.
+ *  - v_pool     [num_blocks][Hkv][d][16]   channel-major inside a block, so
+ *                                  that 16 consecutive tokens of one channel
+ *                                  are one contiguous 32-byte (bf16) run.
+ *  - lse        [R][Hq] float32, natural log of the scaled scores.
+ *  - block_table int32 [B][bt_stride]; entries past ceil((q_start+q_len)/16)
+ *                of a sequence are never read.
+ * Element type of q, k_pool, v_pool and out: bf16 (PMATTN_BF16) or float32
+ * (PMATTN_F32), all the same.
+ *
+ * Threading and errors: every function is safe to call from several threads
+ * on distinct plans. No function throws across the ABI; failures return a
+ * status and set a thread-local message (pmattn_last_error()).
+ */
+#ifndef PMATTN_H
+#define PMATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pmattn_status {
+  PMATTN_OK = 0,
+  PMATTN_E_INVALID = 1,      /* malformed arguments (lengths, ids, pointers) */
+  PMATTN_E_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, block size, dtype) */
+  PMATTN_E_WORKSPACE = 3,    /* workspace too small */
+  PMATTN_E_HIP = 4,          /* a HIP runtime call failed; see pmattn_last_error() */
+  PMATTN_E_NOMEM = 5         /* host allocation failed */
+} pmattn_status;
+
+typedef enum pmattn_dtype { PMATTN_BF16 = 0, PMATTN_F32 = 1 } pmattn_dtype;
+
+/* Batch description for pmattn_plan. All pointers are HOST pointers borrowed
+ * for the duration of the call only.
+ *  q_len[s]    query rows of sequence s this step (0 allowed: no rows).
+ *  seq_len[s]  keys of s present in the pool, including this step's query
+ *              tokens (their K/V are written before attention runs).
+ *  q_start[s]  absolute position of the first query row; requires
+ *              q_start + q_len <= seq_len. Decode: q_start = seq_len - 1,
+ *              q_len = 1. Prefill chunk: q_len = chunk. Verify of k linear
+ *              drafts: q_len = k (causal among the drafts).
+ *  block_table [num_seqs][bt_stride] physical block ids; bt_stride must be
+ *              >= ceil(seq_len/16) for every sequence with q_len > 0.
+ *  num_kv_splits  0: the planner chooses KV partitions per sequence;
+ *              n in 1..256: every sequence uses n block-aligned partitions
+ *              (n_blk = ceil((q_start+q_len)/16), chunk = ceil(n_blk/n) blocks,
+ *              partition p = [p*chunk*16, min((p+1)*chunk*16, q_start+q_len))).
+ *  num_cus     compute units the plan balances for (0: 256, one MI355X).
+ *  work_shuffle_seed  0: deterministic cost order; otherwise the work list is
+ *              permuted by this seed (results must not change: a race check). */
+typedef struct pmattn_plan_desc {
+  int32_t num_seqs;
+  const int32_t* q_len;
+  const int32_t* seq_len;
+  const int32_t* q_start;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t num_pool_blocks;
+  int32_t block_size;      /* must be 16 */
+  int32_t num_q_heads;     /* Hq */
+  int32_t num_kv_heads;    /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 64 */
+  int32_t head_dim;        /* 64 or 128 */
+  int32_t dtype;           /* pmattn_dtype */
+  float scale;             /* softmax scale, finite and > 0 (usually 1/sqrt(d)) */
+  int32_t num_kv_splits;
+  int32_t num_cus;
+  uint64_t work_shuffle_seed;
+} pmattn_plan_desc;
+
+typedef struct pmattn_plan_s* pmattn_plan_t;
+
+/* One tile task of the work list (the Task-Table analogue): query tokens
+ * [row_begin, row_begin + n_tok) of sequence `seq` (positions pos_begin..)
+ * for the Hq/Hkv query heads of kv head `kv_head`, against keys
+ * [kv_begin, kv_end). part < 0: the task covers the rows' whole key range and
+ * writes out/lse directly; otherwise it writes partial results to records
+ * part + t*G + i (t = token, i = head within the group) for the merge. */
+typedef struct pmattn_work_item {
+  int32_t seq;
+  int32_t kv_head;
+  int32_t row_begin;
+  int32_t n_tok;
+  int32_t pos_begin;
+  int32_t kv_begin;
+  int32_t kv_end;
+  int32_t part;
+} pmattn_work_item;
+
+/* One output row (row, q_head) assembled from nparts partial records
+ * rec0, rec0 + rec_stride, ... by the log-sum-exp merge. */
+typedef struct pmattn_merge_row {
+  int32_t rec0;
+  int32_t rec_stride;
+  int32_t nparts;
+  int32_t row;
+  int32_t q_head;
+} pmattn_merge_row;
+
+/* Read-only views of a plan's canonical tables (owned by the plan, valid
+ * until pmattn_plan_destroy). */
+typedef struct pmattn_plan_tables {
+  int32_t num_rows;                 /* R */
+  const int32_t* row_seq;           /* [R] sequence of each query row */
+  const int32_t* row_pos;           /* [R] absolute position of each query row */
+  int32_t num_seqs;
+  const int32_t* num_splits;        /* [B] KV partitions of each sequence (0 if q_len == 0) */
+  const int32_t* split_offset;      /* [B+1] prefix sums of num_splits */
+  const int32_t* split_begin;       /* [sum num_splits] first key of each partition */
+  const int32_t* split_end;         /* [sum num_splits] one past its last key (may equal begin) */
+  int32_t num_items;
+  const pmattn_work_item* items;    /* [num_items] in launch order */
+  int32_t num_classes;              /* tile-shape classes, each a contiguous item range */
+  const int32_t* class_rows;        /* [num_classes] query rows (tokens x group) per task, max */
+  const int32_t* class_begin;       /* [num_classes + 1] item ranges */
+  int32_t num_merge_rows;
+  const pmattn_merge_row* merge_rows;
+  int32_t num_part_records;         /* partial (output, lse) records in the workspace */
+} pmattn_plan_tables;
+
+/* Build a plan on the host. Validates the batch (see pmattn_plan_desc),
+ * splits the work into tile tasks, orders them by estimated cost (largest
+ * first) and prepares the merge list. Makes no HIP call and touches no GPU.
+ * Errors: PMATTN_E_INVALID for null pointers, negative lengths,
+ * q_start + q_len > seq_len, a block id outside [0, num_pool_blocks) among the
+ * blocks a row can see, bt_stride too small, Hq % Hkv != 0, scale not finite
+ * or <= 0, num_kv_splits outside 0..256; PMATTN_E_UNSUPPORTED for
+ * block_size != 16, head_dim not in {64, 128}, an unknown dtype, or
+ * Hq / Hkv > 64. On success *out owns host memory until pmattn_plan_destroy. */
+pmattn_status pmattn_plan(const pmattn_plan_desc* desc, pmattn_plan_t* out);
+
+void pmattn_plan_destroy(pmattn_plan_t plan);
+
+/* Device workspace bytes pmattn_forward needs for this plan (work list,
+ * merge list, partial records), >= 256. */
+pmattn_status pmattn_plan_workspace_bytes(pmattn_plan_t plan, size_t* bytes);
+
+pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* tables);
+
+/* Copy the plan's work and merge lists into `workspace` (device memory of at
+ * least pmattn_plan_workspace_bytes) with an asynchronous host-to-device copy
+ * on `stream` (a hipStream_t; NULL = the default stream). pmattn_forward does
+ * this by itself whenever the workspace does not hold this plan's lists, so an
+ * explicit call is only needed after the caller has written into the
+ * workspace memory itself. Errors: PMATTN_E_INVALID, PMATTN_E_WORKSPACE,
+ * PMATTN_E_HIP. */
+pmattn_status pmattn_plan_upload(pmattn_plan_t plan, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* Run the attention of `plan` on the GPU, asynchronously on `stream`.
+ * Device pointers (caller-owned): q [R][Hq][d], k_pool, v_pool (layouts
+ * above, at least num_pool_blocks blocks), block_table_dev int32
+ * [B][bt_stride] holding the same ids as the host table given to pmattn_plan,
+ * out [R][Hq][d] (same element type as q), lse [R][Hq] float32 or NULL,
+ * workspace of ws_bytes >= pmattn_plan_workspace_bytes. The kernels read only
+ * keys a row can see; pool slots no row can see may hold anything (NaN
+ * included) without affecting the result. Errors: PMATTN_E_INVALID (null
+ * pointer), PMATTN_E_WORKSPACE, PMATTN_E_HIP (launch failure). */
+pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table_dev, void* out,
+                             float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* The two passes pmattn_forward runs, exported separately so that a caller
+ * can interleave other work or time them apart (same arguments and errors as
+ * pmattn_forward). Pass 1, pmattn_forward_tasks, runs every tile task: tasks
+ * that cover their rows' whole key range write out/lse, the others write
+ * partial (output, lse) records into the workspace. Pass 2,
+ * pmattn_forward_merge, merges those records into out/lse (a no-op when the
+ * plan split nothing). pass 2 must follow pass 1 on the same stream, with the
+ * same workspace. This is the split-KV scheme of "Flash-Decoding for
+ * long-context inference" (XY-Serve pith review, reference list). */
+pmattn_status pmattn_forward_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table_dev, void* out,
+                                   float* lse, void* workspace, size_t ws_bytes, void* stream);
+pmattn_status pmattn_forward_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
+                                   size_t ws_bytes, void* stream);
+
+/* Merge P partial attention results over disjoint key sets into the full
+ * result (the Flash-Decoding merge): with L = ln sum_p exp(part_lse[p]),
+ * out = sum_p exp(part_lse[p] - L) * part_o[p], lse = L. Partitions with
+ * lse = -inf weigh 0; if all are -inf the output is 0 and lse -inf.
+ * Device pointers: part_o float32 [P][rows][H][d], part_lse float32
+ * [P][rows][H], out [rows][H][d] of out_dtype (pmattn_dtype), lse float32
+ * [rows][H] or NULL. Asynchronous on `stream`. Errors: PMATTN_E_INVALID
+ * (P < 1, rows < 0, H < 1, null pointers), PMATTN_E_UNSUPPORTED (d not in
+ * {64, 128}), PMATTN_E_HIP. */
+pmattn_status pmattn_merge_lse(int32_t num_parts, int32_t num_rows, int32_t num_heads,
+                               int32_t head_dim, const float* part_o, const float* part_lse,
+                               void* out, int32_t out_dtype, float* lse, void* stream);
+
+/* Thread-local message describing the last failure on this thread ("" if none). */
+const char* pmattn_last_error(void);
+const char* pmattn_status_str(pmattn_status status);
+/* Library version as "major.minor.patch". */
+const char* pmattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMATTN_H */

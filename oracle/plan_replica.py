@@ -1,0 +1,152 @@
+"""Independent statement of the planner's canonical tables, and the coverage rule.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The XY-Serve review page ("Core claim") decomposes each stage's attention into
+tile tasks recorded in a Token-Table and a Task-Table. The library's planner
+is checked against this file in two ways:
+
+* the tables with one right answer (row -> sequence, row -> position, the
+  number of KV partitions per sequence and their bounds) must match
+  bit-exactly; the partition count rule and the token tiling restate the
+  library's documented policy, the partition bounds follow the split-KV
+  reading in ``attention.partition_bounds``;
+* the work list itself may come in any order, so it is checked by coverage:
+  every (query row, query head, visible key) triple is covered by exactly one
+  task and no task covers an invisible one.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import partition_bounds
+
+BLOCK = 16
+MAX_TASK_ROWS = 64
+CLASS_ROWS = (16, 32, 64)
+TASKS_PER_CU = 16
+MIN_QUANTUM = 48
+MAX_AUTO_SPLITS = 64
+
+
+def row_tables(q_len, q_start):
+    """row_seq[R], row_pos[R]: each query row's sequence and absolute position."""
+    q_len = np.asarray(q_len, np.int64)
+    row_seq = np.repeat(np.arange(q_len.shape[0]), q_len)
+    first = np.concatenate([[0], np.cumsum(q_len)[:-1]])
+    row_pos = np.asarray(q_start, np.int64)[row_seq] + (np.arange(row_seq.shape[0]) - first[row_seq])
+    return row_seq.astype(np.int32), row_pos.astype(np.int32)
+
+
+def token_tiles(q_len, q_start, group):
+    """Runs of query tokens one task holds: floor(64 / G) tokens (at least 1);
+    returns (seq, first token, tokens, rows class, kv end of the run)."""
+    per = max(1, MAX_TASK_ROWS // group)
+    tiles = []
+    for s, (ql, qs) in enumerate(zip(q_len, q_start)):
+        for t0 in range(0, int(ql), per):
+            nt = min(per, int(ql) - t0)
+            rows = nt * group
+            cls = next(c for c in CLASS_ROWS if rows <= c)
+            tiles.append((s, t0, nt, cls, int(qs) + t0 + nt))
+    return tiles
+
+
+def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
+    """KV partitions per sequence. Explicit: the requested count for every
+    sequence with rows. Automatic: a task over n blocks costs n * (2 + rows/16)
+    block units; the quantum is the total cost over (CUs x 16) tasks (at
+    least 48 units); a sequence gets ceil(cost of its largest tile / quantum)
+    partitions, at most 64 and at most its number of blocks."""
+    q_len = np.asarray(q_len, np.int64)
+    q_start = np.asarray(q_start, np.int64)
+    out = np.zeros(q_len.shape[0], np.int32)
+    if num_kv_splits > 0:
+        out[q_len > 0] = num_kv_splits
+        return out
+    tiles = token_tiles(q_len, q_start, group)
+    total = 0
+    last = np.zeros(q_len.shape[0], np.int64)
+    for s, _, _, cls, kv_end in tiles:
+        c = -(-kv_end // BLOCK) * (2 + cls // 16)
+        total += c * num_kv_heads
+        last[s] = max(last[s], c)
+    target = (num_cus if num_cus > 0 else 256) * TASKS_PER_CU
+    quantum = max(MIN_QUANTUM, -(-total // target))
+    for s in range(q_len.shape[0]):
+        if q_len[s] == 0:
+            continue
+        nblk = -(-int(q_start[s] + q_len[s]) // BLOCK)
+        out[s] = max(1, min(-(-int(last[s]) // quantum), MAX_AUTO_SPLITS, nblk))
+    return out
+
+
+def split_ranges(q_len, q_start, splits):
+    """Concatenated [begin, end) of every sequence's partitions."""
+    lo, hi = [], []
+    for s, p in enumerate(splits):
+        if p == 0:
+            continue
+        pb = partition_bounds(int(q_start[s] + q_len[s]), int(p))
+        lo.append(pb[:, 0])
+        hi.append(pb[:, 1])
+    if not lo:
+        return np.zeros(0, np.int32), np.zeros(0, np.int32)
+    return np.concatenate(lo).astype(np.int32), np.concatenate(hi).astype(np.int32)
+
+
+def expected_tasks(q_len, q_start, num_kv_heads, group, splits):
+    """The set of tasks (seq, kv_head, row_begin, n_tok, pos_begin, kv_begin,
+    kv_end): every tile x kv head x non-empty partition, the partition clipped
+    to the tile's last position."""
+    first = np.concatenate([[0], np.cumsum(np.asarray(q_len, np.int64))[:-1]])
+    tasks = set()
+    for s, t0, nt, _, kv_end in token_tiles(q_len, q_start, group):
+        pb = partition_bounds(int(q_start[s] + q_len[s]), int(splits[s]))
+        for g in range(num_kv_heads):
+            for lo, hi in pb:
+                hi = min(int(hi), kv_end)
+                if lo < hi:
+                    tasks.add((s, g, int(first[s]) + t0, nt, int(q_start[s]) + t0, int(lo), hi))
+    return tasks
+
+
+def check_coverage(items, q_len, q_start, num_kv_heads):
+    """Every visible (row, kv head, key) is covered by exactly one task.
+
+    ``items``: int array [n][>=7] of (seq, kv_head, row_begin, n_tok,
+    pos_begin, kv_begin, kv_end, ...). Raises AssertionError otherwise.
+    """
+    items = np.asarray(items, np.int64)
+    row_seq, row_pos = row_tables(q_len, q_start)
+    nrows = row_seq.shape[0]
+    if items.shape[0] == 0:
+        assert nrows == 0, "rows exist but the work list is empty"
+        return
+    nt = items[:, 3]
+    rep = np.repeat(np.arange(items.shape[0]), nt)
+    tok = np.arange(rep.shape[0]) - np.repeat(np.cumsum(nt) - nt, nt)
+    row = items[rep, 2] + tok
+    kvh = items[rep, 1]
+    pos = items[rep, 4] + tok
+    assert (row >= 0).all() and (row < nrows).all(), "task row outside the batch"
+    assert (row_seq[row] == items[rep, 0]).all(), "task row belongs to another sequence"
+    assert (row_pos[row] == pos).all(), "task position disagrees with the row table"
+    assert (items[:, 5] % BLOCK == 0).all(), "partition start not block aligned"
+    lo = items[rep, 5]
+    hi = np.minimum(items[rep, 6], pos + 1)
+    assert (items[:, 6] <= items[:, 4] + items[:, 3]).all(), "task reads past its last position"
+    keep = lo < hi
+    row, kvh, lo, hi = row[keep], kvh[keep], lo[keep], hi[keep]
+    order = np.lexsort((lo, kvh, row))
+    row, kvh, lo, hi = row[order], kvh[order], lo[order], hi[order]
+    key = row * num_kv_heads + kvh
+    want = np.arange(nrows * num_kv_heads)
+    starts = np.searchsorted(key, want, side="left")
+    ends = np.searchsorted(key, want, side="right")
+    assert (ends > starts).all(), "a (row, kv head) pair is not covered"
+    assert (lo[starts] == 0).all(), "coverage does not start at key 0"
+    assert (hi[ends - 1] == row_pos[want // num_kv_heads].astype(np.int64) + 1).all(), \
+        "coverage does not end at the row's position"
+    same = key[1:] == key[:-1]
+    assert (hi[:-1][same] == lo[1:][same]).all(), "gap or overlap between tasks of one row"

@@ -1,0 +1,111 @@
+"""ctypes declarations of libpmattn's C ABI (include/pmattn.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpmattn.so")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_NOMEM = range(6)
+BF16, F32 = 0, 1
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("q_len", _i32p),
+        ("seq_len", _i32p),
+        ("q_start", _i32p),
+        ("block_table", _i32p),
+        ("bt_stride", ctypes.c_int32),
+        ("num_pool_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("num_kv_splits", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("work_shuffle_seed", ctypes.c_uint64),
+    ]
+
+
+class WorkItem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("seq", "kv_head", "row_begin", "n_tok", "pos_begin", "kv_begin", "kv_end", "part")]
+
+
+class MergeRow(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("rec0", "rec_stride", "nparts", "row", "q_head")]
+
+
+class PlanTables(ctypes.Structure):
+    _fields_ = [
+        ("num_rows", ctypes.c_int32),
+        ("row_seq", _i32p),
+        ("row_pos", _i32p),
+        ("num_seqs", ctypes.c_int32),
+        ("num_splits", _i32p),
+        ("split_offset", _i32p),
+        ("split_begin", _i32p),
+        ("split_end", _i32p),
+        ("num_items", ctypes.c_int32),
+        ("items", ctypes.POINTER(WorkItem)),
+        ("num_classes", ctypes.c_int32),
+        ("class_rows", _i32p),
+        ("class_begin", _i32p),
+        ("num_merge_rows", ctypes.c_int32),
+        ("merge_rows", ctypes.POINTER(MergeRow)),
+        ("num_part_records", ctypes.c_int32),
+    ]
+
+
+# (name, restype, argtypes) for every function the header declares.
+SIGNATURES = [
+    ("pmattn_plan", ctypes.c_int, [ctypes.POINTER(PlanDesc), ctypes.POINTER(ctypes.c_void_p)]),
+    ("pmattn_plan_destroy", None, [ctypes.c_void_p]),
+    ("pmattn_plan_workspace_bytes", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]),
+    ("pmattn_plan_export", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(PlanTables)]),
+    ("pmattn_plan_upload", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]),
+    ("pmattn_forward", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]),
+    ("pmattn_forward_tasks", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
+    ("pmattn_forward_merge", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("pmattn_merge_lse", ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
+    ("pmattn_last_error", ctypes.c_char_p, []),
+    ("pmattn_status_str", ctypes.c_char_p, [ctypes.c_int]),
+    ("pmattn_version", ctypes.c_char_p, []),
+]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpmattn.so (built in-tree). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m prefix_shared_paged_pmattn_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib

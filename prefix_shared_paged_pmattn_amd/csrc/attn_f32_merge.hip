@@ -1,0 +1,173 @@
+// float32 attention (the plumbing path) and the log-sum-exp merge kernel.
+#include "attn_kernels.h"
+
+namespace pmattn {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One wave per tile task, one query row at a time: lanes score 64 keys in
+// parallel (serial dot products), then accumulate P.V with lane = channel.
+// Plain online softmax in fp32 with expf/logf. Correct for any task shape;
+// used for PMATTN_F32 batches, whose sizes are small.
+template <int D>
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
+  constexpr int V = D / 64;  // channels per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int idx = blockIdx.x * 4 + wave;
+  if (idx >= a.item_count) return;
+  const pmattn_work_item it = a.items[idx];
+  const int G = a.group, hq = a.hq, hkv = a.hkv, kvh = it.kv_head;
+  const float* __restrict__ qp = static_cast<const float*>(a.q);
+  const float* __restrict__ kpool = static_cast<const float*>(a.k_pool);
+  const float* __restrict__ vpool = static_cast<const float*>(a.v_pool);
+  const int32_t* bt_row = a.block_table + (int64_t)it.seq * a.bt_stride;
+  const int M = it.n_tok * G;
+  for (int m = 0; m < M; ++m) {
+    const int t = m / G;
+    const int qh = kvh * G + (m - t * G);
+    const int64_t row = it.row_begin + t;
+    const int kend = min(it.kv_end, it.pos_begin + t + 1);
+    const float* qrow = qp + (row * hq + qh) * D;
+    float m_run = kNegInf, l_run = 0.f, acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
+    for (int kb = it.kv_begin; kb < kend; kb += 64) {
+      const int j = kb + lane;
+      const bool valid = j < kend;
+      const int blk = valid ? bt_row[j >> 4] : 0;
+      float s = kNegInf;
+      if (valid) {
+        const float* kr = kpool + (((int64_t)blk * hkv + kvh) * 16 + (j & 15)) * D;
+        float dot = 0.f;
+        for (int c = 0; c < D; ++c) dot = fmaf(qrow[c], kr[c], dot);
+        s = dot * a.scale;
+      }
+      const float m_new = fmaxf(m_run, wave_max(s));  // finite: key kb is visible
+      const float alpha = expf(m_run - m_new);
+      const float p = valid ? expf(s - m_new) : 0.f;
+      l_run = l_run * alpha + wave_sum(p);
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] *= alpha;
+      const int nk = min(64, kend - kb);
+      for (int jj = 0; jj < nk; ++jj) {
+        const float pj = __shfl(p, jj);
+        const int bj = __shfl(blk, jj);
+        const float* vr = vpool + ((int64_t)bj * hkv + kvh) * D * 16 + ((kb + jj) & 15);
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = fmaf(pj, vr[(lane + 64 * v) * 16], acc[v]);
+      }
+      m_run = m_new;
+    }
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse = l_run > 0.f ? m_run + logf(l_run) : kNegInf;
+    if (it.part < 0) {
+      float* dst = static_cast<float*>(a.out) + (row * hq + qh) * D;
+#pragma unroll
+      for (int v = 0; v < V; ++v) dst[lane + 64 * v] = acc[v] * inv;
+      if (a.lse && lane == 0) a.lse[row * hq + qh] = lse;
+    } else {
+      const int64_t rec = (int64_t)it.part + m;
+#pragma unroll
+      for (int v = 0; v < V; ++v) a.part_o[rec * D + lane + 64 * v] = acc[v] * inv;
+      if (lane == 0) a.part_lse[rec] = lse;
+    }
+  }
+}
+
+// Log-sum-exp merge of partial results (Flash-Decoding, reference list of the
+// XY-Serve pith review): one wave per output (row, head); lane owns D/64
+// consecutive channels. out = sum_p w_p O_p / sum_p w_p with
+// w_p = exp(lse_p - max lse); lse = max + ln sum w_p. Empty partials (-inf)
+// weigh 0; if all are empty the output is 0 and lse is -inf.
+template <int D, bool BF16_OUT>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int V = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= a.count) return;
+  int64_t rec0, stride;
+  int np, qh;
+  int64_t row;
+  if (a.rows) {
+    const pmattn_merge_row mr = a.rows[w];
+    rec0 = mr.rec0;
+    stride = mr.rec_stride;
+    np = mr.nparts;
+    row = mr.row;
+    qh = mr.q_head;
+  } else {
+    rec0 = w;
+    stride = (int64_t)a.implicit_rows * a.hq;
+    np = a.implicit_parts;
+    row = w / a.hq;
+    qh = w - (int)row * a.hq;
+  }
+  float mx = kNegInf;
+  for (int p = 0; p < np; ++p) mx = fmaxf(mx, a.part_lse[rec0 + p * stride]);
+  float acc[V], tot = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  if (mx != kNegInf) {
+    for (int p = 0; p < np; ++p) {
+      const int64_t rec = rec0 + p * stride;
+      const float l = a.part_lse[rec];
+      const float wt = (l == kNegInf) ? 0.f : expf(l - mx);
+      tot += wt;
+      const float* src = a.part_o + rec * D + lane * V;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] = fmaf(wt, src[v], acc[v]);
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const int64_t o = (row * a.hq + qh) * D + lane * V;
+  if (BF16_OUT) {
+    __bf16* dst = static_cast<__bf16*>(a.out) + o;
+#pragma unroll
+    for (int v = 0; v < V; ++v) dst[v] = (__bf16)(acc[v] * inv);
+  } else {
+    float* dst = static_cast<float*>(a.out) + o;
+#pragma unroll
+    for (int v = 0; v < V; ++v) dst[v] = acc[v] * inv;
+  }
+  if (a.lse && lane == 0) a.lse[row * a.hq + qh] = tot > 0.f ? mx + logf(tot) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (a.item_count <= 0) return hipSuccess;
+  const dim3 grid((a.item_count + 3) / 4), block(256);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_f32_kernel<128>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_f32_kernel<64>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st) {
+  if (a.count <= 0) return hipSuccess;
+  const dim3 grid((a.count + 3) / 4), block(256);
+  const bool bf = out_dtype == PMATTN_BF16;
+  if (head_dim == 128) {
+    if (bf) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, st, a);
+  } else {
+    if (bf) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pmattn

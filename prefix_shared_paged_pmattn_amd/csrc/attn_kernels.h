@@ -1,0 +1,51 @@
+// Device-side definitions shared by the attention and merge kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pmattn.h"
+
+namespace pmattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+struct AttnArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_table;
+  void* out;
+  float* lse;                    // may be null
+  const pmattn_work_item* items; // this launch's first task
+  float* part_o;                 // [records][d]
+  float* part_lse;               // [records]
+  int32_t item_count;
+  int32_t bt_stride;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;
+  float scale;                   // softmax scale
+  float scale_log2;              // scale * log2(e)
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const pmattn_merge_row* rows;  // null: implicit [P][rows][H] layout
+  void* out;
+  float* lse;
+  int32_t count;                 // output (row, head) pairs
+  int32_t hq;                    // heads per output row
+  int32_t implicit_parts;        // implicit layout: P
+  int32_t implicit_rows;         // implicit layout: rows
+};
+
+// Host launchers (forward.hip).
+hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
+hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
+
+}  // namespace pmattn

@@ -1,0 +1,187 @@
+// Launcher half of the C ABI: uploads a plan's work list into the caller's
+// workspace and launches the tile-task kernels and the merge on the caller's
+// stream. All device memory is the caller's; nothing here allocates.
+#include <cmath>
+#include <mutex>
+#include <unordered_map>
+
+#include "attn_kernels.h"
+#include "plan_internal.h"
+
+namespace pmattn {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Which plan's lists each workspace currently holds (by plan id; ids are never
+// reused), so that forward() uploads only when the workspace changed hands.
+std::mutex g_ws_mu;
+std::unordered_map<const void*, uint64_t> g_ws_owner;
+
+pmattn_status hip_fail(hipError_t e, const char* what) {
+  return fail(PMATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pmattn_status upload(const Plan& P, void* ws, hipStream_t st) {
+  if (!P.upload_blob.empty()) {
+    hipError_t e = hipMemcpyAsync(ws, P.upload_blob.data(), P.upload_blob.size(),
+                                  hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  }
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  g_ws_owner[ws] = P.id;
+  return PMATTN_OK;
+}
+
+}  // namespace
+}  // namespace pmattn
+
+using namespace pmattn;
+
+extern "C" {
+
+void pmattn_plan_destroy(pmattn_plan_t plan) {
+  if (!plan) return;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    for (auto it = g_ws_owner.begin(); it != g_ws_owner.end();)
+      it = (it->second == plan->p.id) ? g_ws_owner.erase(it) : std::next(it);
+  }
+  delete plan;
+}
+
+pmattn_status pmattn_plan_upload(pmattn_plan_t plan, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!plan || !workspace) return fail(PMATTN_E_INVALID, "NULL plan or workspace");
+  if (ws_bytes < plan->p.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
+  return upload(plan->p, workspace, static_cast<hipStream_t>(stream));
+}
+
+static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table_dev, void* out,
+                               float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  if (!plan) return fail(PMATTN_E_INVALID, "plan is NULL");
+  const Plan& P = plan->p;
+  if (P.items.empty()) return PMATTN_OK;
+  if (!q || !k_pool || !v_pool || !block_table_dev || !out || !workspace)
+    return fail(PMATTN_E_INVALID, "q, k_pool, v_pool, block_table, out and workspace must be non-NULL");
+  if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bool need_upload;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws_owner.find(workspace);
+    need_upload = it == g_ws_owner.end() || it->second != P.id;
+  }
+  if (need_upload) {
+    pmattn_status s = upload(P, workspace, st);
+    if (s != PMATTN_OK) return s;
+  }
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  AttnArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table_dev;
+  a.out = out;
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + P.off_part_o);
+  a.part_lse = reinterpret_cast<float*>(ws + P.off_part_lse);
+  a.bt_stride = P.bt_stride;
+  a.hq = P.hq;
+  a.hkv = P.hkv;
+  a.group = P.group;
+  a.scale = P.scale;
+  a.scale_log2 = P.scale * kLog2e;
+  const pmattn_work_item* items = reinterpret_cast<const pmattn_work_item*>(ws + P.off_items);
+  for (size_t c = 0; c < P.class_rows.size(); ++c) {
+    a.items = items + P.class_begin[c];
+    a.item_count = P.class_begin[c + 1] - P.class_begin[c];
+    hipError_t e = P.dtype == PMATTN_BF16 ? launch_attn_bf16(P.head_dim, P.class_rows[c], a, st)
+                                          : launch_attn_f32(P.head_dim, a, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  }
+  return PMATTN_OK;
+}
+
+static pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (!plan) return fail(PMATTN_E_INVALID, "plan is NULL");
+  const Plan& P = plan->p;
+  if (P.merge_rows.empty()) return PMATTN_OK;
+  if (!out || !workspace) return fail(PMATTN_E_INVALID, "out and workspace must be non-NULL");
+  if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws_owner.find(workspace);
+    if (it == g_ws_owner.end() || it->second != P.id)
+      return fail(PMATTN_E_INVALID, "workspace does not hold this plan's lists: run the tasks pass first");
+  }
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  MergeArgs m;
+  m.part_o = reinterpret_cast<const float*>(ws + P.off_part_o);
+  m.part_lse = reinterpret_cast<const float*>(ws + P.off_part_lse);
+  m.rows = reinterpret_cast<const pmattn_merge_row*>(ws + P.off_merge);
+  m.out = out;
+  m.lse = lse;
+  m.count = (int32_t)P.merge_rows.size();
+  m.hq = P.hq;
+  m.implicit_parts = 0;
+  m.implicit_rows = 0;
+  hipError_t e = launch_merge(P.head_dim, P.dtype, m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return PMATTN_OK;
+}
+
+pmattn_status pmattn_forward_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_table_dev, void* out,
+                                   float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  return run_tasks(plan, q, k_pool, v_pool, block_table_dev, out, lse, workspace, ws_bytes, stream);
+}
+
+pmattn_status pmattn_forward_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  clear_error();
+  return run_merge(plan, out, lse, workspace, ws_bytes, stream);
+}
+
+pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_pool,
+                             const void* v_pool, const int32_t* block_table_dev, void* out,
+                             float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  pmattn_status s = run_tasks(plan, q, k_pool, v_pool, block_table_dev, out, lse, workspace,
+                              ws_bytes, stream);
+  if (s != PMATTN_OK) return s;
+  return run_merge(plan, out, lse, workspace, ws_bytes, stream);
+}
+
+pmattn_status pmattn_merge_lse(int32_t num_parts, int32_t num_rows, int32_t num_heads,
+                               int32_t head_dim, const float* part_o, const float* part_lse,
+                               void* out, int32_t out_dtype, float* lse, void* stream) {
+  clear_error();
+  if (num_parts < 1 || num_rows < 0 || num_heads < 1)
+    return fail(PMATTN_E_INVALID, "need num_parts >= 1, num_rows >= 0, num_heads >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(PMATTN_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (out_dtype != PMATTN_BF16 && out_dtype != PMATTN_F32)
+    return fail(PMATTN_E_UNSUPPORTED, "out_dtype must be PMATTN_BF16 or PMATTN_F32");
+  if ((int64_t)num_parts * num_rows * num_heads > INT32_MAX / 2)
+    return fail(PMATTN_E_INVALID, "too many partial records");
+  if (num_rows == 0) return PMATTN_OK;
+  if (!part_o || !part_lse || !out) return fail(PMATTN_E_INVALID, "part_o, part_lse and out must be non-NULL");
+  MergeArgs m;
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.rows = nullptr;
+  m.out = out;
+  m.lse = lse;
+  m.count = num_rows * num_heads;
+  m.hq = num_heads;
+  m.implicit_parts = num_parts;
+  m.implicit_rows = num_rows;
+  hipError_t e = launch_merge(head_dim, out_dtype, m, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return PMATTN_OK;
+}
+
+}  // extern "C"

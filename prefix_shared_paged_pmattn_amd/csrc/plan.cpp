@@ -1,0 +1,332 @@
+// Host planner: validates a batch and turns it into a list of tile tasks.
+//
+// This is the Token-Table / Task-Table step of the XY-Serve design (XY-Serve
+// pith review, "Core claim": each stage's attention work is decomposed into
+// tile-level tasks recorded in tables; "What carries the argument": tiles are
+// ordered by computational area at run time). Here a task is
+// (sequence, kv head, a run of query tokens, a KV partition). The query heads
+// of one GQA group ride together in the MFMA column dimension, so a task holds
+// tokens x (Hq/Hkv) query rows. KV partitions are the split-KV of
+// Flash-Decoding (reference list of the same page); partial results are
+// merged by log-sum-exp afterwards.
+//
+// Pure host code: no HIP call, so every rule here is testable on a CPU.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "plan_internal.h"
+
+namespace pmattn {
+
+namespace {
+thread_local std::string g_last_error;
+std::atomic<uint64_t> g_next_plan_id{1};
+
+// Cost model for ordering and automatic splitting, in "block units": a task
+// over n KV blocks costs n * (2 + rows/16). The constant 2 stands for the
+// K/V stream of each block, the rows/16 term for its MFMA column tiles.
+int64_t unit_cost(int cls) { return 2 + kClassRows[cls] / 16; }
+// Automatic splitting aims at this many tasks per compute unit ...
+constexpr int64_t kTasksPerCu = 16;
+// ... but never cuts a task below this many block units.
+constexpr int64_t kMinQuantum = 48;
+constexpr int kMaxAutoSplits = 64;
+
+int class_of_rows(int rows) {
+  for (int c = 0; c < kNumClasses; ++c)
+    if (rows <= kClassRows[c]) return c;
+  return -1;
+}
+
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+struct Tile {
+  int32_t seq, tok_begin, n_tok, cls;
+  int32_t kv_end;  // position of the tile's last token + 1
+};
+}  // namespace
+
+pmattn_status fail(pmattn_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+void clear_error() { g_last_error.clear(); }
+
+static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
+  if (!d) return fail(PMATTN_E_INVALID, "desc is NULL");
+  const int B = d->num_seqs;
+  if (B < 0) return fail(PMATTN_E_INVALID, "num_seqs < 0");
+  if (B > 0 && (!d->q_len || !d->seq_len || !d->q_start || !d->block_table))
+    return fail(PMATTN_E_INVALID, "q_len, seq_len, q_start and block_table must be non-NULL");
+  if (d->block_size != kBlock) return fail(PMATTN_E_UNSUPPORTED, "block_size must be 16");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PMATTN_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (d->dtype != PMATTN_BF16 && d->dtype != PMATTN_F32)
+    return fail(PMATTN_E_UNSUPPORTED, "dtype must be PMATTN_BF16 or PMATTN_F32");
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1)
+    return fail(PMATTN_E_INVALID, "num_q_heads and num_kv_heads must be >= 1");
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(PMATTN_E_INVALID, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G > kMaxTaskRows) return fail(PMATTN_E_UNSUPPORTED, "num_q_heads / num_kv_heads must be <= 64");
+  if (!std::isfinite(d->scale) || !(d->scale > 0.f))
+    return fail(PMATTN_E_INVALID, "scale must be finite and > 0");
+  if (d->num_kv_splits < 0 || d->num_kv_splits > kMaxSplits)
+    return fail(PMATTN_E_INVALID, "num_kv_splits must be in 0..256");
+  if (d->num_cus < 0) return fail(PMATTN_E_INVALID, "num_cus must be >= 0");
+  if (d->num_pool_blocks < 0) return fail(PMATTN_E_INVALID, "num_pool_blocks < 0");
+  if (B > 0 && d->bt_stride < 1) return fail(PMATTN_E_INVALID, "bt_stride must be >= 1");
+
+  P.num_seqs = B;
+  P.bt_stride = d->bt_stride;
+  P.num_pool_blocks = d->num_pool_blocks;
+  P.hq = d->num_q_heads;
+  P.hkv = d->num_kv_heads;
+  P.group = G;
+  P.head_dim = d->head_dim;
+  P.dtype = d->dtype;
+  P.scale = d->scale;
+
+  // ---- validate sequences, row tables -------------------------------------
+  int64_t rows = 0;
+  for (int s = 0; s < B; ++s) {
+    const int64_t ql = d->q_len[s], sl = d->seq_len[s], qs = d->q_start[s];
+    if (ql < 0 || sl < 0 || qs < 0)
+      return fail(PMATTN_E_INVALID, "negative q_len/seq_len/q_start at sequence " + std::to_string(s));
+    if (qs + ql > sl)
+      return fail(PMATTN_E_INVALID, "q_start + q_len > seq_len at sequence " + std::to_string(s));
+    if (ql == 0) continue;
+    const int64_t need_blocks = (sl + kBlock - 1) / kBlock;
+    if (need_blocks > d->bt_stride)
+      return fail(PMATTN_E_INVALID, "bt_stride < ceil(seq_len/16) at sequence " + std::to_string(s));
+    const int64_t vis_blocks = (qs + ql + kBlock - 1) / kBlock;
+    const int32_t* row = d->block_table + (int64_t)s * d->bt_stride;
+    for (int64_t j = 0; j < vis_blocks; ++j)
+      if (row[j] < 0 || row[j] >= d->num_pool_blocks)
+        return fail(PMATTN_E_INVALID, "block id out of [0, num_pool_blocks) at sequence " +
+                                          std::to_string(s) + " block " + std::to_string(j));
+    rows += ql;
+  }
+  if (rows > INT32_MAX / std::max(1, d->num_q_heads))
+    return fail(PMATTN_E_INVALID, "too many query rows");
+  P.num_rows = (int32_t)rows;
+  P.row_seq.resize(rows);
+  P.row_pos.resize(rows);
+  {
+    int64_t r = 0;
+    for (int s = 0; s < B; ++s)
+      for (int t = 0; t < d->q_len[s]; ++t, ++r) {
+        P.row_seq[r] = s;
+        P.row_pos[r] = d->q_start[s] + t;
+      }
+  }
+
+  // ---- tiles: runs of query tokens whose G heads fit one task --------------
+  const int tok_per_task = std::max(1, kMaxTaskRows / G);
+  std::vector<Tile> tiles;
+  std::vector<int32_t> row_off(B + 1, 0);
+  for (int s = 0; s < B; ++s) row_off[s + 1] = row_off[s] + d->q_len[s];
+  for (int s = 0; s < B; ++s) {
+    for (int t0 = 0; t0 < d->q_len[s]; t0 += tok_per_task) {
+      const int nt = std::min(tok_per_task, d->q_len[s] - t0);
+      tiles.push_back(Tile{s, t0, nt, class_of_rows(nt * G), d->q_start[s] + t0 + nt});
+    }
+  }
+
+  // ---- KV partitions per sequence ----------------------------------------
+  P.num_splits.assign(B, 0);
+  if (d->num_kv_splits > 0) {
+    for (int s = 0; s < B; ++s) P.num_splits[s] = d->q_len[s] > 0 ? d->num_kv_splits : 0;
+  } else {
+    int64_t total = 0;
+    std::vector<int64_t> last_cost(B, 0);
+    for (const Tile& t : tiles) {
+      const int64_t c = (int64_t)((t.kv_end + kBlock - 1) / kBlock) * unit_cost(t.cls);
+      total += c * d->num_kv_heads;
+      last_cost[t.seq] = std::max(last_cost[t.seq], c);
+    }
+    const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
+    const int64_t target = cus * kTasksPerCu;
+    const int64_t quantum = std::max(kMinQuantum, (total + target - 1) / target);
+    for (int s = 0; s < B; ++s) {
+      if (d->q_len[s] == 0) continue;
+      const int64_t nblk = (d->q_start[s] + d->q_len[s] + kBlock - 1) / kBlock;
+      int64_t p = (last_cost[s] + quantum - 1) / quantum;
+      p = std::min<int64_t>(std::min<int64_t>(p, kMaxAutoSplits), nblk);
+      P.num_splits[s] = (int32_t)std::max<int64_t>(1, p);
+    }
+  }
+  P.split_offset.assign(B + 1, 0);
+  for (int s = 0; s < B; ++s) P.split_offset[s + 1] = P.split_offset[s] + P.num_splits[s];
+  P.split_begin.resize(P.split_offset[B]);
+  P.split_end.resize(P.split_offset[B]);
+  for (int s = 0; s < B; ++s) {
+    const int np = P.num_splits[s];
+    if (!np) continue;
+    const int64_t kv = (int64_t)d->q_start[s] + d->q_len[s];
+    const int64_t nblk = (kv + kBlock - 1) / kBlock;
+    const int64_t chunk = std::max<int64_t>(1, (nblk + np - 1) / np);
+    for (int p = 0; p < np; ++p) {
+      P.split_begin[P.split_offset[s] + p] = (int32_t)std::min<int64_t>(p * chunk * kBlock, kv);
+      P.split_end[P.split_offset[s] + p] = (int32_t)std::min<int64_t>((p + 1) * chunk * kBlock, kv);
+    }
+  }
+
+  // ---- tasks, partial records and merge rows --------------------------------
+  std::vector<std::vector<pmattn_work_item>> by_class(kNumClasses);
+  int64_t records = 0;
+  for (const Tile& t : tiles) {
+    const int trows = t.n_tok * G;
+    const int base = P.split_offset[t.seq];
+    int k = 0;
+    for (int p = 0; p < P.num_splits[t.seq]; ++p)
+      if (P.split_begin[base + p] < std::min(P.split_end[base + p], t.kv_end)) ++k;
+    for (int g = 0; g < d->num_kv_heads; ++g) {
+      const int64_t rec_base = records;
+      if (k > 1) records += (int64_t)k * trows;
+      int made = 0;
+      for (int p = 0; p < P.num_splits[t.seq]; ++p) {
+        const int32_t lo = P.split_begin[base + p];
+        const int32_t hi = std::min(P.split_end[base + p], t.kv_end);
+        if (lo >= hi) continue;
+        pmattn_work_item it;
+        it.seq = t.seq;
+        it.kv_head = g;
+        it.row_begin = row_off[t.seq] + t.tok_begin;
+        it.n_tok = t.n_tok;
+        it.pos_begin = d->q_start[t.seq] + t.tok_begin;
+        it.kv_begin = lo;
+        it.kv_end = hi;
+        it.part = k > 1 ? (int32_t)(rec_base + (int64_t)made * trows) : -1;
+        by_class[t.cls].push_back(it);
+        ++made;
+      }
+      if (k > 1)
+        for (int m = 0; m < trows; ++m)
+          P.merge_rows.push_back(pmattn_merge_row{(int32_t)(rec_base + m), trows, k,
+                                                  row_off[t.seq] + t.tok_begin + m / G, g * G + m % G});
+    }
+  }
+  if (records > INT32_MAX / 2) return fail(PMATTN_E_INVALID, "too many partial records");
+  P.num_records = (int32_t)records;
+
+  // ---- order: largest estimated cost first within each class (LPT) --------
+  uint64_t rng = d->work_shuffle_seed;
+  P.class_begin.push_back(0);
+  for (int c = 0; c < kNumClasses; ++c) {
+    auto& v = by_class[c];
+    if (v.empty()) continue;
+    std::vector<int64_t> cost(v.size());
+    for (size_t i = 0; i < v.size(); ++i)
+      cost[i] = (int64_t)((v[i].kv_end - v[i].kv_begin + kBlock - 1) / kBlock) * unit_cost(c);
+    std::vector<size_t> idx(v.size());
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
+    if (d->work_shuffle_seed)
+      for (size_t i = idx.size(); i > 1; --i) std::swap(idx[i - 1], idx[splitmix64(rng) % i]);
+    for (size_t i : idx) P.items.push_back(v[i]);
+    P.class_rows.push_back(kClassRows[c]);
+    P.class_begin.push_back((int32_t)P.items.size());
+  }
+
+  // ---- workspace layout and the upload image --------------------------------
+  P.off_items = 0;
+  P.off_merge = align_up(P.off_items + P.items.size() * sizeof(pmattn_work_item), kAlign);
+  P.off_part_o = align_up(P.off_merge + P.merge_rows.size() * sizeof(pmattn_merge_row), kAlign);
+  P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
+  P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
+  P.upload_blob.assign(P.off_part_o, 0);
+  if (!P.items.empty())
+    std::memcpy(P.upload_blob.data() + P.off_items, P.items.data(),
+                P.items.size() * sizeof(pmattn_work_item));
+  if (!P.merge_rows.empty())
+    std::memcpy(P.upload_blob.data() + P.off_merge, P.merge_rows.data(),
+                P.merge_rows.size() * sizeof(pmattn_merge_row));
+  P.id = g_next_plan_id.fetch_add(1);
+  return PMATTN_OK;
+}
+
+}  // namespace pmattn
+
+using namespace pmattn;
+
+extern "C" {
+
+pmattn_status pmattn_plan(const pmattn_plan_desc* desc, pmattn_plan_t* out) {
+  clear_error();
+  if (!out) return fail(PMATTN_E_INVALID, "out is NULL");
+  *out = nullptr;
+  pmattn_plan_s* h = new (std::nothrow) pmattn_plan_s();
+  if (!h) return fail(PMATTN_E_NOMEM, "plan allocation failed");
+  pmattn_status st;
+  try {
+    st = build_plan(desc, h->p);
+  } catch (const std::bad_alloc&) {
+    st = fail(PMATTN_E_NOMEM, "host allocation failed while planning");
+  } catch (...) {
+    st = fail(PMATTN_E_INVALID, "unexpected error while planning");
+  }
+  if (st != PMATTN_OK) {
+    delete h;
+    return st;
+  }
+  *out = h;
+  return PMATTN_OK;
+}
+
+pmattn_status pmattn_plan_workspace_bytes(pmattn_plan_t plan, size_t* bytes) {
+  clear_error();
+  if (!plan || !bytes) return fail(PMATTN_E_INVALID, "NULL argument");
+  *bytes = plan->p.ws_bytes;
+  return PMATTN_OK;
+}
+
+pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
+  clear_error();
+  if (!plan || !t) return fail(PMATTN_E_INVALID, "NULL argument");
+  const Plan& P = plan->p;
+  t->num_rows = P.num_rows;
+  t->row_seq = P.row_seq.data();
+  t->row_pos = P.row_pos.data();
+  t->num_seqs = P.num_seqs;
+  t->num_splits = P.num_splits.data();
+  t->split_offset = P.split_offset.data();
+  t->split_begin = P.split_begin.data();
+  t->split_end = P.split_end.data();
+  t->num_items = (int32_t)P.items.size();
+  t->items = P.items.data();
+  t->num_classes = (int32_t)P.class_rows.size();
+  t->class_rows = P.class_rows.data();
+  t->class_begin = P.class_begin.data();
+  t->num_merge_rows = (int32_t)P.merge_rows.size();
+  t->merge_rows = P.merge_rows.data();
+  t->num_part_records = P.num_records;
+  return PMATTN_OK;
+}
+
+const char* pmattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* pmattn_status_str(pmattn_status s) {
+  switch (s) {
+    case PMATTN_OK: return "PMATTN_OK";
+    case PMATTN_E_INVALID: return "PMATTN_E_INVALID";
+    case PMATTN_E_UNSUPPORTED: return "PMATTN_E_UNSUPPORTED";
+    case PMATTN_E_WORKSPACE: return "PMATTN_E_WORKSPACE";
+    case PMATTN_E_HIP: return "PMATTN_E_HIP";
+    case PMATTN_E_NOMEM: return "PMATTN_E_NOMEM";
+  }
+  return "PMATTN_E_UNKNOWN";
+}
+
+const char* pmattn_version(void) { return "0.1.0"; }
+
+}  // extern "C"

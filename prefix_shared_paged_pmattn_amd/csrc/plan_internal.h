@@ -1,0 +1,51 @@
+// Internal plan representation shared by the host planner (plan.cpp) and the
+// launcher (forward.hip). Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pmattn.h"
+
+namespace pmattn {
+
+constexpr int kBlock = 16;
+// Query rows (tokens x heads of one GQA group) one task may hold; tile-shape
+// classes are 16, 32 and 64 rows (one, two or four 16-row MFMA column tiles).
+constexpr int kMaxTaskRows = 64;
+constexpr int kNumClasses = 3;
+constexpr int kClassRows[kNumClasses] = {16, 32, 64};
+constexpr int kMaxSplits = 256;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  uint64_t id = 0;
+  // batch shape
+  int32_t num_seqs = 0, num_rows = 0, bt_stride = 0, num_pool_blocks = 0;
+  int32_t hq = 0, hkv = 0, group = 0, head_dim = 0, dtype = 0;
+  float scale = 0.f;
+  // canonical tables
+  std::vector<int32_t> row_seq, row_pos;
+  std::vector<int32_t> num_splits, split_offset, split_begin, split_end;
+  std::vector<pmattn_work_item> items;
+  std::vector<int32_t> class_rows, class_begin;
+  std::vector<pmattn_merge_row> merge_rows;
+  int32_t num_records = 0;
+  // workspace layout (bytes): [items | merge rows | partial O | partial lse]
+  size_t off_items = 0, off_merge = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+  std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
+};
+
+// thread-local error message helpers (plan.cpp)
+pmattn_status fail(pmattn_status st, const std::string& msg);
+void clear_error();
+
+}  // namespace pmattn
+
+struct pmattn_plan_s {
+  pmattn::Plan p;
+};

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: bf16 inputs max-abs <= 2e-2 and mean-abs <= 2e-3 over every compared
+output element (lse within 1e-3); fp32 inputs max-abs <= 1e-5. Invariants the
+pages state (shared = private blocks, padding never affects the output) and
+the race check (work-list order) must hold bit-exactly on the GPU.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import prefix_shared_paged_pmattn_amd as pm
+import workloads as wl
+from gpu_helpers import compare, make_plan, note, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _batch_cases():
+    S = dict
+    return {
+        # decode rows, GQA 4, ragged lengths across block edges
+        "decode-g4-d128": (dict(hq=8, hkv=2, d=128), [S(q_len=1, seq_len=n) for n in (1, 15, 16, 17, 33, 100, 513, 1000)], 0),
+        "decode-g8-d128-split3": (dict(hq=16, hkv=2, d=128), [S(q_len=1, seq_len=n) for n in (2, 47, 300, 777)], 3),
+        "decode-g4-d64": (dict(hq=8, hkv=2, d=64), [S(q_len=1, seq_len=n) for n in (5, 64, 65, 129, 400)], 0),
+        "verify5-g4": (dict(hq=8, hkv=2, d=128), [S(q_len=5, seq_len=n) for n in (5, 21, 37, 300)], 0),
+        "prefill-unaligned": (dict(hq=8, hkv=2, d=128), [S(q_len=37, seq_len=42, q_start=5), S(q_len=100, seq_len=100),
+                                                         S(q_len=64, seq_len=264, q_start=200)], 0),
+        "prefill-d64-split2": (dict(hq=4, hkv=1, d=64), [S(q_len=70, seq_len=90, q_start=20), S(q_len=16, seq_len=16)], 2),
+        "mha-g1": (dict(hq=4, hkv=4, d=128), [S(q_len=20, seq_len=50, q_start=30), S(q_len=1, seq_len=80)], 0),
+        "g2": (dict(hq=6, hkv=3, d=64), [S(q_len=9, seq_len=30, q_start=21), S(q_len=3, seq_len=3)], 0),
+        "g16": (dict(hq=32, hkv=2, d=128), [S(q_len=5, seq_len=60, q_start=55), S(q_len=1, seq_len=19)], 0),
+        "g32": (dict(hq=32, hkv=1, d=128), [S(q_len=3, seq_len=40, q_start=37), S(q_len=1, seq_len=33)], 0),
+        "g64": (dict(hq=64, hkv=1, d=64), [S(q_len=2, seq_len=50, q_start=48), S(q_len=1, seq_len=7)], 0),
+        "g12-ragged": (dict(hq=12, hkv=1, d=128), [S(q_len=11, seq_len=99, q_start=88)], 0),
+        "empty-seqs-mixed": (dict(hq=8, hkv=2, d=128), [S(q_len=0, seq_len=10), S(q_len=3, seq_len=35),
+                                                        S(q_len=0, seq_len=0), S(q_len=1, seq_len=64)], 0),
+        "many-splits-empty-parts": (dict(hq=8, hkv=2, d=128), [S(q_len=1, seq_len=40), S(q_len=4, seq_len=200)], 64),
+        "position-zero": (dict(hq=4, hkv=2, d=128), [S(q_len=1, seq_len=1, q_start=0), S(q_len=4, seq_len=4, q_start=0)], 0),
+        "keys-beyond-last-query": (dict(hq=8, hkv=2, d=128), [S(q_len=3, seq_len=90, q_start=10)], 0),
+    }
+
+
+CASES = _batch_cases()
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_small_batches(name):
+    shape, specs, splits = CASES[name]
+    b = wl.custom(specs, seed=zlib.crc32(name.encode()) % 1000, num_kv_splits=splits, name=name, extra_blocks=2,
+                  **shape)
+    note(f"case {name}: rows={b.num_rows}")
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
+
+
+def test_config1_f32_plumbing():
+    b = wl.config(1)
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
+
+
+def test_f32_splits_and_gqa():
+    b = wl.custom([dict(q_len=3, seq_len=70, q_start=60), dict(q_len=1, seq_len=33)], hq=4, hkv=2,
+                  d=128, dtype="f32", seed=3, num_kv_splits=3)
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
+
+
+def test_single_key_is_exact():
+    """One visible key: p = 1 exactly, so the output is V_0 bit for bit."""
+    b = wl.custom([dict(q_len=1, seq_len=1, q_start=0), dict(q_len=1, seq_len=17, q_start=0)],
+                  hq=8, hkv=2, d=128, seed=4)
+    out, lse = run_gpu(b)
+    for s in range(2):
+        for h in range(8):
+            v0 = wl.bf16_bits_to_f32(b.v_pool[b.block_table[s, 0], h // 4, :, 0]).astype(np.float64)
+            assert np.array_equal(out[s, h], v0)
+    compare(b, out, lse)
+
+
+def test_full_config2_decode():
+    b = wl.config(2)
+    note(f"config 2: {b.num_rows} rows, {b.num_pool_blocks} blocks")
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
+
+
+def test_full_config5_long_decode():
+    b = wl.config(5)
+    note(f"config 5: {b.num_rows} rows, {b.num_pool_blocks} blocks, splits {b.num_kv_splits}")
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
+
+
+def test_full_config3_sampled_rows():
+    b = wl.config(3)
+    rng = np.random.Generator(np.random.PCG64(33))
+    rows = np.unique(np.concatenate([rng.choice(b.num_rows, 48, replace=False),
+                                     [0, 15, 16, 127, 128, 32640, b.num_rows - 1]]))
+    note(f"config 3: {b.num_rows} rows, sampling {rows.size}")
+    out, lse = run_gpu(b)
+    compare(b, out, lse, rows=rows)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_full_config4_sampled_rows():
+    b = wl.config(4)
+    off = b.row_offsets()
+    rng = np.random.Generator(np.random.PCG64(44))
+    firsts = [int(off[s]) for s in range(16)] + [int(off[s + 1]) - 1 for s in range(16)]
+    rows = np.unique(np.concatenate([np.arange(int(off[16]), b.num_rows),      # decode + verify
+                                     rng.choice(int(off[16]), 64, replace=False), firsts]))
+    note(f"config 4: {b.num_rows} rows, sampling {rows.size}")
+    out, lse = run_gpu(b)
+    compare(b, out, lse, rows=rows)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_poison_in_invisible_slots_changes_nothing():
+    b = wl.custom([dict(q_len=1, seq_len=37), dict(q_len=5, seq_len=50, q_start=41),
+                   dict(q_len=20, seq_len=33, q_start=2), dict(q_len=3, seq_len=90, q_start=10)],
+                  hq=8, hkv=2, d=128, seed=12, extra_blocks=3, num_kv_splits=2)
+    ref_o, ref_l = run_gpu(b)
+    for val in (float("nan"), 6e4, -6e4):
+        o, l = run_gpu(wl.with_poison(b, val))
+        assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l), val
+    compare(b, ref_o, ref_l)
+
+
+def test_work_order_does_not_change_bits():
+    """Race check: any permutation of the work list gives bit-identical output."""
+    b = wl.custom([dict(q_len=1, seq_len=n) for n in (100, 333, 517)] +
+                  [dict(q_len=40, seq_len=300, q_start=260), dict(q_len=5, seq_len=80)],
+                  hq=8, hkv=2, d=128, seed=5, num_kv_splits=3)
+    dev = to_device(b)
+    ref_o, ref_l = run_gpu(b, dev)
+    for seed in (1, 2, 99):
+        o, l = run_gpu(b, dev, work_shuffle_seed=seed)
+        assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l)
+
+
+def test_shared_blocks_equal_private_copies_bitwise():
+    b = wl.custom([dict(q_len=3, seq_len=70, q_start=40, nodes=["a", "b"]), dict(q_len=1, seq_len=55, nodes=["a"]),
+                   dict(q_len=2, seq_len=90, q_start=88, nodes=["a", "b"])],
+                  node_blocks={"a": 2, "b": 1}, hq=8, hkv=2, d=128, seed=9)
+    ref_o, ref_l = run_gpu(b)
+    for other in (wl.private_copy(b), wl.relabel(b, 3)):
+        o, l = run_gpu(other)
+        assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l)
+    compare(b, ref_o, ref_l)
+
+
+def test_decode_row_matches_prefill_row():
+    """Class independence on the GPU: a decode row equals the prefill row at the
+    same position (within the bf16 bar; the tile shapes differ)."""
+    pre = wl.custom([dict(q_len=6, seq_len=245, q_start=239)], hq=8, hkv=2, d=128, seed=21)
+    po, pl = run_gpu(pre)
+    for t in (0, 3, 5):
+        dec = pre.replace(q_len=np.array([1], np.int32), q_start=np.array([239 + t], np.int32),
+                          seq_len=np.array([240 + t], np.int32), q=pre.q[t:t + 1])
+        o, l = run_gpu(dec)
+        assert np.abs(o[0] - po[t]).max() <= 1e-2 and np.abs(l[0] - pl[t]).max() <= 1e-4
+
+
+def test_two_passes_equal_forward():
+    import torch
+    b = wl.custom([dict(q_len=1, seq_len=n) for n in (300, 700)] + [dict(q_len=9, seq_len=100)],
+                  hq=8, hkv=2, d=128, seed=6, num_kv_splits=4)
+    dev = to_device(b)
+    ref_o, ref_l = run_gpu(b, dev)
+    p = make_plan(b)
+    out = torch.zeros((b.num_rows, 8, 128), dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.zeros((b.num_rows, 8), dtype=torch.float32, device="cuda:0")
+    ws = pm.forward_tasks(p, dev["q"], dev["k"], dev["v"], dev["bt"], out, lse)
+    pm.forward_merge(p, out, lse, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), ref_o) and np.array_equal(lse.cpu().numpy(), ref_l)
+    other = torch.zeros_like(ws)
+    with pytest.raises(pm.PmattnError):
+        pm.forward_merge(p, out, lse, other)
+
+
+def test_empty_plan_launches_nothing():
+    import torch
+    b = wl.custom([dict(q_len=0, seq_len=30)], hq=4, hkv=2, d=128, seed=1)
+    p = make_plan(b)
+    out = torch.zeros((0, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    dev = to_device(b)
+    pm.forward(p, dev["q"], dev["k"], dev["v"], dev["bt"], out)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
+def test_merge_lse_standalone(d, out_dtype):
+    import torch
+    rng = np.random.Generator(np.random.PCG64(d))
+    P, rows, H = 5, 7, 3
+    po = rng.standard_normal((P, rows, H, d)).astype(np.float32)
+    pl = (rng.standard_normal((P, rows, H)) * 3).astype(np.float32)
+    pl[1, 2, :] = -np.inf            # an empty partition
+    pl[:, 4, 1] = -np.inf            # a row with every partition empty
+    po[:, 4, 1] = 0
+    ref_o, ref_l = oracle.merge_partitions(po.astype(np.float64), pl.astype(np.float64))
+    et = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out = torch.full((rows, H, d), float("nan"), dtype=et, device="cuda:0")
+    lse = torch.full((rows, H), float("nan"), dtype=torch.float32, device="cuda:0")
+    pm.merge_lse(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(), out, lse)
+    torch.cuda.synchronize()
+    go = out.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    tol = 8e-3 if out_dtype == "bf16" else 2e-6
+    assert np.abs(go - ref_o).max() <= tol
+    fin = np.isfinite(ref_l)
+    assert np.abs(gl[fin] - ref_l[fin]).max() <= 2e-6
+    assert np.array_equal(np.isneginf(gl), ~fin) and (go[4, 1] == 0).all()
+
+
+def test_forward_rejects_mis_sized_tensors():
+    import torch
+    b = wl.custom([dict(q_len=2, seq_len=20)], hq=4, hkv=2, d=128, seed=1)
+    p = make_plan(b)
+    dev = to_device(b)
+    out = torch.zeros((2, 4, 128), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(ValueError):
+        pm.forward(p, dev["q"][:1], dev["k"], dev["v"], dev["bt"], out)
+    with pytest.raises(ValueError):
+        pm.forward(p, dev["q"], dev["k"][:1], dev["v"], dev["bt"], out)
+    with pytest.raises(ValueError):
+        pm.forward(p, dev["q"], dev["k"], dev["v"], dev["bt"], out.float())
+    with pytest.raises(ValueError):
+        pm.forward(p, dev["q"], dev["k"], dev["v"], dev["bt"], out,
+                   workspace=torch.zeros(16, dtype=torch.uint8, device="cuda:0"))

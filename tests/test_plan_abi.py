@@ -1,0 +1,205 @@
+"""Host planner through the C ABI (no GPU needed): tables bit-exact against the
+oracle's replica, exact coverage of every visible (row, head, key), error paths,
+and the exported symbol set."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.plan_replica as R
+import prefix_shared_paged_pmattn_amd as pm
+import workloads as wl
+from prefix_shared_paged_pmattn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def make_plan(b, **kw):
+    return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, num_pool_blocks=b.num_pool_blocks,
+                   num_q_heads=b.num_q_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
+                   dtype=b.dtype, scale=b.scale, num_kv_splits=kw.pop("num_kv_splits", b.num_kv_splits),
+                   **kw)
+
+
+def check_plan(b, p, num_cus=0):
+    t = p.tables()
+    grp = b.num_q_heads // b.num_kv_heads
+    rs, rp = R.row_tables(b.q_len, b.q_start)
+    assert np.array_equal(t["row_seq"], rs) and np.array_equal(t["row_pos"], rp)
+    ns = R.num_splits(b.q_len, b.q_start, b.num_kv_heads, grp, b.num_kv_splits, num_cus)
+    assert np.array_equal(t["num_splits"], ns)
+    lo, hi = R.split_ranges(b.q_len, b.q_start, ns)
+    assert np.array_equal(t["split_begin"], lo) and np.array_equal(t["split_end"], hi)
+    got = {tuple(int(x) for x in it[:7]) for it in t["items"]}
+    assert len(got) == t["items"].shape[0], "duplicate tasks"
+    assert got == R.expected_tasks(b.q_len, b.q_start, b.num_kv_heads, grp, ns)
+    R.check_coverage(t["items"], b.q_len, b.q_start, b.num_kv_heads)
+    check_records(b, t)
+    return t
+
+
+def check_records(b, t):
+    """Direct tasks write each (row, head) once; split (row, head) pairs have one
+    merge row whose records are exactly the parts its tasks write."""
+    grp = b.num_q_heads // b.num_kv_heads
+    items, merge = t["items"], t["merge_rows"]
+    direct, recs = {}, {}
+    for it in items:
+        seq, g, r0, ntok, p0, lo, hi, part = (int(x) for x in it)
+        for m in range(ntok * grp):
+            key = (r0 + m // grp, g * grp + m % grp)
+            if part < 0:
+                direct[key] = direct.get(key, 0) + 1
+            else:
+                recs.setdefault(key, []).append(part + m)
+    assert all(v == 1 for v in direct.values())
+    seen = set()
+    for rec0, stride, nparts, row, qh in merge:
+        key = (int(row), int(qh))
+        assert key not in direct and key not in seen
+        seen.add(key)
+        assert sorted(recs[key]) == [int(rec0) + p * int(stride) for p in range(int(nparts))]
+    assert seen == set(recs)
+    assert len(direct) + len(seen) == t["row_seq"].shape[0] * b.num_q_heads
+    allrec = [r for v in recs.values() for r in v]
+    assert len(set(allrec)) == len(allrec) and (not allrec or max(allrec) < t["num_part_records"])
+    # classes are contiguous ranges whose tasks fit the class's row count
+    cb, cr = t["class_begin"], t["class_rows"]
+    assert cb[0] == 0 and cb[-1] == items.shape[0]
+    for c in range(cr.shape[0]):
+        rows = items[cb[c]:cb[c + 1], 3] * grp
+        assert (rows <= cr[c]).all()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_plan_tables_match_replica(cfg):
+    b = wl.config(cfg, values=False)
+    check_plan(b, make_plan(b))
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+@pytest.mark.parametrize("seed", range(4))
+def test_plan_random_small_batches(splits, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for hq, hkv in ((4, 4), (8, 2), (32, 8), (64, 1), (12, 4)):
+        specs = []
+        for _ in range(int(rng.integers(1, 9))):
+            n = int(rng.integers(1, 300))
+            ql = int(rng.integers(0, min(n, 70) + 1))
+            qs = int(rng.integers(0, n - ql + 1))
+            specs.append(dict(q_len=ql, seq_len=n, q_start=qs))
+        b = wl.custom(specs, hq=hq, hkv=hkv, d=128, seed=seed, num_kv_splits=splits, values=False)
+        for cus in (0, 3, 80):
+            check_plan(b, make_plan(b, num_cus=cus), num_cus=cus)
+
+
+def test_shuffle_changes_order_not_content():
+    b = wl.config(4, values=False)
+    a = make_plan(b).tables()
+    s = make_plan(b, work_shuffle_seed=1234).tables()
+    assert not np.array_equal(a["items"], s["items"])
+    assert sorted(map(tuple, a["items"][:, :7].tolist())) == sorted(map(tuple, s["items"][:, :7].tolist()))
+    check_plan(b, make_plan(b, work_shuffle_seed=1234))
+
+
+def test_cost_order_is_descending_within_class():
+    b = wl.config(2, values=False)
+    t = make_plan(b).tables()
+    it = t["items"]
+    for c in range(t["class_rows"].shape[0]):
+        blk = -(-(it[t["class_begin"][c]:t["class_begin"][c + 1], 6]
+                  - it[t["class_begin"][c]:t["class_begin"][c + 1], 5]) // 16)
+        assert (np.diff(blk) <= 0).all()
+
+
+def test_workspace_bytes():
+    b = wl.config(5, values=False)
+    p = make_plan(b)
+    t = p.tables()
+    assert p.workspace_bytes >= t["num_part_records"] * (128 + 1) * 4 + t["items"].shape[0] * 32
+    assert p.workspace_bytes % 256 == 0
+
+
+def _desc_kwargs(b):
+    return dict(num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
+                num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, scale=b.scale)
+
+
+def test_error_paths():
+    b = wl.custom([dict(q_len=2, seq_len=40, q_start=38), dict(q_len=1, seq_len=17)],
+                  hq=4, hkv=2, d=64, values=False)
+    kw = _desc_kwargs(b)
+
+    def err(status, **over):
+        args = dict(q_len=b.q_len, seq_len=b.seq_len, q_start=b.q_start, block_table=b.block_table)
+        k2 = dict(kw)
+        for k, v in over.items():
+            (args if k in args else k2)[k] = v
+        with pytest.raises(pm.PmattnError) as e:
+            pm.plan(args["q_len"], args["seq_len"], args["q_start"], args["block_table"], **k2)
+        assert e.value.status == status, str(e.value)
+        return str(e.value)
+
+    INV, UNS = _lib.E_INVALID, _lib.E_UNSUPPORTED
+    assert "q_start + q_len > seq_len" in err(INV, q_start=np.array([39, 16]))
+    err(INV, q_len=np.array([-1, 1]))
+    bad = b.block_table.copy()
+    bad[0, 1] = b.num_pool_blocks
+    assert "block id" in err(INV, block_table=bad)
+    bad[0, 1] = -1
+    err(INV, block_table=bad)
+    err(INV, block_table=b.block_table[:, :2])           # stride < ceil(40/16)
+    err(INV, num_q_heads=6, num_kv_heads=4)
+    err(INV, scale=0.0)
+    err(INV, scale=float("nan"))
+    err(INV, num_kv_splits=257)
+    err(INV, num_kv_splits=-1)
+    err(UNS, head_dim=96)
+    err(UNS, num_q_heads=130, num_kv_heads=1)
+    # block size is fixed at 16 by the binding; check the C check directly
+    lib = _lib.load()
+    d = _lib.PlanDesc(num_seqs=0, block_size=8, num_q_heads=1, num_kv_heads=1, head_dim=64, dtype=0,
+                      scale=1.0)
+    h = ctypes.c_void_p()
+    assert lib.pmattn_plan(ctypes.byref(d), ctypes.byref(h)) == UNS
+    assert b"block_size" in lib.pmattn_last_error()
+    d = _lib.PlanDesc(num_seqs=0, block_size=16, num_q_heads=1, num_kv_heads=1, head_dim=64,
+                      dtype=7, scale=1.0)
+    assert lib.pmattn_plan(ctypes.byref(d), ctypes.byref(h)) == UNS
+    d = _lib.PlanDesc(num_seqs=2, block_size=16, num_q_heads=1, num_kv_heads=1, head_dim=64,
+                      dtype=0, scale=1.0)                  # null arrays
+    assert lib.pmattn_plan(ctypes.byref(d), ctypes.byref(h)) == INV
+    assert lib.pmattn_plan(None, ctypes.byref(h)) == INV
+
+
+def test_unused_table_entries_are_not_validated():
+    # entries past the visible blocks may be anything (here -1); rows of length 0 read nothing
+    b = wl.custom([dict(q_len=1, seq_len=20, q_start=5), dict(q_len=0, seq_len=33)], hq=2, hkv=1,
+                  d=64, values=False)
+    bt = b.block_table.copy()
+    bt[0, 1] = -7        # block 1 holds keys 16..19, invisible to the row at position 5
+    bt[1, :] = 10 ** 6   # sequence without rows
+    p = pm.plan(b.q_len, b.seq_len, b.q_start, bt, **_desc_kwargs(b))
+    t = p.tables()
+    assert t["num_splits"].tolist() == [1, 0] and t["items"].shape[0] == 1
+
+
+def test_empty_batch():
+    p = pm.plan(np.zeros(0), np.zeros(0), np.zeros(0), np.zeros((0, 1)), num_pool_blocks=0,
+                num_q_heads=1, num_kv_heads=1, head_dim=64, dtype="bf16", scale=1.0)
+    t = p.tables()
+    assert t["items"].shape[0] == 0 and t["row_seq"].shape[0] == 0 and p.workspace_bytes >= 256
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "pmattn.h")).read()
+    declared = set(re.findall(r"\b(pmattn_[a-z_]+)\s*\(", header))
+    declared -= {"pmattn_plan_s"}
+    assert {"pmattn_plan", "pmattn_forward", "pmattn_merge_lse"} <= declared
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == {n for n, _, _ in _lib.SIGNATURES}
+    assert pm.version() == "0.1.0"
