@@ -9,9 +9,11 @@ head_dim 128, bf16, 16-token blocks, random non-contiguous block tables).
 One step = one ``pmattn_forward`` of the whole batch (tile tasks + merge) with
 inputs resident in HBM; the plan is built once per batch on the host (as a
 serving loop reuses it for every layer) and its host time is reported apart.
-Before each timed step a 512 MiB scratch write evicts L2 and the MALL, so KV
-blocks come from HBM; HIP events on the launch stream bracket the tasks pass
-and the merge pass of every step.
+Before each timed step a read sweep over a 1 GiB scratch buffer (four times
+the 256 MiB Infinity Cache) evicts L2 and the MALL, so KV blocks come from HBM.
+The sweep reads rather than writes: a write would leave dirty lines whose
+write-back the next kernel would pay for. HIP events on the launch stream
+bracket the tasks pass and the merge pass of every step.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -77,6 +79,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--num-kv-splits", type=int, default=None)
+    ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
@@ -86,6 +91,17 @@ def main():
     import torch
     import prefix_shared_paged_pmattn_amd as pm
     import workloads as wl
+
+    if args.copy_calibration:
+        # A copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel calibrate
+        # the counters against 1 GiB read + 1 GiB written per dispatch.
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(copy_bytes=1 << 30, dispatches=3)), flush=True)
+        return
 
     t0 = time.perf_counter()
     b = wl.config(args.config)
@@ -114,7 +130,7 @@ def main():
         return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table,
                        num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
                        num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
-                       scale=b.scale, num_kv_splits=b.num_kv_splits)
+                       scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus)
 
     plan_times = []
     for _ in range(20):
@@ -126,7 +142,11 @@ def main():
     ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     p.upload(ws, stream)
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)       # 1 GiB, read to evict caches
+    flush_sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def flush():
+        torch.sum(scratch, dim=0, dtype=torch.int64, out=flush_sink)
 
     # Validate every tensor once through the binding, then call the two C-ABI
     # passes with pre-marshalled arguments so that host overhead stays far
@@ -155,7 +175,7 @@ def main():
 
     for _ in range(args.warmup):
         if not args.no_flush:
-            scratch.zero_()
+            flush()
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -163,7 +183,7 @@ def main():
     w0 = time.perf_counter()
     for k in range(args.steps):
         if not args.no_flush:
-            scratch.zero_()
+            flush()
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0

@@ -22,9 +22,8 @@
 //     [g*d/4, (g+1)*d/4)  -> d/32 consecutive 16-byte loads;
 //   V operand, lane (i, g): channel 16t + i, keys 8g..8g+7 of the chunk,
 //     which the channel-major V block stores contiguously -> one 16-byte load.
-// K and V tiles are gathered through the block table (physical ids read once
-// per 64 blocks into a VGPR and broadcast with readlane); no contiguous copy
-// of the KV is ever formed (the K/V concatenation the XY-Serve referee report
+// K and V tiles are gathered through the block table (physical ids fetched
+// with scalar loads a chunk ahead); no contiguous copy of the KV is ever formed (the K/V concatenation the XY-Serve referee report
 // blames for the baseline's losses).
 //
 // Masks are row-wise (XY-Serve review, "Editorial extensions": one kernel for
@@ -44,6 +43,11 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ bf16x8 ld16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ void issue_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>
@@ -72,23 +76,37 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& ch, const uint16_t* __restr
   for (int t = 0; t < DT; ++t) ch.v[t] = ld16(vp + 16 * 16 * t);
 }
 
-template <int D, int NT, bool MASK>
-__device__ __forceinline__ void compute_chunk(Chunk<D>& ch, const bf16x8 (&qop)[NT][D / 32],
-                                              f32x4 (&o)[NT][D / 16], float (&m_run)[NT],
-                                              float (&l_run)[NT], const int (&pos)[NT], int c0,
-                                              int kv_end, float sl2, int g) {
-  constexpr int KS = D / 32, DT = D / 16;
-  const int kbase = c0 + 8 * g;  // key of this lane's first score slot
-  if (MASK) {
-    const int nv = kv_end - kbase;  // V lanes past the task's end must be zero
-    if (nv < 8) {
+// Zero the V lanes of keys at or past the task's end (only the last, partial
+// chunk has any; the masks are all-ones elsewhere): a masked key has weight
+// exactly 0, but 0 * NaN would still poison the PV product if the slot holds
+// garbage.
+template <int D>
+__device__ __forceinline__ void zero_tail_v(Chunk<D>& ch, int c0, int kv_end, int g) {
+  const int nv = kv_end - (c0 + 8 * g);
+  uint32_t keep[4];
 #pragma unroll
-      for (int t = 0; t < DT; ++t)
+  for (int w = 0; w < 4; ++w)
+    keep[w] = (2 * w + 1 < nv ? 0xFFFF0000u : 0u) | (2 * w < nv ? 0x0000FFFFu : 0u);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j >= nv) ch.v[t][j] = (__bf16)0.0f;
-    }
+  for (int t = 0; t < Chunk<D>::DT; ++t) {
+    uint4 u = __builtin_bit_cast(uint4, ch.v[t]);
+    u.x &= keep[0];
+    u.y &= keep[1];
+    u.z &= keep[2];
+    u.w &= keep[3];
+    ch.v[t] = __builtin_bit_cast(bf16x8, u);
   }
+}
+
+// One 32-key chunk: scores, row-wise causal mask, online softmax, PV.
+// The mask is applied unconditionally (a handful of selects per 32 keys) so
+// that the streaming loop has no data-dependent branches.
+template <int D, int NT>
+__device__ __forceinline__ void compute_chunk(const Chunk<D>& ch, const bf16x8 (&qop)[NT][D / 32],
+                                              f32x4 (&o)[NT][D / 16], float (&m_run)[NT],
+                                              float (&l_run)[NT], const int (&lim_base)[NT], int c0,
+                                              float sl2, int g) {
+  constexpr int KS = D / 32, DT = D / 16;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -98,11 +116,10 @@ __device__ __forceinline__ void compute_chunk(Chunk<D>& ch, const bf16x8 (&qop)[
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[1][s], qop[n][s], s1, 0, 0, 0);
     }
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    if (MASK) {
-      const int lim = min(pos[n] + 1, kv_end) - kbase;  // slots j < lim are visible
+    // slot j holds key c0 + 8g + j; visible iff key < min(pos + 1, kv_end)
+    const int lim = lim_base[n] - c0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sv[j] = (j < lim) ? sv[j] : kNegInf;
-    }
+    for (int j = 0; j < 8; ++j) sv[j] = (j < lim) ? sv[j] : kNegInf;
     float mx = sv[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
@@ -129,13 +146,50 @@ __device__ __forceinline__ void compute_chunk(Chunk<D>& ch, const bf16x8 (&qop)[
   }
 }
 
+// Read-only tables are read through the constant address space so that
+// wave-uniform indices turn into scalar loads: their waits count on lgkmcnt and
+// never drain the vector loads of the KV stream.
+typedef const int32_t __attribute__((address_space(4)))* cint_p;
+
+__device__ __forceinline__ pmattn_work_item load_item(const pmattn_work_item* items, int idx) {
+  const cint_p p = (cint_p)(items + idx);
+  pmattn_work_item it;
+  it.seq = p[0];
+  it.kv_head = p[1];
+  it.row_begin = p[2];
+  it.n_tok = p[3];
+  it.pos_begin = p[4];
+  it.kv_begin = p[5];
+  it.kv_end = p[6];
+  it.part = p[7];
+  return it;
+}
+
+// Decode-shaped tasks (one 16-row tile) keep two waves per SIMD so
+// that eight waves per CU keep KV loads in flight; the 64-row variant needs
+// the whole register file.
+#ifndef PMATTN_DECODE_DEPTH
+#define PMATTN_DECODE_DEPTH 2
+#endif
+#ifndef PMATTN_DECODE_WAVES
+#define PMATTN_DECODE_WAVES 2
+#endif
+template <int NT>
+struct WavesPerEu { static constexpr int value = NT == 1 ? PMATTN_DECODE_WAVES : 1; };
+// Chunks in flight per wave: 1 (occupancy hides latency) or 2 (explicit
+// double buffering).
+template <int NT>
+struct Depth { static constexpr int value = NT == 1 ? PMATTN_DECODE_DEPTH : 2; };
+
 template <int D, int NT>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))
+void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * 4 + wave;
   if (idx >= a.item_count) return;
-  const pmattn_work_item it = a.items[idx];
+  const pmattn_work_item it = load_item(a.items, idx);
   const int i = lane & 15, g = lane >> 4;
   const int G = a.group, hq = a.hq, hkv = a.hkv, kvh = it.kv_head;
   const int M = it.n_tok * G;
@@ -173,55 +227,69 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     for (int t = 0; t < DT; ++t) o[n][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  // Physical block ids of up to 64 consecutive logical blocks, one per lane.
-  const int32_t* bt_row = a.block_table + (int64_t)it.seq * a.bt_stride;
-  const int nblk_end = (it.kv_end + 15) >> 4;
-  int ids_base = it.kv_begin >> 4;
-  int ids = (ids_base + lane < nblk_end) ? bt_row[ids_base + lane] : 0;
-  auto block_id = [&](int bi) -> int {
-    if (bi - ids_base >= 64) {
-      ids_base = bi;
-      ids = (ids_base + lane < nblk_end) ? bt_row[ids_base + lane] : 0;
-    }
-    return __builtin_amdgcn_readlane(ids, bi - ids_base);
-  };
-  auto chunk_blocks = [&](int c, int& b0, int& b1) {
+  // Physical block ids, fetched with scalar loads one chunk ahead of use.
+  const cint_p bt_row = (cint_p)(a.block_table + (int64_t)it.seq * a.bt_stride);
+  const int last_blk = ((it.kv_end + 15) >> 4) - 1;
+  auto chunk_ids = [&](int c, int& b0, int& b1) {
     const int bi = c >> 4;
-    b0 = block_id(bi);
-    b1 = (bi + 1 < nblk_end) ? block_id(bi + 1) : b0;
+    b0 = bt_row[min(bi, last_blk)];
+    b1 = bt_row[min(bi + 1, last_blk)];
   };
 
   const float sl2 = a.scale_log2;
   const int kv_end = it.kv_end;
-  const int first_pos = it.pos_begin;
-  Chunk<D> A, B;
-  int c0 = it.kv_begin, b0, b1;
-  chunk_blocks(c0, b0, b1);
-  load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
-  // Two named buffers: while one chunk is computed the next one is in flight.
-  // The prefetch is unconditional; past the last chunk it re-reads the current
-  // one (an L2 hit, same block ids) so that the wait counts stay static.
-  for (;;) {
-    int cn = c0 + 32;
-    bool more = cn < kv_end;
-    if (more) chunk_blocks(cn, b0, b1);
-    load_chunk<D>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
-    if (c0 + 31 > first_pos || c0 + 32 > kv_end)
-      compute_chunk<D, NT, true>(A, qop, o, m_run, l_run, pos, c0, kv_end, sl2, g);
-    else
-      compute_chunk<D, NT, false>(A, qop, o, m_run, l_run, pos, c0, kv_end, sl2, g);
-    if (!more) break;
-    c0 = cn;
-    cn = c0 + 32;
-    more = cn < kv_end;
-    if (more) chunk_blocks(cn, b0, b1);
+  // per row: keys below min(pos + 1, kv_end) are visible; lanes of group g see
+  // keys c0 + 8g + j, so fold 8g in once
+  int lim_base[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) lim_base[n] = min(pos[n] + 1, kv_end) - 8 * g;
+  if constexpr (Depth<NT>::value == 1) {
+    // One buffer per wave; latency is hidden by the other waves on the SIMD.
+    const int nch = (kv_end - it.kv_begin + 31) >> 5;
+    Chunk<D> A;
+    int c0 = it.kv_begin, b0, b1;
+    chunk_ids(c0, b0, b1);
+    for (int k = 0; k < nch; ++k) {
+      load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
+      chunk_ids(c0 + 32, b0, b1);
+      zero_tail_v<D>(A, c0, kv_end, g);
+      compute_chunk<D, NT>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g);
+      c0 += 32;
+    }
+  } else {
+    // Software pipeline over pairs of 32-key chunks with two register buffers:
+    // while one buffer is consumed the other one's loads are in flight. The
+    // body has no data-dependent branch. An odd chunk count leaves one
+    // trailing compute on a chunk past kv_end: every score there is masked and
+    // every V lane zeroed, so it adds exactly nothing. Loads past the last
+    // chunk re-read the last chunk's blocks (cache hits), never memory
+    // outside them.
+    const int nch = (kv_end - it.kv_begin + 31) >> 5;
+    const int npairs = (nch + 1) >> 1;
+    Chunk<D> A, B;
+    int c0 = it.kv_begin, b0, b1;
+    chunk_ids(c0, b0, b1);
     load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
-    if (c0 + 31 > first_pos || c0 + 32 > kv_end)
-      compute_chunk<D, NT, true>(B, qop, o, m_run, l_run, pos, c0, kv_end, sl2, g);
-    else
-      compute_chunk<D, NT, false>(B, qop, o, m_run, l_run, pos, c0, kv_end, sl2, g);
-    if (!more) break;
-    c0 = cn;
+    chunk_ids(c0 + 32, b0, b1);
+    load_chunk<D>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
+    // issue_barrier() pins each chunk's loads to the point where they are
+    // issued (a compiler memory barrier plus a scheduling barrier), so that the
+    // optimizer can neither sink them next to their first use nor hoist the
+    // other buffer's math above them (either would undo the prefetch).
+    issue_barrier();
+    for (int k = 0; k < npairs; ++k) {
+      chunk_ids(c0 + 64, b0, b1);
+      zero_tail_v<D>(A, c0, kv_end, g);
+      compute_chunk<D, NT>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g);
+      load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
+      issue_barrier();
+      chunk_ids(c0 + 96, b0, b1);
+      zero_tail_v<D>(B, c0 + 32, kv_end, g);
+      compute_chunk<D, NT>(B, qop, o, m_run, l_run, lim_base, c0 + 32, sl2, g);
+      load_chunk<D>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
+      issue_barrier();
+      c0 += 64;
+    }
   }
 
   // Epilogue: lane (i, g) owns channels 16t + 4g + r of row 16n + i.

@@ -91,10 +91,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 // consecutive channels. out = sum_p w_p O_p / sum_p w_p with
 // w_p = exp(lse_p - max lse); lse = max + ln sum w_p. Empty partials (-inf)
 // weigh 0; if all are empty the output is 0 and lse is -inf.
+// Latency-lean: lane p loads lse_p (64 partials per round), the max and the
+// weight sum are wave reductions, and the partial-output loads are unrolled
+// so that a merge costs about two memory round trips, not one per partial.
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int V = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + wave;
   if (w >= a.count) return;
   int64_t rec0, stride;
@@ -115,19 +119,42 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     qh = w - (int)row * a.hq;
   }
   float mx = kNegInf;
-  for (int p = 0; p < np; ++p) mx = fmaxf(mx, a.part_lse[rec0 + p * stride]);
+  for (int p0 = 0; p0 < np; p0 += 64)
+    if (p0 + lane < np) mx = fmaxf(mx, a.part_lse[rec0 + (p0 + lane) * stride]);
+  mx = wave_max(mx);
   float acc[V], tot = 0.f;
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
   if (mx != kNegInf) {
-    for (int p = 0; p < np; ++p) {
-      const int64_t rec = rec0 + p * stride;
-      const float l = a.part_lse[rec];
-      const float wt = (l == kNegInf) ? 0.f : expf(l - mx);
-      tot += wt;
-      const float* src = a.part_o + rec * D + lane * V;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+      const int pn = min(64, np - p0);
+      float wt = 0.f;
+      if (lane < pn) {
+        const float l = a.part_lse[rec0 + (p0 + lane) * stride];
+        wt = (l == kNegInf) ? 0.f : expf(l - mx);
+      }
+      tot += wave_sum(wt);
+      int q = 0;
+      for (; q + 8 <= pn; q += 8) {
+        float src[8][V];
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] = fmaf(wt, src[v], acc[v]);
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int v = 0; v < V; ++v)
+            src[u][v] = a.part_o[(rec0 + (int64_t)(p0 + q + u) * stride) * D + lane * V + v];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wu = __shfl(wt, q + u);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[v] = fmaf(wu, src[u][v], acc[v]);
+        }
+      }
+      for (; q < pn; ++q) {
+        const float wu = __shfl(wt, q);
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          acc[v] = fmaf(wu, a.part_o[(rec0 + (int64_t)(p0 + q) * stride) * D + lane * V + v], acc[v]);
+      }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
