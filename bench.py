@@ -41,6 +41,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(config_idx):
+    """HBM bytes per launch of the tasks kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, calibrated by a 1 GiB copy),
+    or None when there is none for this workload or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    prof = {2: "attn_bf16_decode_64seq.md"}.get(config_idx)
+    if prof is None:
+        return None
+    path = os.path.join(ROOT, "profiles", prof)
+    src = os.path.join(ROOT, "prefix_shared_paged_pmattn_amd", "csrc", "attn_bf16.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes", "kernel_source")))
+    if fields.get("kernel_source_sha256_16") != sha:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(batch, work, min_seconds=10.0):
     """Time the fp64 oracle on the same batch (whole batch, repeated until
     ``min_seconds`` of CPU work); returns a dict in the metric's unit."""
@@ -213,7 +235,9 @@ def main():
         unit = "GB/s"
         achieved = work["bytes"] / (ms_task * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS, traffic=None)
+                    frac=achieved / HBM_PEAK_GBS,
+                    traffic=None if args.num_kv_splits is not None or args.num_cus
+                    else measured_traffic(args.config))
     log(f"[bench] value {value:.1f} {unit}; dominant kernel (tasks pass) {achieved:.1f} {roof['unit']} "
         f"= {100 * roof['frac']:.1f}% of {roof['bound']} peak")
 
