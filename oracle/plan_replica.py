@@ -22,8 +22,9 @@ import numpy as np
 from .attention import partition_bounds
 
 BLOCK = 16
-MAX_TASK_ROWS = 64
-CLASS_ROWS = (16, 32, 64)
+MAX_WAVE_ROWS = 64
+MAX_TASK_ROWS = 128
+CLASS_ROWS = (16, 32, 64, 128)
 TASKS_PER_CU = 32
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
@@ -39,16 +40,23 @@ def row_tables(q_len, q_start):
 
 
 def token_tiles(q_len, q_start, group):
-    """Runs of query tokens one task holds: floor(64 / G) tokens (at least 1);
-    returns (seq, first token, tokens, rows class, kv end of the run)."""
-    per = max(1, MAX_TASK_ROWS // group)
+    """Runs of query tokens one task holds: a sequence with q_len * G <= 64
+    rows is one tile (rows class 16, 32 or 64); a longer one is cut into runs
+    of floor(128 / G) tokens (at least 1), rows class 128. Returns
+    (seq, first token, tokens, rows class, kv end of the run)."""
     tiles = []
     for s, (ql, qs) in enumerate(zip(q_len, q_start)):
-        for t0 in range(0, int(ql), per):
-            nt = min(per, int(ql) - t0)
-            rows = nt * group
-            cls = next(c for c in CLASS_ROWS if rows <= c)
-            tiles.append((s, t0, nt, cls, int(qs) + t0 + nt))
+        ql, qs = int(ql), int(qs)
+        if ql == 0:
+            continue
+        if ql * group <= MAX_WAVE_ROWS:
+            cls = next(c for c in CLASS_ROWS if ql * group <= c)
+            tiles.append((s, 0, ql, cls, qs + ql))
+            continue
+        per = max(1, MAX_TASK_ROWS // group)
+        for t0 in range(0, ql, per):
+            nt = min(per, ql - t0)
+            tiles.append((s, t0, nt, MAX_TASK_ROWS, qs + t0 + nt))
     return tiles
 
 

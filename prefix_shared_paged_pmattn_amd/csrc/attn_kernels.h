@@ -45,6 +45,7 @@ struct MergeArgs {
 
 // Host launchers (forward.hip).
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
 

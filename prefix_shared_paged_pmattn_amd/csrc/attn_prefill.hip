@@ -1,0 +1,333 @@
+// bf16 prefill/verify tile kernel for gfx950: one workgroup per 128-row task.
+//
+// A task here is up to 128 query rows of one sequence and one kv head (128/G
+// tokens x the G query heads of the group) against one KV partition: the
+// matmul-softmax-matmul tile of the XY-Serve meta-kernel (XY-Serve pith
+// review, "What carries the argument"), laid out for CDNA4:
+//
+// * 4 waves x 32 rows. All four share the kv head, so each 64-key chunk of
+//   K and V is gathered through the block table once per workgroup into LDS
+//   (double-buffered, one barrier per chunk) and read by every wave from
+//   there: the K/V concatenation the XY-Serve referee report blames for the
+//   baseline's prefix-reuse losses never happens.
+// * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16. Each lane
+//   owns one query row (l % 32) and 16 keys of every 32-key score tile. The
+//   keys are permuted inside a tile (bits 2 and 3 of the slot swapped) so that
+//   the P operand of the PV product is read straight from the S accumulator
+//   registers and every V operand is one 16-byte LDS read of 8 consecutive
+//   keys of one channel (V blocks are channel-major).
+// * Online softmax in fp32 with exp2 (scale*log2e folded in). The O rescale
+//   is lazy: the running reference max moves only when some row's max grows by
+//   more than 2^8, which after the first chunks almost never happens; P stays
+//   below 2^8 and the final O/l is exact either way (online softmax equals
+//   softmax: "Assumptions & free parameters").
+// * Row-wise causal masks ("Editorial extensions"): chunks wholly visible to
+//   every row of the task take an unmasked path (Figure 11, mask-aware
+//   computation); V lanes of keys past the task's end are zeroed when the chunk
+//   is staged, so pool slots no row can see may hold NaN.
+// * Two workgroups per CU (2 waves per SIMD), so that one wave's softmax VALU
+//   overlaps the other wave's MFMA.
+#include "attn_kernels.h"
+
+namespace pmattn {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+// lazy rescale threshold, in log2 units of the scaled scores
+constexpr float kRescaleLog2 = 8.0f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef const int32_t __attribute__((address_space(4)))* cint_p;
+
+template <int D>
+struct Cfg {
+  static constexpr int CHUNK = 64;            // keys per iteration (4 blocks)
+  static constexpr int KSTEPS = D / 16;       // QK k-steps of 16 channels
+  static constexpr int DT = D / 32;           // 32-channel output tiles
+  static constexpr int KROW = D + 8;          // LDS K row (bf16), +16 B pad: conflict-free reads
+  static constexpr int VROW = CHUNK + 8;      // LDS V row (bf16), +16 B pad
+  static constexpr int K_ELEMS = CHUNK * KROW;
+  static constexpr int STAGE = K_ELEMS + D * VROW;
+  static constexpr int PIECES = D / 32;       // 16-byte pieces per thread for K (and for V)
+};
+
+__device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ void issue_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ pmattn_work_item load_item(const pmattn_work_item* items, int idx) {
+  const cint_p p = (cint_p)(items + idx);
+  pmattn_work_item it;
+  it.seq = p[0];
+  it.kv_head = p[1];
+  it.row_begin = p[2];
+  it.n_tok = p[3];
+  it.pos_begin = p[4];
+  it.kv_begin = p[5];
+  it.kv_end = p[6];
+  it.part = p[7];
+  return it;
+}
+
+// Global -> register staging of one 64-key chunk (4 blocks): thread `tid`
+// carries PIECES 16-byte pieces of K and of V; consecutive threads read
+// consecutive 16-byte pieces of a block, so every wave load is 1 KiB
+// contiguous.
+template <int D>
+struct Stage {
+  uint4 k[Cfg<D>::PIECES];
+  uint4 v[Cfg<D>::PIECES];
+};
+
+template <int D>
+__device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restrict__ kpool,
+                                           const uint16_t* __restrict__ vpool, const int (&blk)[4],
+                                           int nvalid_blocks, int kvh, int hkv, int tid) {
+  constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;  // pieces per 4 KiB (d=128) block
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    const int q = tid + 256 * u;
+    const int b = q / PER_BLOCK, r = q % PER_BLOCK;
+    if (b < nvalid_blocks) {
+      const int64_t base = (int64_t)blk[b] * hkv + kvh;
+      // K block [16 tokens][D]: token r / (D/8), channel chunk r % (D/8)
+      st.k[u] = *reinterpret_cast<const uint4*>(kpool + (base * 16 + r / (D / 8)) * D + 8 * (r % (D / 8)));
+      // V block [D][16 tokens]: channel r / 2, half r % 2
+      st.v[u] = *reinterpret_cast<const uint4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
+    } else {
+      st.k[u] = make_uint4(0, 0, 0, 0);
+      st.v[u] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Register -> LDS. V pieces of keys >= kv_end are zeroed (only in the chunk
+// that holds the task's end).
+template <int D>
+__device__ __forceinline__ void stage_store(uint16_t* lds, Stage<D>& st, int c0, int kv_end, int tid) {
+  constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;
+  uint16_t* kl = lds;
+  uint16_t* vl = lds + Cfg<D>::K_ELEMS;
+  const bool tail = c0 + Cfg<D>::CHUNK > kv_end;
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    const int q = tid + 256 * u;
+    const int b = q / PER_BLOCK, r = q % PER_BLOCK;
+    *reinterpret_cast<uint4*>(kl + (16 * b + r / (D / 8)) * Cfg<D>::KROW + 8 * (r % (D / 8))) = st.k[u];
+    uint4 v = st.v[u];
+    if (tail) {
+      const int nv = kv_end - (c0 + 16 * b + 8 * (r % 2));  // keys of this piece below kv_end
+      const uint32_t k0 = (0 < nv ? 0xFFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
+      const uint32_t k1 = (2 < nv ? 0xFFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
+      const uint32_t k2 = (4 < nv ? 0xFFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u);
+      const uint32_t k3 = (6 < nv ? 0xFFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u);
+      v.x &= k0;
+      v.y &= k1;
+      v.z &= k2;
+      v.w &= k3;
+    }
+    *reinterpret_cast<uint4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = v;
+  }
+}
+
+// Key offset (within a 64-key chunk) of score register r of tile kt held by
+// lane half h: slot 8*(r/4) + 4h + r%4 of the 32x32 accumulator, with slot
+// bits 2 and 3 swapped.
+__device__ __forceinline__ int key_off(int kt, int r, int h) {
+  return 32 * kt + 16 * (r >> 3) + 8 * h + 4 * ((r >> 2) & 1) + (r & 3);
+}
+
+template <int D, bool MASK>
+__device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 (&qop)[D / 16],
+                                              f32x16 (&o)[D / 32], float& m_used, float& l_part,
+                                              int lim, int c0, float sl2, int i32, int h) {
+  constexpr int KSTEPS = D / 16, DT = D / 32;
+  const uint16_t* kl = lds;
+  const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
+  // S^T for two 32-key tiles; A-operand row i32 holds key kappa(i32): slot bits 2,3 swapped
+  const int kap = (i32 & ~12) | ((i32 & 4) << 1) | ((i32 & 8) >> 1);
+  f32x16 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x16 acc = {};
+    const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(kr + 8 * st), qop[st], acc, 0, 0, 0);
+    s[kt] = acc;
+  }
+  if (MASK) {
+    // visible iff key < lim (lim = min(pos + 1, kv_end) - c0 for this lane's row)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = key_off(kt, r, h) < lim ? s[kt][r] : kNegInf;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // lazy rescale: move the reference max only when it grows by > 2^8 somewhere
+  const bool grow = mx != kNegInf && (m_used == kNegInf || (mx - m_used) * sl2 > kRescaleLog2);
+  if (__any(grow)) {
+    const float m_new = fmaxf(m_used, mx);
+    const float alpha = m_used == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2);
+    l_part *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    m_used = m_new;
+  }
+  const float ms = m_used == kNegInf ? 0.f : m_used * sl2;
+  bf16x8 pb[2][2];
+  float ps = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    f32x8 p0, p1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p0[e] = __builtin_amdgcn_exp2f(s[kt][e] * sl2 - ms);
+      p1[e] = __builtin_amdgcn_exp2f(s[kt][8 + e] * sl2 - ms);
+      ps += p0[e] + p1[e];
+    }
+    pb[kt][0] = __builtin_convertvector(p0, bf16x8);
+    pb[kt][1] = __builtin_convertvector(p1, bf16x8);
+  }
+  l_part += ps;
+  // O^T += V^T . P^T: A = V^T (channel 32t + i32, keys 32kt + 16kk + 8h .. +8)
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const uint16_t* vr = vl + (32 * t + i32) * Cfg<D>::VROW + 8 * h;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr + 32 * kt + 16 * kk), pb[kt][kk], o[t], 0, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_prefill_kernel(AttnArgs a) {
+  constexpr int KSTEPS = D / 16, DT = D / 32, CHUNK = Cfg<D>::CHUNK;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int i32 = lane & 31, h = lane >> 5;
+  if ((int)blockIdx.x >= a.item_count) return;  // uniform over the workgroup
+  const pmattn_work_item it = load_item(a.items, blockIdx.x);
+  const int G = a.group, hq = a.hq, hkv = a.hkv, kvh = it.kv_head;
+  const int M = it.n_tok * G;
+  const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ kpool = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* __restrict__ vpool = static_cast<const uint16_t*>(a.v_pool);
+
+  // this lane's query row and its Q operand (B of QK): channels (D/2)h + 8s
+  const int m = 32 * wave + i32;
+  const bool row_valid = m < M;
+  const int t = row_valid ? m / G : 0;
+  const int pos = row_valid ? it.pos_begin + t : -1;
+  bf16x8 qop[KSTEPS];
+  if (row_valid) {
+    const uint16_t* src = qp + ((int64_t)(it.row_begin + t) * hq + kvh * G + (m - t * G)) * D + (D / 2) * h;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + 8 * s));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qop[s] = (bf16x8)(__bf16)0.0f;
+  }
+  f32x16 o[DT];
+#pragma unroll
+  for (int tt = 0; tt < DT; ++tt) o[tt] = (f32x16){};
+  float m_used = kNegInf, l_part = 0.f;
+
+  const cint_p bt_row = (cint_p)(a.block_table + (int64_t)it.seq * a.bt_stride);
+  const int kv_end = it.kv_end;
+  const int last_blk = ((kv_end + 15) >> 4) - 1;
+  const int nch = (kv_end - it.kv_begin + CHUNK - 1) / CHUNK;
+  const int min_pos = it.pos_begin;  // first token of the task
+  const int row_lim = min(pos + 1, kv_end);
+  const float sl2 = a.scale_log2;
+
+  auto chunk_blocks = [&](int c0, int (&blk)[4]) -> int {
+    const int bi = c0 >> 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) blk[b] = bt_row[min(bi + b, last_blk)];
+    return min(4, last_blk - bi + 1);
+  };
+
+  Stage<D> stg;
+  int blk[4];
+  int c0 = it.kv_begin;
+  int nvb = chunk_blocks(c0, blk);
+  stage_load<D>(stg, kpool, vpool, blk, nvb, kvh, hkv, tid);
+  stage_store<D>(lds, stg, c0, kv_end, tid);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c, c0 += CHUNK) {
+    const bool more = c + 1 < nch;
+    if (more) {
+      nvb = chunk_blocks(c0 + CHUNK, blk);
+      stage_load<D>(stg, kpool, vpool, blk, nvb, kvh, hkv, tid);
+    }
+    issue_barrier();
+    const uint16_t* cur = lds + (c & 1) * Cfg<D>::STAGE;
+    // every row of the task sees every key of the chunk: no mask needed
+    if (c0 + CHUNK - 1 <= min_pos && c0 + CHUNK <= kv_end)
+      compute_chunk<D, false>(cur, qop, o, m_used, l_part, 0, c0, sl2, i32, h);
+    else
+      compute_chunk<D, true>(cur, qop, o, m_used, l_part, row_lim - c0, c0, sl2, i32, h);
+    if (more) stage_store<D>(lds + ((c + 1) & 1) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
+    __syncthreads();
+  }
+
+  // epilogue: lane (i32, h) owns channels 32t + 8q + 4h + (0..3) of its row
+  const float l = l_part + __shfl_xor(l_part, 32);
+  if (!row_valid) return;
+  const int64_t row = it.row_begin + t;
+  const int qh = kvh * G + (m - t * G);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float lse = l > 0.f ? m_used * a.scale + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  if (it.part < 0) {
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + (row * hq + qh) * D + 4 * h;
+#pragma unroll
+    for (int tt = 0; tt < DT; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {o[tt][4 * q] * inv, o[tt][4 * q + 1] * inv, o[tt][4 * q + 2] * inv, o[tt][4 * q + 3] * inv};
+        *reinterpret_cast<uint2*>(dst + 32 * tt + 8 * q) = __builtin_bit_cast(uint2, __builtin_convertvector(v, bf16x4));
+      }
+    if (a.lse && h == 0) a.lse[row * hq + qh] = lse;
+  } else {
+    const int64_t rec = (int64_t)it.part + m;
+    float* dst = a.part_o + rec * D + 4 * h;
+#pragma unroll
+    for (int tt = 0; tt < DT; ++tt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {o[tt][4 * q] * inv, o[tt][4 * q + 1] * inv, o[tt][4 * q + 2] * inv, o[tt][4 * q + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst + 32 * tt + 8 * q) = v;
+      }
+    if (h == 0) a.part_lse[rec] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st) {
+  if (a.item_count <= 0) return hipSuccess;
+  const dim3 grid(a.item_count), block(256);
+  if (head_dim == 128)
+    hipLaunchKernelGGL((attn_prefill_kernel<128>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_prefill_kernel<64>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace pmattn

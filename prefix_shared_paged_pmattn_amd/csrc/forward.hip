@@ -97,8 +97,13 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   for (size_t c = 0; c < P.class_rows.size(); ++c) {
     a.items = items + P.class_begin[c];
     a.item_count = P.class_begin[c + 1] - P.class_begin[c];
-    hipError_t e = P.dtype == PMATTN_BF16 ? launch_attn_bf16(P.head_dim, P.class_rows[c], a, st)
-                                          : launch_attn_f32(P.head_dim, a, st);
+    hipError_t e;
+    if (P.dtype != PMATTN_BF16)
+      e = launch_attn_f32(P.head_dim, a, st);
+    else if (P.class_rows[c] > kMaxWaveRows)
+      e = launch_attn_prefill(P.head_dim, a, st);
+    else
+      e = launch_attn_bf16(P.head_dim, P.class_rows[c], a, st);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   }
   return PMATTN_OK;

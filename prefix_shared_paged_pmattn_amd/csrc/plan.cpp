@@ -77,7 +77,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (d->num_q_heads % d->num_kv_heads)
     return fail(PMATTN_E_INVALID, "num_q_heads must be a multiple of num_kv_heads");
   const int G = d->num_q_heads / d->num_kv_heads;
-  if (G > kMaxTaskRows) return fail(PMATTN_E_UNSUPPORTED, "num_q_heads / num_kv_heads must be <= 64");
+  if (G > kMaxWaveRows) return fail(PMATTN_E_UNSUPPORTED, "num_q_heads / num_kv_heads must be <= 64");
   if (!std::isfinite(d->scale) || !(d->scale > 0.f))
     return fail(PMATTN_E_INVALID, "scale must be finite and > 0");
   if (d->num_kv_splits < 0 || d->num_kv_splits > kMaxSplits)
@@ -131,14 +131,22 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   }
 
   // ---- tiles: runs of query tokens whose G heads fit one task --------------
-  const int tok_per_task = std::max(1, kMaxTaskRows / G);
+  // A sequence whose rows fit one wave task (q_len * G <= 64) is one tile;
+  // longer ones are cut into runs of 128/G tokens for the workgroup kernel.
+  const int tok_per_wg = std::max(1, kMaxTaskRows / G);
   std::vector<Tile> tiles;
   std::vector<int32_t> row_off(B + 1, 0);
   for (int s = 0; s < B; ++s) row_off[s + 1] = row_off[s] + d->q_len[s];
   for (int s = 0; s < B; ++s) {
-    for (int t0 = 0; t0 < d->q_len[s]; t0 += tok_per_task) {
-      const int nt = std::min(tok_per_task, d->q_len[s] - t0);
-      tiles.push_back(Tile{s, t0, nt, class_of_rows(nt * G), d->q_start[s] + t0 + nt});
+    const int ql = d->q_len[s];
+    if (ql == 0) continue;
+    if ((int64_t)ql * G <= kMaxWaveRows) {
+      tiles.push_back(Tile{s, 0, ql, class_of_rows(ql * G), d->q_start[s] + ql});
+      continue;
+    }
+    for (int t0 = 0; t0 < ql; t0 += tok_per_wg) {
+      const int nt = std::min(tok_per_wg, ql - t0);
+      tiles.push_back(Tile{s, t0, nt, kNumClasses - 1, d->q_start[s] + t0 + nt});
     }
   }
 

@@ -12,11 +12,15 @@
 namespace pmattn {
 
 constexpr int kBlock = 16;
-// Query rows (tokens x heads of one GQA group) one task may hold; tile-shape
-// classes are 16, 32 and 64 rows (one, two or four 16-row MFMA column tiles).
-constexpr int kMaxTaskRows = 64;
-constexpr int kNumClasses = 3;
-constexpr int kClassRows[kNumClasses] = {16, 32, 64};
+// Query rows (tokens x heads of one GQA group) a task may hold. Tasks of at
+// most 64 rows run one per wave (classes 16, 32, 64: one, two or four 16-row
+// MFMA column tiles); sequences with more rows than that are cut into
+// 128-row tasks that run one per workgroup (4 waves x 32 rows, K/V staged in
+// LDS).
+constexpr int kMaxWaveRows = 64;
+constexpr int kMaxTaskRows = 128;
+constexpr int kNumClasses = 4;
+constexpr int kClassRows[kNumClasses] = {16, 32, 64, 128};
 constexpr int kMaxSplits = 256;
 constexpr size_t kAlign = 256;
 

@@ -40,6 +40,11 @@ def _batch_cases():
         "many-splits-empty-parts": (dict(hq=8, hkv=2, d=128), [S(q_len=1, seq_len=40), S(q_len=4, seq_len=200)], 64),
         "position-zero": (dict(hq=4, hkv=2, d=128), [S(q_len=1, seq_len=1, q_start=0), S(q_len=4, seq_len=4, q_start=0)], 0),
         "keys-beyond-last-query": (dict(hq=8, hkv=2, d=128), [S(q_len=3, seq_len=90, q_start=10)], 0),
+        # workgroup (128-row) tasks: partial records, long MHA runs, d=64, tiny contexts
+        "prefill-wg-splits": (dict(hq=8, hkv=2, d=128), [S(q_len=100, seq_len=300, q_start=200), S(q_len=65, seq_len=65)], 3),
+        "prefill-mha-long": (dict(hq=2, hkv=2, d=128), [S(q_len=200, seq_len=260, q_start=60)], 0),
+        "prefill-d64-g8": (dict(hq=16, hkv=2, d=64), [S(q_len=33, seq_len=50, q_start=17), S(q_len=9, seq_len=9)], 0),
+        "prefill-wg-tail-in-first-chunk": (dict(hq=8, hkv=2, d=128), [S(q_len=20, seq_len=23, q_start=3)], 0),
     }
 
 
