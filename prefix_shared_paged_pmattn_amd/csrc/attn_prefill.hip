@@ -5,7 +5,7 @@
 // matmul-softmax-matmul tile of the XY-Serve meta-kernel (XY-Serve pith
 // review, "What carries the argument"), laid out for CDNA4:
 //
-// * 4 waves x 32 rows. All four share the kv head, so each 64-key chunk of
+// * 4 waves x 32 rows. All four share the kv head, so each 32-key chunk of
 //   K and V is gathered through the block table once per workgroup into LDS
 //   (double-buffered, one barrier per chunk) and read by every wave from
 //   there: the K/V concatenation the XY-Serve referee report blames for the
@@ -25,8 +25,10 @@
 //   every row of the task take an unmasked path (Figure 11, mask-aware
 //   computation); V lanes of keys past the task's end are zeroed when the chunk
 //   is staged, so pool slots no row can see may hold NaN.
-// * Two workgroups per CU (2 waves per SIMD), so that one wave's softmax VALU
-//   overlaps the other wave's MFMA.
+// * Three waves per SIMD (168 VGPRs, 37 KiB of LDS per workgroup), so that
+//   LDS latency and one wave's softmax VALU hide behind the other waves' MFMA.
+//   Measured on the few-shot workload: 32-key chunks at 3 waves/SIMD beat
+//   64-key chunks at 2 waves/SIMD by 9%; 4 waves/SIMD spills.
 #include "attn_kernels.h"
 
 namespace pmattn {
@@ -40,16 +42,32 @@ constexpr float kRescaleLog2 = 8.0f;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef const int32_t __attribute__((address_space(4)))* cint_p;
 
+// Tuning knobs (compile-time); the defaults are the measured best.
+#ifndef PMATTN_PF_CHUNK
+#define PMATTN_PF_CHUNK 32
+#endif
+#ifndef PMATTN_PF_WAVES
+#define PMATTN_PF_WAVES 3
+#endif
+#ifndef PMATTN_PF_TILE_OUTER
+#define PMATTN_PF_TILE_OUTER 1
+#endif
+#ifndef PMATTN_PF_KEEP
+#define PMATTN_PF_KEEP 0
+#endif
+
 template <int D>
 struct Cfg {
-  static constexpr int CHUNK = 64;            // keys per iteration (4 blocks)
+  static constexpr int CHUNK = PMATTN_PF_CHUNK;   // keys per iteration (CHUNK/16 blocks)
+  static constexpr int NBLK = CHUNK / 16;
+  static constexpr int NTILE = CHUNK / 32;        // 32-key score tiles per chunk
   static constexpr int KSTEPS = D / 16;       // QK k-steps of 16 channels
   static constexpr int DT = D / 32;           // 32-channel output tiles
   static constexpr int KROW = D + 8;          // LDS K row (bf16), +16 B pad: conflict-free reads
   static constexpr int VROW = CHUNK + 8;      // LDS V row (bf16), +16 B pad
   static constexpr int K_ELEMS = CHUNK * KROW;
   static constexpr int STAGE = K_ELEMS + D * VROW;
-  static constexpr int PIECES = D / 32;       // 16-byte pieces per thread for K (and for V)
+  static constexpr int PIECES = D * CHUNK / 2048;  // 16-byte pieces per thread for K (and for V)
 };
 
 __device__ __forceinline__ bf16x8 lds16(const uint16_t* p) {
@@ -86,52 +104,53 @@ struct Stage {
 
 template <int D>
 __device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restrict__ kpool,
-                                           const uint16_t* __restrict__ vpool, const int (&blk)[4],
-                                           int nvalid_blocks, int kvh, int hkv, int tid) {
-  constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;  // pieces per 4 KiB (d=128) block
+                                           const uint16_t* __restrict__ vpool, const int (&blk)[Cfg<D>::NBLK],
+                                           int kvh, int hkv, int tid) {
+  constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;  // 16-byte pieces per block
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     const int q = tid + 256 * u;
     const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-    if (b < nvalid_blocks) {
-      const int64_t base = (int64_t)blk[b] * hkv + kvh;
-      // K block [16 tokens][D]: token r / (D/8), channel chunk r % (D/8)
-      st.k[u] = *reinterpret_cast<const uint4*>(kpool + (base * 16 + r / (D / 8)) * D + 8 * (r % (D / 8)));
-      // V block [D][16 tokens]: channel r / 2, half r % 2
-      st.v[u] = *reinterpret_cast<const uint4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
-    } else {
-      st.k[u] = make_uint4(0, 0, 0, 0);
-      st.v[u] = make_uint4(0, 0, 0, 0);
-    }
+    const int64_t base = (int64_t)blk[b] * hkv + kvh;
+    // K block [16 tokens][D]: token r / (D/8), channel chunk r % (D/8)
+    st.k[u] = *reinterpret_cast<const uint4*>(kpool + (base * 16 + r / (D / 8)) * D + 8 * (r % (D / 8)));
+    // V block [D][16 tokens]: channel r / 2, half r % 2
+    st.v[u] = *reinterpret_cast<const uint4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
   }
 }
 
-// Register -> LDS. V pieces of keys >= kv_end are zeroed (only in the chunk
-// that holds the task's end).
+// Keeps the enclosing uniform branch a real branch: the compiler may not
+// if-convert (speculate) a block containing it, so the rarely needed masking
+// code runs only when its condition holds.
+__device__ __forceinline__ void keep_branch() { asm volatile(""); }
+
+// Register -> LDS. In the chunk that holds the task's end, V pieces of keys
+// >= kv_end are zeroed first (chunks past the last block re-read the last
+// block; their keys are >= kv_end as well).
 template <int D>
 __device__ __forceinline__ void stage_store(uint16_t* lds, Stage<D>& st, int c0, int kv_end, int tid) {
   constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;
   uint16_t* kl = lds;
   uint16_t* vl = lds + Cfg<D>::K_ELEMS;
-  const bool tail = c0 + Cfg<D>::CHUNK > kv_end;
+  if (c0 + Cfg<D>::CHUNK > kv_end) {
+    keep_branch();
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int q = tid + 256 * u;
+      const int b = q / PER_BLOCK, r = q % PER_BLOCK;
+      const int nv = kv_end - (c0 + 16 * b + 8 * (r % 2));  // keys of this piece below kv_end
+      st.v[u].x &= (0 < nv ? 0xFFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
+      st.v[u].y &= (2 < nv ? 0xFFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
+      st.v[u].z &= (4 < nv ? 0xFFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u);
+      st.v[u].w &= (6 < nv ? 0xFFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u);
+    }
+  }
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     const int q = tid + 256 * u;
     const int b = q / PER_BLOCK, r = q % PER_BLOCK;
     *reinterpret_cast<uint4*>(kl + (16 * b + r / (D / 8)) * Cfg<D>::KROW + 8 * (r % (D / 8))) = st.k[u];
-    uint4 v = st.v[u];
-    if (tail) {
-      const int nv = kv_end - (c0 + 16 * b + 8 * (r % 2));  // keys of this piece below kv_end
-      const uint32_t k0 = (0 < nv ? 0xFFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t k1 = (2 < nv ? 0xFFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t k2 = (4 < nv ? 0xFFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t k3 = (6 < nv ? 0xFFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u);
-      v.x &= k0;
-      v.y &= k1;
-      v.z &= k2;
-      v.w &= k3;
-    }
-    *reinterpret_cast<uint4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = v;
+    *reinterpret_cast<uint4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = st.v[u];
   }
 }
 
@@ -142,41 +161,42 @@ __device__ __forceinline__ int key_off(int kt, int r, int h) {
   return 32 * kt + 16 * (r >> 3) + 8 * h + 4 * ((r >> 2) & 1) + (r & 3);
 }
 
-template <int D, bool MASK>
-__device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 (&qop)[D / 16],
-                                              f32x16 (&o)[D / 32], float& m_used, float& l_part,
-                                              int lim, int c0, float sl2, int i32, int h) {
+template <int D>
+__device__ __forceinline__ void keep_compute_branch() {
+#if PMATTN_PF_KEEP
+  keep_branch();
+#endif
+}
+
+// One 32-key score tile: S^T = K.Q^T, mask, online softmax with lazy
+// rescale, then O^T += V^T.P^T.
+template <int D>
+__device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const bf16x8 (&qop)[D / 16],
+                                             f32x16 (&o)[D / 32], float& m_used, float& l_part,
+                                             bool mask, int lim, float sl2, int i32, int h) {
   constexpr int KSTEPS = D / 16, DT = D / 32;
   const uint16_t* kl = lds;
   const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
-  // S^T for two 32-key tiles; A-operand row i32 holds key kappa(i32): slot bits 2,3 swapped
+  // A-operand row i32 holds key kappa(i32): slot bits 2 and 3 swapped
   const int kap = (i32 & ~12) | ((i32 & 4) << 1) | ((i32 & 8) >> 1);
-  f32x16 s[2];
+  f32x16 s = {};
+  const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    f32x16 acc = {};
-    const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(kr + 8 * st), qop[st], acc, 0, 0, 0);
-    s[kt] = acc;
-  }
-  if (MASK) {
+  for (int st = 0; st < KSTEPS; ++st)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(kr + 8 * st), qop[st], s, 0, 0, 0);
+  if (mask) {
+    keep_compute_branch<D>();
     // visible iff key < lim (lim = min(pos + 1, kv_end) - c0 for this lane's row)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = key_off(kt, r, h) < lim ? s[kt][r] : kNegInf;
+    for (int r = 0; r < 16; ++r) s[r] = key_off(kt, r, h) < lim ? s[r] : kNegInf;
   }
-  float mx = s[0][0];
+  float mx = s[0];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // lazy rescale: move the reference max only when it grows by > 2^8 somewhere
   const bool grow = mx != kNegInf && (m_used == kNegInf || (mx - m_used) * sl2 > kRescaleLog2);
   if (__any(grow)) {
+    keep_compute_branch<D>();
     const float m_new = fmaxf(m_used, mx);
     const float alpha = m_used == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2);
     l_part *= alpha;
@@ -185,10 +205,76 @@ __device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 
     m_used = m_new;
   }
   const float ms = m_used == kNegInf ? 0.f : m_used * sl2;
-  bf16x8 pb[2][2];
+  f32x8 p0, p1;
   float ps = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int e = 0; e < 8; ++e) {
+    p0[e] = __builtin_amdgcn_exp2f(s[e] * sl2 - ms);
+    p1[e] = __builtin_amdgcn_exp2f(s[8 + e] * sl2 - ms);
+    ps += p0[e] + p1[e];
+  }
+  l_part += ps;
+  const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
+  const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const uint16_t* vr = vl + (32 * t + i32) * Cfg<D>::VROW + 32 * kt + 8 * h;
+    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr), pb0, o[t], 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr + 16), pb1, o[t], 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 (&qop)[D / 16],
+                                              f32x16 (&o)[D / 32], float& m_used, float& l_part,
+                                              bool mask, int lim, float sl2, int i32, int h) {
+#if PMATTN_PF_TILE_OUTER
+#pragma unroll
+  for (int kt = 0; kt < Cfg<D>::NTILE; ++kt)
+    compute_tile<D>(lds, kt, qop, o, m_used, l_part, mask, lim, sl2, i32, h);
+#else
+  constexpr int KSTEPS = D / 16, DT = D / 32, NT = Cfg<D>::NTILE;
+  const uint16_t* kl = lds;
+  const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
+  const int kap = (i32 & ~12) | ((i32 & 4) << 1) | ((i32 & 8) >> 1);
+  f32x16 s[NT];
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    f32x16 acc = {};
+    const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(kr + 8 * st), qop[st], acc, 0, 0, 0);
+    s[kt] = acc;
+  }
+  if (mask) {
+    keep_compute_branch<D>();
+#pragma unroll
+    for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = key_off(kt, r, h) < lim ? s[kt][r] : kNegInf;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool grow = mx != kNegInf && (m_used == kNegInf || (mx - m_used) * sl2 > kRescaleLog2);
+  if (__any(grow)) {
+    keep_compute_branch<D>();
+    const float m_new = fmaxf(m_used, mx);
+    const float alpha = m_used == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2);
+    l_part *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+    m_used = m_new;
+  }
+  const float ms = m_used == kNegInf ? 0.f : m_used * sl2;
+  bf16x8 pb[NT][2];
+  float ps = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
     f32x8 p0, p1;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -200,20 +286,20 @@ __device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 
     pb[kt][1] = __builtin_convertvector(p1, bf16x8);
   }
   l_part += ps;
-  // O^T += V^T . P^T: A = V^T (channel 32t + i32, keys 32kt + 16kk + 8h .. +8)
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
     const uint16_t* vr = vl + (32 * t + i32) * Cfg<D>::VROW + 8 * h;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr + 32 * kt + 16 * kk), pb[kt][kk], o[t], 0, 0, 0);
   }
+#endif
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PMATTN_PF_WAVES, PMATTN_PF_WAVES)))
 void attn_prefill_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 16, DT = D / 32, CHUNK = Cfg<D>::CHUNK;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
@@ -255,33 +341,32 @@ void attn_prefill_kernel(AttnArgs a) {
   const int row_lim = min(pos + 1, kv_end);
   const float sl2 = a.scale_log2;
 
-  auto chunk_blocks = [&](int c0, int (&blk)[4]) -> int {
+  // physical ids of the chunk's blocks; blocks past the last one repeat it
+  constexpr int NBLK = Cfg<D>::NBLK;
+  auto chunk_blocks = [&](int c0, int (&blk)[NBLK]) {
     const int bi = c0 >> 4;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) blk[b] = bt_row[min(bi + b, last_blk)];
-    return min(4, last_blk - bi + 1);
+    for (int b = 0; b < NBLK; ++b) blk[b] = bt_row[min(bi + b, last_blk)];
   };
 
   Stage<D> stg;
-  int blk[4];
+  int blk[NBLK];
   int c0 = it.kv_begin;
-  int nvb = chunk_blocks(c0, blk);
-  stage_load<D>(stg, kpool, vpool, blk, nvb, kvh, hkv, tid);
+  chunk_blocks(c0, blk);
+  stage_load<D>(stg, kpool, vpool, blk, kvh, hkv, tid);
   stage_store<D>(lds, stg, c0, kv_end, tid);
   __syncthreads();
   for (int c = 0; c < nch; ++c, c0 += CHUNK) {
     const bool more = c + 1 < nch;
     if (more) {
-      nvb = chunk_blocks(c0 + CHUNK, blk);
-      stage_load<D>(stg, kpool, vpool, blk, nvb, kvh, hkv, tid);
+      chunk_blocks(c0 + CHUNK, blk);
+      stage_load<D>(stg, kpool, vpool, blk, kvh, hkv, tid);
     }
     issue_barrier();
     const uint16_t* cur = lds + (c & 1) * Cfg<D>::STAGE;
-    // every row of the task sees every key of the chunk: no mask needed
-    if (c0 + CHUNK - 1 <= min_pos && c0 + CHUNK <= kv_end)
-      compute_chunk<D, false>(cur, qop, o, m_used, l_part, 0, c0, sl2, i32, h);
-    else
-      compute_chunk<D, true>(cur, qop, o, m_used, l_part, row_lim - c0, c0, sl2, i32, h);
+    // a chunk every row of the task sees whole needs no mask
+    const bool mask = c0 + CHUNK - 1 > min_pos || c0 + CHUNK > kv_end;
+    compute_chunk<D>(cur, qop, o, m_used, l_part, mask, row_lim - c0, sl2, i32, h);
     if (more) stage_store<D>(lds + ((c + 1) & 1) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
     __syncthreads();
   }
