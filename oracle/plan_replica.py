@@ -26,6 +26,7 @@ MAX_WAVE_ROWS = 64
 MAX_TASK_ROWS = 128
 CLASS_ROWS = (16, 32, 64, 128)
 TASKS_PER_CU = 32
+WG_TASKS_PER_CU = 4
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
 
@@ -63,34 +64,34 @@ def token_tiles(q_len, q_start, group):
 def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
     """KV partitions per sequence. Explicit: the requested count for every
     sequence with rows. Automatic: a task over n blocks costs n * (2 + rows/16)
-    block units; the quantum is the total cost over (CUs x 32) tasks (at
-    least 48 units); a sequence gets ceil(cost of its largest tile /
-    (quantum x rows/16 of that tile)) partitions, at most 64 and at most its
-    number of blocks."""
+    block units. Wave tasks (<= 64 rows) and workgroup tasks (128 rows) are
+    balanced separately: each kind's quantum is its total cost over
+    (CUs x 32) wave tasks or (CUs x 4) workgroup tasks, at least 48 units; a
+    sequence gets ceil(cost of its largest tile / its kind's quantum)
+    partitions, at most 64 and at most its number of blocks."""
     q_len = np.asarray(q_len, np.int64)
     q_start = np.asarray(q_start, np.int64)
     out = np.zeros(q_len.shape[0], np.int32)
     if num_kv_splits > 0:
         out[q_len > 0] = num_kv_splits
         return out
-    tiles = token_tiles(q_len, q_start, group)
-    total = 0
+    total = [0, 0]
     last = np.zeros(q_len.shape[0], np.int64)
-    last_rows16 = np.ones(q_len.shape[0], np.int64)
-    for s, _, _, cls, kv_end in tiles:
+    kind = np.zeros(q_len.shape[0], np.int64)
+    for s, _, _, cls, kv_end in token_tiles(q_len, q_start, group):
+        k = 1 if cls > MAX_WAVE_ROWS else 0
         c = -(-kv_end // BLOCK) * (2 + cls // 16)
-        total += c * num_kv_heads
-        if c > last[s]:
-            last[s] = c
-            last_rows16[s] = cls // 16
-    target = (num_cus if num_cus > 0 else 256) * TASKS_PER_CU
-    quantum = max(MIN_QUANTUM, -(-total // target))
+        total[k] += c * num_kv_heads
+        last[s] = max(last[s], c)
+        kind[s] = k
+    cus = num_cus if num_cus > 0 else 256
+    quantum = [max(MIN_QUANTUM, -(-total[k] // t)) for k, t in ((0, cus * TASKS_PER_CU),
+                                                                (1, cus * WG_TASKS_PER_CU))]
     for s in range(q_len.shape[0]):
         if q_len[s] == 0:
             continue
         nblk = -(-int(q_start[s] + q_len[s]) // BLOCK)
-        q = quantum * int(last_rows16[s])
-        out[s] = max(1, min(-(-int(last[s]) // q), MAX_AUTO_SPLITS, nblk))
+        out[s] = max(1, min(-(-int(last[s]) // quantum[kind[s]]), MAX_AUTO_SPLITS, nblk))
     return out
 
 

@@ -165,29 +165,40 @@ __device__ __forceinline__ pmattn_work_item load_item(const pmattn_work_item* it
   return it;
 }
 
-// Decode-shaped tasks (one 16-row tile) keep two waves per SIMD so
-// that eight waves per CU keep KV loads in flight; the 64-row variant needs
-// the whole register file.
+// Decode-shaped tasks keep two waves per SIMD so that eight waves per CU keep
+// KV loads in flight; the 64-row variant needs the whole register file.
 #ifndef PMATTN_DECODE_DEPTH
 #define PMATTN_DECODE_DEPTH 2
 #endif
 #ifndef PMATTN_DECODE_WAVES
 #define PMATTN_DECODE_WAVES 2
 #endif
+#ifndef PMATTN_VERIFY_DEPTH
+#define PMATTN_VERIFY_DEPTH 1
+#endif
 template <int NT>
-struct WavesPerEu { static constexpr int value = NT == 1 ? PMATTN_DECODE_WAVES : 1; };
+struct WavesPerEu {
+  static constexpr int value = NT == 1 ? PMATTN_DECODE_WAVES : (NT == 2 && PMATTN_VERIFY_DEPTH == 1 ? 2 : 1);
+};
 // Chunks in flight per wave: 1 (occupancy hides latency) or 2 (explicit
-// double buffering).
+// double buffering). 16-row tasks double-buffer at 2 waves/SIMD; 32-row tasks
+// (speculative verify) keep one buffer so that they too fit 2 waves/SIMD.
 template <int NT>
-struct Depth { static constexpr int value = NT == 1 ? PMATTN_DECODE_DEPTH : 2; };
+struct Depth {
+  static constexpr int value = NT == 1 ? PMATTN_DECODE_DEPTH : (NT == 2 ? PMATTN_VERIFY_DEPTH : 2);
+};
+
+// Tasks are independent; a workgroup holds four of them, one per wave (1- and
+// 2-wave workgroups measured the same or slower on the decode workloads).
+constexpr int kWavesPerWg = 4;
 
 template <int D, int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))
+__global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * 4 + wave;
+  const int idx = blockIdx.x * kWavesPerWg + wave;
   if (idx >= a.item_count) return;
   const pmattn_work_item it = load_item(a.items, idx);
   const int i = lane & 15, g = lane >> 4;
@@ -329,7 +340,7 @@ void attn_bf16_kernel(AttnArgs a) {
 
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
-  const dim3 grid((a.item_count + 3) / 4), block(256);
+  const dim3 grid((a.item_count + kWavesPerWg - 1) / kWavesPerWg), block(64 * kWavesPerWg);
 #define PMATTN_LAUNCH(D, NT) hipLaunchKernelGGL((attn_bf16_kernel<D, NT>), grid, block, 0, st, a)
   if (head_dim == 128) {
     if (class_rows <= 16) PMATTN_LAUNCH(128, 1);

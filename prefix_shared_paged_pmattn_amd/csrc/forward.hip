@@ -18,6 +18,20 @@ constexpr float kLog2e = 1.44269504088896340736f;
 std::mutex g_ws_mu;
 std::unordered_map<const void*, uint64_t> g_ws_owner;
 
+// Per-device auxiliary stream (default priority) and fork/join events: a plan
+// that mixes wave tasks (decode/verify, KV-stream bound) and workgroup tasks
+// (prefill, MFMA bound) runs the two kinds concurrently, the wave tasks on the
+// auxiliary stream, joined back into the caller's stream before the merge.
+// The record/wait sequence is enqueued under a mutex, so concurrent callers
+// never interleave the shared events (a wait binds to the latest record at
+// enqueue time).
+struct DeviceAux {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_aux_mu;
+std::unordered_map<int, DeviceAux> g_aux;
+
 pmattn_status hip_fail(hipError_t e, const char* what) {
   return fail(PMATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -94,18 +108,48 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.scale = P.scale;
   a.scale_log2 = P.scale * kLog2e;
   const pmattn_work_item* items = reinterpret_cast<const pmattn_work_item*>(ws + P.off_items);
-  for (size_t c = 0; c < P.class_rows.size(); ++c) {
-    a.items = items + P.class_begin[c];
-    a.item_count = P.class_begin[c + 1] - P.class_begin[c];
-    hipError_t e;
-    if (P.dtype != PMATTN_BF16)
-      e = launch_attn_f32(P.head_dim, a, st);
-    else if (P.class_rows[c] > kMaxWaveRows)
-      e = launch_attn_prefill(P.head_dim, a, st);
-    else
-      e = launch_attn_bf16(P.head_dim, P.class_rows[c], a, st);
-    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  auto launch_class = [&](size_t c, hipStream_t s) -> hipError_t {
+    AttnArgs ac = a;
+    ac.items = items + P.class_begin[c];
+    ac.item_count = P.class_begin[c + 1] - P.class_begin[c];
+    if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);
+    if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
+    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, s);
+  };
+  bool has_wg = false, has_wave = false;
+  for (int32_t rows : P.class_rows) (rows > kMaxWaveRows ? has_wg : has_wave) = true;
+  if (!(P.dtype == PMATTN_BF16 && has_wg && has_wave)) {
+    for (size_t c = 0; c < P.class_rows.size(); ++c) {
+      hipError_t e = launch_class(c, st);
+      if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    }
+    return PMATTN_OK;
   }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_aux_mu);
+  DeviceAux& aux = g_aux[dev];
+  if (!aux.stream) {
+    if ((e = hipStreamCreateWithFlags(&aux.stream, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&aux.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&aux.join, hipEventDisableTiming)) != hipSuccess) {
+      g_aux.erase(dev);
+      return hip_fail(e, "auxiliary stream setup");
+    }
+  }
+  if ((e = hipEventRecord(aux.fork, st)) != hipSuccess ||
+      (e = hipStreamWaitEvent(aux.stream, aux.fork, 0)) != hipSuccess)
+    return hip_fail(e, "stream fork");
+  for (size_t c = 0; c < P.class_rows.size(); ++c)
+    if (P.class_rows[c] <= kMaxWaveRows && (e = launch_class(c, aux.stream)) != hipSuccess)
+      return hip_fail(e, "attention kernel launch (wave tasks)");
+  for (size_t c = 0; c < P.class_rows.size(); ++c)
+    if (P.class_rows[c] > kMaxWaveRows && (e = launch_class(c, st)) != hipSuccess)
+      return hip_fail(e, "attention kernel launch (workgroup tasks)");
+  if ((e = hipEventRecord(aux.join, aux.stream)) != hipSuccess ||
+      (e = hipStreamWaitEvent(st, aux.join, 0)) != hipSuccess)
+    return hip_fail(e, "stream join");
   return PMATTN_OK;
 }
 

@@ -30,8 +30,10 @@ std::atomic<uint64_t> g_next_plan_id{1};
 // over n KV blocks costs n * (2 + rows/16). The constant 2 stands for the
 // K/V stream of each block, the rows/16 term for its MFMA column tiles.
 int64_t unit_cost(int cls) { return 2 + kClassRows[cls] / 16; }
-// Automatic splitting aims at this many tasks per compute unit ...
+// Automatic splitting aims at this many wave tasks (and workgroup tasks) per
+// compute unit ...
 constexpr int64_t kTasksPerCu = 32;
+constexpr int64_t kWgTasksPerCu = 4;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;
 constexpr int kMaxAutoSplits = 64;
@@ -155,25 +157,29 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (d->num_kv_splits > 0) {
     for (int s = 0; s < B; ++s) P.num_splits[s] = d->q_len[s] > 0 ? d->num_kv_splits : 0;
   } else {
-    int64_t total = 0;
-    std::vector<int64_t> last_cost(B, 0), last_tiles16(B, 1);
+    // Two resource classes are balanced separately: wave tasks (<= 64 rows,
+    // KV-stream bound) and workgroup tasks (128 rows, MFMA bound). A
+    // sequence's partition count is ceil(cost of its largest tile / quantum
+    // of its class).
+    int64_t total[2] = {0, 0};
+    std::vector<int64_t> last_cost(B, 0);
+    std::vector<int> seq_kind(B, 0);
     for (const Tile& t : tiles) {
+      const int kind = kClassRows[t.cls] > kMaxWaveRows ? 1 : 0;
       const int64_t c = (int64_t)((t.kv_end + kBlock - 1) / kBlock) * unit_cost(t.cls);
-      total += c * d->num_kv_heads;
-      if (c > last_cost[t.seq]) {
-        last_cost[t.seq] = c;
-        last_tiles16[t.seq] = kClassRows[t.cls] / 16;
-      }
+      total[kind] += c * d->num_kv_heads;
+      last_cost[t.seq] = std::max(last_cost[t.seq], c);
+      seq_kind[t.seq] = kind;
     }
     const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
-    const int64_t target = cus * kTasksPerCu;
-    const int64_t quantum = std::max(kMinQuantum, (total + target - 1) / target);
+    const int64_t target[2] = {cus * kTasksPerCu, cus * kWgTasksPerCu};
+    int64_t quantum[2];
+    for (int k = 0; k < 2; ++k)
+      quantum[k] = std::max(kMinQuantum, (total[k] + target[k] - 1) / target[k]);
     for (int s = 0; s < B; ++s) {
       if (d->q_len[s] == 0) continue;
       const int64_t nblk = (d->q_start[s] + d->q_len[s] + kBlock - 1) / kBlock;
-      // Multi-row tiles are split less eagerly (quantum x rows/16): each split
-      // row costs a partial record and a merge, and such tiles are numerous.
-      const int64_t q = quantum * last_tiles16[s];
+      const int64_t q = quantum[seq_kind[s]];
       int64_t p = (last_cost[s] + q - 1) / q;
       p = std::min<int64_t>(std::min<int64_t>(p, kMaxAutoSplits), nblk);
       P.num_splits[s] = (int32_t)std::max<int64_t>(1, p);

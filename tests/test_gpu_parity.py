@@ -45,6 +45,10 @@ def _batch_cases():
         "prefill-mha-long": (dict(hq=2, hkv=2, d=128), [S(q_len=200, seq_len=260, q_start=60)], 0),
         "prefill-d64-g8": (dict(hq=16, hkv=2, d=64), [S(q_len=33, seq_len=50, q_start=17), S(q_len=9, seq_len=9)], 0),
         "prefill-wg-tail-in-first-chunk": (dict(hq=8, hkv=2, d=128), [S(q_len=20, seq_len=23, q_start=3)], 0),
+        # wave and workgroup tasks in one plan (run concurrently on two streams)
+        "mixed-classes": (dict(hq=8, hkv=2, d=128), [S(q_len=50, seq_len=300, q_start=250), S(q_len=1, seq_len=700),
+                                                     S(q_len=5, seq_len=405), S(q_len=1, seq_len=33),
+                                                     S(q_len=130, seq_len=130)], 0),
     }
 
 
