@@ -35,7 +35,14 @@
  * Memory layouts (all row-major, no padding between elements):
  *  - q, out     [R][Hq][d]         R = sum of q_len; rows of sequence s are
  *                                  contiguous, sequences in descriptor order.
- *  - k_pool     [num_blocks][Hkv][16][d]   token-major inside a block.
+ *  - k_pool     [num_blocks][Hkv][d/x][16][x]   grouped inside a block,
+ *                                  x = 16 bytes / element size (8 for bf16, 4
+ *                                  for float32): channel c of slot o sits at
+ *                                  [c/x][o][c%x], so each 16-byte group holds
+ *                                  x channels of one token and the 16 tokens
+ *                                  of a group are 256 contiguous bytes (the
+ *                                  grouped K cache of the PagedAttention
+ *                                  kernel the pages build on).
  *  - v_pool     [num_blocks][Hkv][d][16]   channel-major inside a block, so
  *                                  that 16 consecutive tokens of one channel
  *                                  are one contiguous 32-byte (bf16) run.

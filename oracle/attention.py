@@ -35,8 +35,10 @@ What is computed, and where the pages fix it
   states each partition's (output, lse) and the merge formula directly.
 
 Layouts (shared with the library ABI): q ``[R][Hq][d]``; k_pool
-``[blocks][Hkv][16][d]``; v_pool ``[blocks][Hkv][d][16]``; block_table int32
-``[B][stride]``. Query head ``h`` reads kv head ``h // (Hq // Hkv)``
+``[blocks][Hkv][d/x][16][x]`` with x = gcd(d, 16 bytes / element size), i.e.
+channel ``c`` of slot ``o`` sits at ``[.., c // x, o, c % x]`` (the grouped K
+layout of the PagedAttention paper's kernel, which the pages build on);
+v_pool ``[blocks][Hkv][d][16]``; block_table int32 ``[B][stride]``. Query head ``h`` reads kv head ``h // (Hq // Hkv)``
 (contiguous GQA groups). ``lse`` is the natural-log log-sum-exp of the scaled
 scores; an empty key set gives ``lse = -inf`` and output 0.
 """
@@ -64,11 +66,13 @@ def gather_kv(k_pool: np.ndarray, v_pool: np.ndarray, bt_row: np.ndarray, kv_hea
     """Logical keys 0..n_keys-1 of one sequence for one kv head, as float64 [n][d].
 
     Logical key j lives in physical block ``bt_row[j // 16]`` at slot ``j % 16``.
+    K slots are stored as channel groups (``[blocks][Hkv][d/x][16][x]``).
     """
     j = np.arange(n_keys)
     blk = np.asarray(bt_row)[j // BLOCK]
     off = j % BLOCK
-    k = k_pool[blk, kv_head, off, :]          # [n][d]
+    k = k_pool[blk, kv_head, :, off, :]       # [n][d/x][x] (fancy indices lead)
+    k = k.reshape(n_keys, -1)                 # [n][d]
     v = v_pool[blk, kv_head, :, off]          # [n][d] (fancy indices lead)
     return decode_values(k, dtype), decode_values(v, dtype)
 
@@ -156,7 +160,9 @@ def merge_partitions(parts_o: np.ndarray, parts_lse: np.ndarray) -> Tuple[np.nda
     has = tot > 0
     lse = np.where(has, top_safe + np.log(np.where(has, tot, 1.0)), -np.inf)
     coef = np.where(has[None], w / np.where(has, tot, 1.0)[None], 0.0)
-    out = (coef[..., None] * po).sum(axis=0)
+    # an empty partition covers no key, so its output slot is left out of the
+    # sum rather than multiplied by 0 (it may hold anything, NaN included)
+    out = np.where(np.isfinite(pl)[..., None], coef[..., None] * po, 0.0).sum(axis=0)
     return out, lse
 
 

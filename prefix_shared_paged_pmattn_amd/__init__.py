@@ -201,7 +201,7 @@ def _vp(t):
 
 def forward(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=None, stream=None):
     """``pmattn_forward``. Tensors: q/out ``[R][Hq][d]``; k_pool
-    ``[blocks][Hkv][16][d]``; v_pool ``[blocks][Hkv][d][16]`` (element type of
+    ``[blocks][Hkv][d/x][16][x]`` (x = 16 bytes / element size); v_pool ``[blocks][Hkv][d][16]`` (element type of
     the plan); block_table int32 ``[B][stride]``; lse float32 ``[R][Hq]`` or
     None; workspace: a uint8 tensor of at least ``p.workspace_bytes``."""
     workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace)

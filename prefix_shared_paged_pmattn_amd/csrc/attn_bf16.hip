@@ -17,22 +17,24 @@
 // Keys are consumed 32 at a time (two 16-token blocks). The channel order
 // inside the QK contraction and the key order inside the PV contraction are
 // permuted (identically on both operands, so the sums are unchanged) so that
-// every operand a lane needs is one contiguous 16-byte run in memory:
-//   K operand, lane (i, g): key 8*(i/4) + 4c + i%4 of the chunk, channels
-//     [g*d/4, (g+1)*d/4)  -> d/32 consecutive 16-byte loads;
-//   V operand, lane (i, g): channel 16t + i, keys 8g..8g+7 of the chunk,
-//     which the channel-major V block stores contiguously -> one 16-byte load.
+// every operand a lane needs is a contiguous run in memory and every load
+// instruction covers whole cache lines:
+//   K operand, tile c = block c, lane (i, g): slot i, channel group 4s + g
+//     of the grouped K block [d/8][16][8] -> d/32 16-byte loads per tile;
+//   V operand, lane (i, g): channel 16t + i, slots 4g..4g+3 of each block,
+//     which the channel-major V block stores contiguously -> two 8-byte loads.
 // K and V tiles are gathered through the block table (physical ids fetched
-// with scalar loads a chunk ahead); no contiguous copy of the KV is ever formed (the K/V concatenation the XY-Serve referee report
-// blames for the baseline's losses).
+// with scalar loads a chunk ahead); no contiguous copy of the KV is ever
+// formed (the K/V concatenation the XY-Serve referee report blames for the
+// baseline's losses).
 //
 // Masks are row-wise (XY-Serve review, "Editorial extensions": one kernel for
 // prefill, decode and verify rows): key j is visible to a row at position pos
-// iff j <= pos; chunks that lie wholly below the task's first position skip
-// the mask (Figure 11, mask-aware computation). Keys at or past the task's end
-// are never used: their scores become -inf and their V lanes are zeroed before
-// the PV product, so pool slots no row can see may hold NaN (virtual padding,
-// "Assumptions & free parameters").
+// iff j <= pos. The mask costs a few selects per 32 keys and is applied to
+// every chunk, so the streaming loop has no data-dependent branch. Keys at or
+// past the task's end are never used: their scores become -inf and their V
+// lanes are zeroed before the PV product, so pool slots no row can see may
+// hold NaN (virtual padding, "Assumptions & free parameters").
 #include "attn_kernels.h"
 
 namespace pmattn {
@@ -59,34 +61,52 @@ struct Chunk {
 };
 
 // Issue the loads of the 32-key chunk made of physical blocks blk0, blk1.
+// Key tile c of the QK product is block c: lane (i, g) holds slot i, and for
+// k-step s the 8 channels of group 4s + g, i.e. one 16-byte piece of the
+// grouped K block [D/8][16][8]; a load instruction covers 1 KiB of one block.
+// Contraction position 8g + 4c + r of the PV product is slot 4g + r of block
+// c, so lane (channel, g) of V^T takes 4 slots of each block: two 8-byte
+// pieces of the channel-major V blocks (512 contiguous bytes per instruction
+// and block).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 __device__ __forceinline__ void load_chunk(Chunk<D>& ch, const uint16_t* __restrict__ kpool,
                                            const uint16_t* __restrict__ vpool, int blk0, int blk1,
                                            int kvh, int hkv, int i, int g) {
   constexpr int KS = Chunk<D>::KS, DT = Chunk<D>::DT;
-  const int64_t blk_k = (i >> 3) ? blk1 : blk0;
-  const uint16_t* kp = kpool + ((blk_k * hkv + kvh) * 16 + 8 * ((i >> 2) & 1) + (i & 3)) * D + g * 8 * KS;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < 2; ++c) {
+    const int64_t bk = c ? blk1 : blk0;
+    const uint16_t* kp = kpool + ((bk * hkv + kvh) * (D / 8) + g) * 128 + 8 * i;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) ch.k[c][s] = ld16(kp + 4 * c * D + 8 * s);
-  const int64_t blk_v = (g >> 1) ? blk1 : blk0;
-  const uint16_t* vp = vpool + ((blk_v * hkv + kvh) * D + i) * 16 + 8 * (g & 1);
+    for (int s = 0; s < KS; ++s) ch.k[c][s] = ld16(kp + 512 * s);
+  }
+  const uint16_t* vp0 = vpool + (((int64_t)blk0 * hkv + kvh) * D + i) * 16 + 4 * g;
+  const uint16_t* vp1 = vpool + (((int64_t)blk1 * hkv + kvh) * D + i) * 16 + 4 * g;
 #pragma unroll
-  for (int t = 0; t < DT; ++t) ch.v[t] = ld16(vp + 16 * 16 * t);
+  for (int t = 0; t < DT; ++t) {
+    const u32x2 x0 = *reinterpret_cast<const u32x2*>(vp0 + 256 * t);
+    const u32x2 x1 = *reinterpret_cast<const u32x2*>(vp1 + 256 * t);
+    ch.v[t] = __builtin_bit_cast(bf16x8, (u32x4){x0.x, x0.y, x1.x, x1.y});
+  }
 }
 
 // Zero the V lanes of keys at or past the task's end (only the last, partial
 // chunk has any; the masks are all-ones elsewhere): a masked key has weight
 // exactly 0, but 0 * NaN would still poison the PV product if the slot holds
 // garbage.
+// Element e of a lane's V operand is key c0 + 4g + slot_off(e).
+__device__ __forceinline__ constexpr int slot_off(int e) { return 16 * (e >> 2) + (e & 3); }
+
 template <int D>
 __device__ __forceinline__ void zero_tail_v(Chunk<D>& ch, int c0, int kv_end, int g) {
-  const int nv = kv_end - (c0 + 8 * g);
+  const int nv = kv_end - (c0 + 4 * g);
   uint32_t keep[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w)
-    keep[w] = (2 * w + 1 < nv ? 0xFFFF0000u : 0u) | (2 * w < nv ? 0x0000FFFFu : 0u);
+    keep[w] = (slot_off(2 * w + 1) < nv ? 0xFFFF0000u : 0u) | (slot_off(2 * w) < nv ? 0x0000FFFFu : 0u);
 #pragma unroll
   for (int t = 0; t < Chunk<D>::DT; ++t) {
     uint4 u = __builtin_bit_cast(uint4, ch.v[t]);
@@ -116,10 +136,11 @@ __device__ __forceinline__ void compute_chunk(const Chunk<D>& ch, const bf16x8 (
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[1][s], qop[n][s], s1, 0, 0, 0);
     }
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-    // slot j holds key c0 + 8g + j; visible iff key < min(pos + 1, kv_end)
+    // score j holds key c0 + 4g + slot_off(j) (tile j/4, accumulator row
+    // 4g + j%4); visible iff key < min(pos + 1, kv_end)
     const int lim = lim_base[n] - c0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = (j < lim) ? sv[j] : kNegInf;
+    for (int j = 0; j < 8; ++j) sv[j] = (slot_off(j) < lim) ? sv[j] : kNegInf;
     float mx = sv[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
@@ -208,8 +229,9 @@ void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* __restrict__ kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* __restrict__ vpool = static_cast<const uint16_t*>(a.v_pool);
 
-  // Q operand (B of the QK product): lane (i, g) holds query row 16n+i,
-  // channels [g*D/4, (g+1)*D/4), in k-step slices of 8.
+  // Q operand (B of the QK product): lane (i, g) holds query row 16n+i; k-step
+  // s takes channels [32s + 8g, 32s + 8g + 8), the channel group K's lanes
+  // hold for the same step.
   bf16x8 qop[NT][KS];
   int pos[NT];
 #pragma unroll
@@ -219,9 +241,9 @@ void attn_bf16_kernel(AttnArgs a) {
     if (m < M) {
       const int t = m / G;
       pos[n] = it.pos_begin + t;
-      const uint16_t* src = qp + ((int64_t)(it.row_begin + t) * hq + kvh * G + (m - t * G)) * D + g * 8 * KS;
+      const uint16_t* src = qp + ((int64_t)(it.row_begin + t) * hq + kvh * G + (m - t * G)) * D + 8 * g;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qop[n][s] = ld16(src + 8 * s);
+      for (int s = 0; s < KS; ++s) qop[n][s] = ld16(src + 32 * s);
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s) qop[n][s] = (bf16x8)(__bf16)0.0f;
@@ -250,10 +272,10 @@ void attn_bf16_kernel(AttnArgs a) {
   const float sl2 = a.scale_log2;
   const int kv_end = it.kv_end;
   // per row: keys below min(pos + 1, kv_end) are visible; lanes of group g see
-  // keys c0 + 8g + j, so fold 8g in once
+  // keys c0 + 4g + slot_off(j), so fold 4g in once
   int lim_base[NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) lim_base[n] = min(pos[n] + 1, kv_end) - 8 * g;
+  for (int n = 0; n < NT; ++n) lim_base[n] = min(pos[n] + 1, kv_end) - 4 * g;
   if constexpr (Depth<NT>::value == 1) {
     // One buffer per wave; latency is hidden by the other waves on the SIMD.
     const int nch = (kv_end - it.kv_begin + 31) >> 5;

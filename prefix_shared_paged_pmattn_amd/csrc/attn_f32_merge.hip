@@ -49,9 +49,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       const int blk = valid ? bt_row[j >> 4] : 0;
       float s = kNegInf;
       if (valid) {
-        const float* kr = kpool + (((int64_t)blk * hkv + kvh) * 16 + (j & 15)) * D;
+        // grouped K block [D/4][16][4]: channel c of slot o at (c/4)*64 + 4o + c%4
+        const float* kr = kpool + ((int64_t)blk * hkv + kvh) * 16 * D + 4 * (j & 15);
         float dot = 0.f;
-        for (int c = 0; c < D; ++c) dot = fmaf(qrow[c], kr[c], dot);
+        for (int c = 0; c < D; ++c) dot = fmaf(qrow[c], kr[(c >> 2) * 64 + (c & 3)], dot);
         s = dot * a.scale;
       }
       const float m_new = fmaxf(m_run, wave_max(s));  // finite: key kb is visible
@@ -89,14 +90,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 // Log-sum-exp merge of partial results (Flash-Decoding, reference list of the
 // XY-Serve pith review): one wave per output (row, head); lane owns D/64
 // consecutive channels. out = sum_p w_p O_p / sum_p w_p with
-// w_p = exp(lse_p - max lse); lse = max + ln sum w_p. Empty partials (-inf)
-// weigh 0; if all are empty the output is 0 and lse is -inf.
-// Latency-lean: lane p loads lse_p (64 partials per round), the max and the
-// weight sum are wave reductions, and the partial-output loads are unrolled
-// so that a merge costs about two memory round trips, not one per partial.
+// w_p = exp(lse_p - max lse); lse = max + ln sum w_p. Partials of weight 0
+// (empty, lse -inf) are left out of the sum, so their output slots may hold
+// anything; if all are empty the output is 0 and lse is -inf.
+// Latency-lean: lane p loads lse_p (64 partials per round) and the max and the
+// weight sum are wave reductions. The partial outputs of the first kPre
+// partials do not depend on the weights, so their loads are issued together
+// with the lse loads; a merge of up to kPre partials costs one memory round
+// trip after its row record. Further partials are loaded in unrolled groups.
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int V = D / 64;
+  constexpr int kPre = 16;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + wave;
@@ -118,8 +123,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     row = w / a.hq;
     qh = w - (int)row * a.hq;
   }
-  float mx = kNegInf;
-  for (int p0 = 0; p0 < np; p0 += 64)
+  const float* po = a.part_o + rec0 * D + lane * V;
+  float pre[kPre][V];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+#pragma unroll
+    for (int v = 0; v < V; ++v) pre[u][v] = u < np ? po[(int64_t)u * stride * D + v] : 0.f;
+  const float l0 = lane < np ? a.part_lse[rec0 + lane * stride] : kNegInf;
+  float mx = l0;
+  for (int p0 = 64; p0 < np; p0 += 64)
     if (p0 + lane < np) mx = fmaxf(mx, a.part_lse[rec0 + (p0 + lane) * stride]);
   mx = wave_max(mx);
   float acc[V], tot = 0.f;
@@ -128,32 +140,40 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (mx != kNegInf) {
     for (int p0 = 0; p0 < np; p0 += 64) {
       const int pn = min(64, np - p0);
-      float wt = 0.f;
-      if (lane < pn) {
-        const float l = a.part_lse[rec0 + (p0 + lane) * stride];
-        wt = (l == kNegInf) ? 0.f : expf(l - mx);
-      }
+      float l = l0;
+      if (p0 > 0) l = lane < pn ? a.part_lse[rec0 + (p0 + lane) * stride] : kNegInf;
+      const float wt = (l == kNegInf) ? 0.f : expf(l - mx);
       tot += wave_sum(wt);
       int q = 0;
+      if (p0 == 0) {
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+          const float wu = __shfl(wt, u);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[v] = fmaf(wu, wu != 0.f ? pre[u][v] : 0.f, acc[v]);
+        }
+        q = min(kPre, pn);
+      }
       for (; q + 8 <= pn; q += 8) {
         float src[8][V];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-          for (int v = 0; v < V; ++v)
-            src[u][v] = a.part_o[(rec0 + (int64_t)(p0 + q + u) * stride) * D + lane * V + v];
+          for (int v = 0; v < V; ++v) src[u][v] = po[(int64_t)(p0 + q + u) * stride * D + v];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const float wu = __shfl(wt, q + u);
 #pragma unroll
-          for (int v = 0; v < V; ++v) acc[v] = fmaf(wu, src[u][v], acc[v]);
+          for (int v = 0; v < V; ++v) acc[v] = fmaf(wu, wu != 0.f ? src[u][v] : 0.f, acc[v]);
         }
       }
       for (; q < pn; ++q) {
         const float wu = __shfl(wt, q);
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-          acc[v] = fmaf(wu, a.part_o[(rec0 + (int64_t)(p0 + q) * stride) * D + lane * V + v], acc[v]);
+        for (int v = 0; v < V; ++v) {
+          const float x = po[(int64_t)(p0 + q) * stride * D + v];
+          acc[v] = fmaf(wu, wu != 0.f ? x : 0.f, acc[v]);
+        }
       }
     }
   }

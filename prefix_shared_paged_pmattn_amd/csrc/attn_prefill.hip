@@ -112,8 +112,8 @@ __device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restr
     const int q = tid + 256 * u;
     const int b = q / PER_BLOCK, r = q % PER_BLOCK;
     const int64_t base = (int64_t)blk[b] * hkv + kvh;
-    // K block [16 tokens][D]: token r / (D/8), channel chunk r % (D/8)
-    st.k[u] = *reinterpret_cast<const uint4*>(kpool + (base * 16 + r / (D / 8)) * D + 8 * (r % (D / 8)));
+    // grouped K block [D/8][16 tokens][8]: channel group r / 16, token r % 16
+    st.k[u] = *reinterpret_cast<const uint4*>(kpool + base * 16 * D + 8 * r);
     // V block [D][16 tokens]: channel r / 2, half r % 2
     st.v[u] = *reinterpret_cast<const uint4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
   }
@@ -149,7 +149,7 @@ __device__ __forceinline__ void stage_store(uint16_t* lds, Stage<D>& st, int c0,
   for (int u = 0; u < P; ++u) {
     const int q = tid + 256 * u;
     const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-    *reinterpret_cast<uint4*>(kl + (16 * b + r / (D / 8)) * Cfg<D>::KROW + 8 * (r % (D / 8))) = st.k[u];
+    *reinterpret_cast<uint4*>(kl + (16 * b + r % 16) * Cfg<D>::KROW + 8 * (r / 16)) = st.k[u];
     *reinterpret_cast<uint4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = st.v[u];
   }
 }

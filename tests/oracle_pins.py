@@ -87,6 +87,7 @@ def _dense_batch(seq_specs, hq, hkv, d, dtype, seed, shared_blocks=0):
     if dtype == "bf16":
         k_pool, v_pool, q = (wl.f32_to_bf16_bits(k_pool), wl.f32_to_bf16_bits(v_pool),
                              wl.f32_to_bf16_bits(q))
+    k_pool = wl.k_pool_layout(k_pool, dtype)
     scale = float(np.float32(1.0 / math.sqrt(d) * (1.0 + 0.37 * (seed % 3))))
     b = wl.Batch(name="dense", q_len=np.array([s["q_len"] for s in seq_specs], np.int32),
                  seq_len=np.array([s["seq_len"] for s in seq_specs], np.int32),
@@ -137,7 +138,7 @@ def pin_single_key(attend):
         for h in range(4):
             g = h // 2
             v0 = _vals(b, b.v_pool[bt[s, 0], g, :, 0])
-            k0 = _vals(b, b.k_pool[bt[s, 0], g, 0, :])
+            k0 = _vals(b, b.k_pool[bt[s, 0], g, :, 0, :].reshape(-1))
             assert np.array_equal(out[row, h], v0), "one visible key must give exactly V_0"
             s0 = b.scale * math.fsum(float(a) * float(c) for a, c in zip(qv[row, h], k0))
             assert abs(lse[row, h] - s0) <= 1e-12 * max(1.0, abs(s0))
@@ -169,7 +170,7 @@ def pin_two_keys(attend):
     qv = _vals(b, b.q)
     blk = b.block_table[0, 0]
     for h in range(3):
-        k = [_vals(b, b.k_pool[blk, h, j, :]) for j in (0, 1)]
+        k = [_vals(b, b.k_pool[blk, h, :, j, :].reshape(-1)) for j in (0, 1)]
         v = [_vals(b, b.v_pool[blk, h, :, j]) for j in (0, 1)]
         s = [b.scale * math.fsum(float(x) * float(y) for x, y in zip(qv[1, h], k[j])) for j in (0, 1)]
         w0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
@@ -195,6 +196,7 @@ def pin_golden(attend):
         for j in range(n):
             k_pool[j // 16, 0, j % 16] = keys[j]
             v_pool[j // 16, 0, :, j % 16] = vals[j]
+        k_pool = wl.k_pool_layout(k_pool, "f32")
         b = wl.Batch(name=fn, q_len=np.array([1], np.int32), seq_len=np.array([n], np.int32),
                      q_start=np.array([n - 1], np.int32),
                      block_table=np.arange(nb, dtype=np.int32)[None], num_pool_blocks=nb,
@@ -209,7 +211,7 @@ def pin_golden(attend):
 def pin_brute_force_sdpa(attend):
     """Small exhaustive batches vs dense torch SDPA (fp64) on K/V scattered by the test."""
     shapes = [(1, 1), (2, 1), (4, 2), (6, 3)]
-    dims = [1, 2, 4, 8]
+    dims = [1, 2, 4, 8, 24]
     cases = 0
     for ci, (hq, hkv) in enumerate(shapes):
         for di, d in enumerate(dims):
@@ -351,6 +353,12 @@ def pin_split_merge(mod):
         perm = rng.permutation(parts)
         mo2, ml2 = mod.merge_partitions(np.array(po)[perm], np.array(pl)[perm])
         assert np.allclose(mo2, mo, rtol=0, atol=1e-14) and np.allclose(ml2, ml, rtol=0, atol=1e-14)
+        # an extra empty partition (no keys: lse -inf) contributes nothing,
+        # whatever its output slot holds
+        junk_o = np.full_like(po[0], np.nan)
+        junk_l = np.full_like(pl[0], -np.inf)
+        mo3, ml3 = mod.merge_partitions(np.array(po + [junk_o]), np.array(pl + [junk_l]))
+        assert np.array_equal(mo3, mo) and np.array_equal(ml3, ml)
     # one known two-way split checked against the closed form of the merge
     o_a, l_a = mod.attend_partitioned(b, [0, 0, 0], [16, 16, 16])
     o_b, l_b = mod.attend_partitioned(b, [16, 16, 16], [70, 33, 20])

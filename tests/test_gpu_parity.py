@@ -204,15 +204,19 @@ def test_empty_plan_launches_nothing():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
-def test_merge_lse_standalone(d, out_dtype):
+@pytest.mark.parametrize("P", [5, 100])
+def test_merge_lse_standalone(d, out_dtype, P):
     import torch
-    rng = np.random.Generator(np.random.PCG64(d))
-    P, rows, H = 5, 7, 3
+    rng = np.random.Generator(np.random.PCG64(d + P))
+    rows, H = 7, 3
     po = rng.standard_normal((P, rows, H, d)).astype(np.float32)
     pl = (rng.standard_normal((P, rows, H)) * 3).astype(np.float32)
-    pl[1, 2, :] = -np.inf            # an empty partition
+    pl[1, 2, :] = -np.inf            # an empty partition: its output slot is not read
+    po[1, 2, :] = np.nan
+    pl[P - 1, 5, :] = -np.inf        # an empty partition past the first 64
+    po[P - 1, 5, :] = np.nan
     pl[:, 4, 1] = -np.inf            # a row with every partition empty
-    po[:, 4, 1] = 0
+    po[:, 4, 1] = np.nan
     ref_o, ref_l = oracle.merge_partitions(po.astype(np.float64), pl.astype(np.float64))
     et = torch.bfloat16 if out_dtype == "bf16" else torch.float32
     out = torch.full((rows, H, d), float("nan"), dtype=et, device="cuda:0")

@@ -19,6 +19,8 @@ MUTANTS = {
     "slot-off-by-one": ("off = j % BLOCK", "off = (j + 1) % BLOCK"),
     "block-index-wrong": ("blk = np.asarray(bt_row)[j // BLOCK]", "blk = np.asarray(bt_row)[j // (2 * BLOCK)]"),
     "v-layout-token-major": ("v = v_pool[blk, kv_head, :, off]", "v = v_pool[blk, kv_head, :, :].reshape(len(j), -1)[:, :k_pool.shape[-1]]"),
+    "k-layout-token-major": ("k = k_pool[blk, kv_head, :, off, :]",
+                             "k = k_pool[blk, kv_head].reshape(len(j), BLOCK, -1)[np.arange(len(j)), off]"),
     "scale-dropped": ("scores = scale * (qf[:, h, :] @ kk.T)", "scores = (qf[:, h, :] @ kk.T)"),
     "k-v-swapped": ("scores = scale * (qf[:, h, :] @ kk.T)", "scores = scale * (qf[:, h, :] @ vv.T)"),
     "no-normalisation": ("o[has] = (w[has] @ vv) / l[has, None]", "o[has] = (w[has] @ vv)"),

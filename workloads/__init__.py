@@ -9,7 +9,9 @@ method code.
 Memory layouts (the library ABI and the oracle read the same bytes):
 
 * ``q``        ``[R][Hq][d]``       rows packed per sequence in descriptor order
-* ``k_pool``   ``[num_blocks][Hkv][16][d]``   token-major inside a block
+* ``k_pool``   ``[num_blocks][Hkv][d/x][16][x]``   inside a block: channel
+  groups of x = gcd(d, 16 bytes / element size) (8 for bf16, 4 for fp32 at
+  d = 64 or 128), each holding the block's 16 tokens; see ``k_pool_layout``
 * ``v_pool``   ``[num_blocks][Hkv][d][16]``   channel-major inside a block
 * ``block_table`` int32 ``[B][bt_stride]``; entries past a sequence's last
   block are ``-1``.
@@ -52,6 +54,25 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
         flat_out[a:a + step] = u
         flat_out[a:a + step][nan] = 0x7FC0
     return out
+
+
+def k_group(d: int, dtype: str) -> int:
+    """Channels per 16-byte group of the K pool layout: gcd(d, 16 / element size)."""
+    return math.gcd(int(d), 8 if dtype == "bf16" else 4)
+
+
+def k_pool_layout(k_tok: np.ndarray, dtype: str) -> np.ndarray:
+    """Token-major K blocks ``[blocks][Hkv][16][d]`` -> the pool layout
+    ``[blocks][Hkv][d/x][16][x]`` (a pure relayout; values are unchanged)."""
+    nb, h, t, d = k_tok.shape
+    x = k_group(d, dtype)
+    return np.ascontiguousarray(k_tok.reshape(nb, h, t, d // x, x).transpose(0, 1, 3, 2, 4))
+
+
+def k_token_major(k_pool: np.ndarray) -> np.ndarray:
+    """Inverse of ``k_pool_layout``: a ``[blocks][Hkv][16][d]`` copy."""
+    nb, h, g, t, x = k_pool.shape
+    return np.ascontiguousarray(k_pool.transpose(0, 1, 3, 2, 4)).reshape(nb, h, t, g * x)
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
@@ -166,7 +187,7 @@ def _assemble(name: str, seqs: List[dict], node_blocks: Dict[object, int], *,
     q = k = v = None
     if values:
         q = _normal(rng, (r, hq, d), dtype)
-        k = _normal(rng, (total, hkv, BLOCK, d), dtype)
+        k = k_pool_layout(_normal(rng, (total, hkv, BLOCK, d), dtype), dtype)
         v = _normal(rng, (total, hkv, d, BLOCK), dtype)
     if scale is None:
         scale = float(np.float32(1.0 / math.sqrt(d)))
@@ -308,7 +329,7 @@ def with_poison(b: Batch, value: float = float("nan")) -> Batch:
     else:
         fill = np.float32(value)
     blk, off = np.nonzero(~vis)
-    k[blk, :, off, :] = fill
+    k[blk, :, :, off, :] = fill
     v[blk, :, :, off] = fill
     return b.replace(k_pool=k, v_pool=v, name=b.name + "+poison")
 
