@@ -41,6 +41,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash():
+    """First 16 hex digits of the sha256 over the decode kernel's source and the
+    planner's (the planner decides the split partials the kernel writes)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "plan.cpp"):
+        with open(os.path.join(ROOT, "prefix_shared_paged_pmattn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(config_idx):
     """HBM bytes per launch of the tasks kernel from the committed rocprofv3
     counter summary (FETCH_SIZE and WRITE_SIZE, calibrated by a 1 GiB copy),
@@ -51,10 +62,9 @@ def measured_traffic(config_idx):
     if prof is None:
         return None
     path = os.path.join(ROOT, "profiles", prof)
-    src = os.path.join(ROOT, "prefix_shared_paged_pmattn_amd", "csrc", "attn_bf16.hip")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = kernel_source_hash()
     except OSError:
         return None
     fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes", "kernel_source")))
