@@ -3,8 +3,9 @@
 Default workload: decode over a paged GQA KV pool, one Llama-3-8B-shaped layer
 (64 sequences, context lengths uniform in [512, 4096], 32 query / 8 kv heads,
 head_dim 128, bf16, 16-token blocks, random non-contiguous block tables).
-``--config N`` selects one of the five synthetic workloads instead
-(1 tiny fp32, 2 decode, 3 few-shot shared prefix, 4 mixed chunk, 5 long decode).
+``--config N`` selects one of the six synthetic workloads instead
+(1 tiny fp32, 2 decode, 3 few-shot shared prefix, 4 mixed chunk, 5 long decode,
+6 token-tree verify).
 
 One step = one ``pmattn_forward`` of the whole batch (tile tasks + merge) with
 inputs resident in HBM; the plan is built once per batch on the host (as a
@@ -162,7 +163,8 @@ def main():
         return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table,
                        num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
                        num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
-                       scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus)
+                       scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus,
+                       tree_parent=b.tree_parent)
 
     plan_times = []
     for _ in range(20):

@@ -94,7 +94,18 @@ typedef enum pmattn_dtype { PMATTN_BF16 = 0, PMATTN_F32 = 1 } pmattn_dtype;
  *              partition p = [p*chunk*16, min((p+1)*chunk*16, q_start+q_len))).
  *  num_cus     compute units the plan balances for (0: 256, one MI355X).
  *  work_shuffle_seed  0: deterministic cost order; otherwise the work list is
- *              permuted by this seed (results must not change: a race check). */
+ *              permuted by this seed (results must not change: a race check).
+ *  tree_parent NULL (every row causal), or [R] int32, one entry per query row
+ *              in row order: the row (0-based, within the same sequence) of its
+ *              parent in a speculative token tree, or -1 for a node that hangs
+ *              off the context. Requires -1 <= parent < row. The rows of a
+ *              sequence are the tree's nodes in topological order, their K/V at
+ *              positions q_start + row. Row r sees every key below q_start
+ *              plus the keys of its ancestors and itself (tree-based
+ *              speculative verification, XY-Serve review, Figure 8 caption and
+ *              "Significance"; Medusa and SpecInfer by title). A chain (parent
+ *              r - 1) is the causal rule. A sequence whose parents are not a
+ *              chain holds at most 64 rows. */
 typedef struct pmattn_plan_desc {
   int32_t num_seqs;
   const int32_t* q_len;
@@ -112,6 +123,7 @@ typedef struct pmattn_plan_desc {
   int32_t num_kv_splits;
   int32_t num_cus;
   uint64_t work_shuffle_seed;
+  const int32_t* tree_parent;
 } pmattn_plan_desc;
 
 typedef struct pmattn_plan_s* pmattn_plan_t;
@@ -162,6 +174,11 @@ typedef struct pmattn_plan_tables {
   int32_t num_merge_rows;
   const pmattn_merge_row* merge_rows;
   int32_t num_part_records;         /* partial (output, lse) records in the workspace */
+  /* [R] or NULL when no sequence is a tree: visibility of the keys just
+   * before each row. Bit d set: the key at position row_pos - d is visible
+   * (as far as the tree is concerned; d >= 64 and keys below q_start always
+   * are). Rows of causal sequences hold all ones. */
+  const uint64_t* row_tree_mask;
 } pmattn_plan_tables;
 
 /* Build a plan on the host. Validates the batch (see pmattn_plan_desc),
@@ -170,9 +187,10 @@ typedef struct pmattn_plan_tables {
  * Errors: PMATTN_E_INVALID for null pointers, negative lengths,
  * q_start + q_len > seq_len, a block id outside [0, num_pool_blocks) among the
  * blocks a row can see, bt_stride too small, Hq % Hkv != 0, scale not finite
- * or <= 0, num_kv_splits outside 0..256; PMATTN_E_UNSUPPORTED for
- * block_size != 16, head_dim not in {64, 128}, an unknown dtype, or
- * Hq / Hkv > 64. On success *out owns host memory until pmattn_plan_destroy. */
+ * or <= 0, num_kv_splits outside 0..256, a tree_parent entry outside
+ * [-1, row); PMATTN_E_UNSUPPORTED for block_size != 16, head_dim not in
+ * {64, 128}, an unknown dtype, Hq / Hkv > 64, or a tree of more than 64
+ * rows. On success *out owns host memory until pmattn_plan_destroy. */
 pmattn_status pmattn_plan(const pmattn_plan_desc* desc, pmattn_plan_t* out);
 
 void pmattn_plan_destroy(pmattn_plan_t plan);

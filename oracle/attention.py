@@ -27,6 +27,13 @@ What is computed, and where the pages fix it
   and the value row is never multiplied in.
 * Online softmax with rescaling equals standard softmax (same section, first
   "standard math" item), so exact softmax is the definition to compare with.
+* Tree-based speculative verification (XY-Serve review, Figure 8 caption and
+  the "Significance" paragraph; Medusa and SpecInfer, cited there by title):
+  the draft tokens of a sequence form a tree, stored as its query rows in
+  topological order with their K/V at positions q_start + r. The reading
+  taken: row r sees every key below q_start (the context) and the draft keys
+  of the rows on its own path to the context (its ancestors and itself),
+  nothing else. A chain of parents is the linear (causal) case.
 * Keys reached through shared physical blocks are the same keys as privately
   copied ones (same section: block-table management with radix-tree reuse and
   copy-on-write keeps K/V semantics).
@@ -77,6 +84,27 @@ def gather_kv(k_pool: np.ndarray, v_pool: np.ndarray, bt_row: np.ndarray, kv_hea
     return decode_values(k, dtype), decode_values(v, dtype)
 
 
+def _tree_visibility(b, s: int, local_rows: np.ndarray, n_keys: int) -> np.ndarray:
+    """bool [rows][n_keys]: keys a draft row may see under sequence s's token tree.
+
+    Context keys (below q_start) are visible to every row; a draft key
+    q_start + a is visible to row r iff a lies on the path from r to the
+    context (walking parent links, r itself included).
+    """
+    off = int(np.sum(np.asarray(b.q_len)[:s]))
+    ql, qs = int(b.q_len[s]), int(b.q_start[s])
+    parent = np.asarray(b.tree_parent)[off:off + ql]
+    vis = np.zeros((local_rows.shape[0], n_keys), dtype=bool)
+    vis[:, :min(qs, n_keys)] = True
+    for i, r in enumerate(local_rows):
+        a = int(r)
+        while a >= 0:
+            if qs + a < n_keys:
+                vis[i, qs + a] = True
+            a = int(parent[a])
+    return vis
+
+
 def _attend_impl(b, rows: Optional[Sequence[int]], key_lo: Optional[np.ndarray],
                  key_hi: Optional[np.ndarray]):
     hq, hkv, d = b.num_q_heads, b.num_kv_heads, b.head_dim
@@ -103,6 +131,8 @@ def _attend_impl(b, rows: Optional[Sequence[int]], key_lo: Optional[np.ndarray],
             raise ValueError("a query position lies beyond seq_len")
         j = np.arange(n_keys)
         visible = j[None, :] <= pos[:, None]      # explicit causal mask [rows][keys]
+        if getattr(b, "tree_parent", None) is not None:
+            visible &= _tree_visibility(b, s, r_glob - row_off[s], n_keys)
         if key_lo is not None:
             visible &= (j[None, :] >= key_lo[s]) & (j[None, :] < key_hi[s])
         qf = decode_values(b.q[r_glob], b.dtype)  # [nr][Hq][d]

@@ -40,6 +40,44 @@ def row_tables(q_len, q_start):
     return row_seq.astype(np.int32), row_pos.astype(np.int32)
 
 
+def row_tree_masks(q_len, tree_parent):
+    """Per-row visibility of the 64 keys just before the row, for token trees.
+
+    ``tree_parent`` gives each row's parent row within its sequence (-1: the
+    context). Bit k of a row's mask says whether the key k positions before
+    the row may be seen: set for the row itself and each ancestor (k = row -
+    ancestor), and for every k beyond the row's own index, which reaches into
+    the context. Sequences whose parents form a chain (the causal rule) get
+    all ones. Returns None when no sequence is a tree (or tree_parent is None).
+    """
+    if tree_parent is None:
+        return None
+    parent = np.asarray(tree_parent, np.int64)
+    masks = []
+    any_tree = False
+    first = 0
+    for ql in (int(x) for x in q_len):
+        par = parent[first:first + ql]
+        chain = all(int(par[r]) == r - 1 for r in range(ql))
+        any_tree = any_tree or not chain
+        for r in range(ql):
+            if chain:
+                masks.append((1 << 64) - 1)
+                continue
+            m = 0
+            for k in range(r + 1, 64):       # keys before the tree's first row
+                m |= 1 << k
+            a = r
+            while a >= 0:                    # the row and its ancestors
+                m |= 1 << (r - a)
+                a = int(par[a])
+            masks.append(m)
+        first += ql
+    if not any_tree:
+        return None
+    return np.array(masks, dtype=np.uint64)
+
+
 def token_tiles(q_len, q_start, group):
     """Runs of query tokens one task holds: a sequence with q_len * G <= 64
     rows is one tile (rows class 16, 32 or 64); a longer one is cut into runs

@@ -101,7 +101,9 @@ class Plan:
             split_begin=arr(t.split_begin, nsp), split_end=arr(t.split_end, nsp),
             items=items, class_rows=arr(t.class_rows, t.num_classes),
             class_begin=arr(t.class_begin, t.num_classes + 1), merge_rows=merge,
-            num_part_records=int(t.num_part_records))
+            num_part_records=int(t.num_part_records),
+            row_tree_mask=(np.ctypeslib.as_array(t.row_tree_mask, shape=(t.num_rows,)).copy()
+                           if t.row_tree_mask and t.num_rows else None))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the work list into ``workspace``."""
@@ -113,8 +115,10 @@ class Plan:
 
 def plan(q_len, seq_len, q_start, block_table, *, num_pool_blocks: int, num_q_heads: int,
          num_kv_heads: int, head_dim: int, dtype="bf16", scale: float, num_kv_splits: int = 0,
-         num_cus: int = 0, work_shuffle_seed: int = 0) -> Plan:
-    """``pmattn_plan`` over host arrays (int32-convertible)."""
+         num_cus: int = 0, work_shuffle_seed: int = 0, tree_parent=None) -> Plan:
+    """``pmattn_plan`` over host arrays (int32-convertible). ``tree_parent``:
+    None, or one int per query row (parent row within its sequence, -1 for the
+    context) for speculative token trees."""
     ql, sl, qs = _i32(q_len), _i32(seq_len), _i32(q_start)
     bt = _i32(block_table)
     if bt.ndim != 2:
@@ -123,13 +127,19 @@ def plan(q_len, seq_len, q_start, block_table, *, num_pool_blocks: int, num_q_he
     if sl.shape != (b,) or qs.shape != (b,) or bt.shape[0] != b:
         raise ValueError("q_len, seq_len, q_start and block_table disagree on num_seqs")
     i32p = lambda a: a.ctypes.data_as(L._i32p)  # noqa: E731
+    tp = None
+    if tree_parent is not None:
+        tp = _i32(tree_parent)
+        if tp.shape != (int(ql.sum()),):
+            raise ValueError("tree_parent needs one entry per query row")
     d = L.PlanDesc(num_seqs=b, q_len=i32p(ql), seq_len=i32p(sl), q_start=i32p(qs),
                    block_table=i32p(bt), bt_stride=int(bt.shape[1]),
                    num_pool_blocks=int(num_pool_blocks), block_size=16,
                    num_q_heads=int(num_q_heads), num_kv_heads=int(num_kv_heads),
                    head_dim=int(head_dim), dtype=_dtype_code(dtype), scale=float(scale),
                    num_kv_splits=int(num_kv_splits), num_cus=int(num_cus),
-                   work_shuffle_seed=int(work_shuffle_seed))
+                   work_shuffle_seed=int(work_shuffle_seed),
+                   tree_parent=i32p(tp) if tp is not None else None)
     h = ctypes.c_void_p()
     _check(L.load().pmattn_plan(ctypes.byref(d), ctypes.byref(h)))
     shape = dict(num_seqs=b, num_rows=int(ql.sum()), bt_stride=int(bt.shape[1]),

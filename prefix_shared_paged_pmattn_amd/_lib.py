@@ -31,6 +31,7 @@ class PlanDesc(ctypes.Structure):
         ("num_kv_splits", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("work_shuffle_seed", ctypes.c_uint64),
+        ("tree_parent", _i32p),
     ]
 
 
@@ -61,6 +62,7 @@ class PlanTables(ctypes.Structure):
         ("num_merge_rows", ctypes.c_int32),
         ("merge_rows", ctypes.POINTER(MergeRow)),
         ("num_part_records", ctypes.c_int32),
+        ("row_tree_mask", ctypes.POINTER(ctypes.c_uint64)),
     ]
 
 

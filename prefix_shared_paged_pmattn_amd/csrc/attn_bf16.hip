@@ -121,11 +121,21 @@ __device__ __forceinline__ void zero_tail_v(Chunk<D>& ch, int c0, int kv_end, in
 // One 32-key chunk: scores, row-wise causal mask, online softmax, PV.
 // The mask is applied unconditionally (a handful of selects per 32 keys) so
 // that the streaming loop has no data-dependent branches.
-template <int D, int NT>
+// Token trees: rel[n] bit k set = the key k positions before row n's own is
+// visible; dbase[n] = that row's position - 4g. Chunks starting above tree_from
+// hold keys within 64 positions of some row of the task; only they are tested.
+template <int NT>
+struct TreeRows {
+  uint64_t rel[NT];
+  int dbase[NT];
+  int tree_from;
+};
+
+template <int D, int NT, bool TREE>
 __device__ __forceinline__ void compute_chunk(const Chunk<D>& ch, const bf16x8 (&qop)[NT][D / 32],
                                               f32x4 (&o)[NT][D / 16], float (&m_run)[NT],
                                               float (&l_run)[NT], const int (&lim_base)[NT], int c0,
-                                              float sl2, int g) {
+                                              float sl2, int g, const TreeRows<NT>& tr) {
   constexpr int KS = D / 32, DT = D / 16;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -141,6 +151,17 @@ __device__ __forceinline__ void compute_chunk(const Chunk<D>& ch, const bf16x8 (
     const int lim = lim_base[n] - c0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) sv[j] = (slot_off(j) < lim) ? sv[j] : kNegInf;
+    if constexpr (TREE) {
+      if (c0 > tr.tree_from) {
+        const int db = tr.dbase[n] - c0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int dd = db - slot_off(j);  // how far before the row's position
+          const bool hide = (unsigned)dd < 64u && !((tr.rel[n] >> dd) & 1ull);
+          sv[j] = hide ? kNegInf : sv[j];
+        }
+      }
+    }
     float mx = sv[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
@@ -213,7 +234,7 @@ struct Depth {
 // 2-wave workgroups measured the same or slower on the decode workloads).
 constexpr int kWavesPerWg = 4;
 
-template <int D, int NT>
+template <int D, int NT, bool TREE>
 __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 32, DT = D / 16;
@@ -276,6 +297,16 @@ void attn_bf16_kernel(AttnArgs a) {
   int lim_base[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) lim_base[n] = min(pos[n] + 1, kv_end) - 4 * g;
+  TreeRows<NT> tr;
+  if constexpr (TREE) {
+    tr.tree_from = it.pos_begin - 95;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int m = 16 * n + i;
+      tr.rel[n] = m < M ? a.row_mask[it.row_begin + m / G] : ~0ull;
+      tr.dbase[n] = pos[n] - 4 * g;
+    }
+  }
   if constexpr (Depth<NT>::value == 1) {
     // One buffer per wave; latency is hidden by the other waves on the SIMD.
     const int nch = (kv_end - it.kv_begin + 31) >> 5;
@@ -286,7 +317,7 @@ void attn_bf16_kernel(AttnArgs a) {
       load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
       chunk_ids(c0 + 32, b0, b1);
       zero_tail_v<D>(A, c0, kv_end, g);
-      compute_chunk<D, NT>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g);
+      compute_chunk<D, NT, TREE>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g, tr);
       c0 += 32;
     }
   } else {
@@ -313,12 +344,12 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int k = 0; k < npairs; ++k) {
       chunk_ids(c0 + 64, b0, b1);
       zero_tail_v<D>(A, c0, kv_end, g);
-      compute_chunk<D, NT>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g);
+      compute_chunk<D, NT, TREE>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g, tr);
       load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
       issue_barrier();
       chunk_ids(c0 + 96, b0, b1);
       zero_tail_v<D>(B, c0 + 32, kv_end, g);
-      compute_chunk<D, NT>(B, qop, o, m_run, l_run, lim_base, c0 + 32, sl2, g);
+      compute_chunk<D, NT, TREE>(B, qop, o, m_run, l_run, lim_base, c0 + 32, sl2, g, tr);
       load_chunk<D>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
       issue_barrier();
       c0 += 64;
@@ -363,7 +394,11 @@ void attn_bf16_kernel(AttnArgs a) {
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
   const dim3 grid((a.item_count + kWavesPerWg - 1) / kWavesPerWg), block(64 * kWavesPerWg);
-#define PMATTN_LAUNCH(D, NT) hipLaunchKernelGGL((attn_bf16_kernel<D, NT>), grid, block, 0, st, a)
+#define PMATTN_LAUNCH(D, NT)                                                            \
+  do {                                                                                 \
+    if (a.row_mask) hipLaunchKernelGGL((attn_bf16_kernel<D, NT, true>), grid, block, 0, st, a); \
+    else hipLaunchKernelGGL((attn_bf16_kernel<D, NT, false>), grid, block, 0, st, a);  \
+  } while (0)
   if (head_dim == 128) {
     if (class_rows <= 16) PMATTN_LAUNCH(128, 1);
     else if (class_rows <= 32) PMATTN_LAUNCH(128, 2);

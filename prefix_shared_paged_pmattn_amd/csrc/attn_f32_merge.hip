@@ -39,13 +39,16 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int qh = kvh * G + (m - t * G);
     const int64_t row = it.row_begin + t;
     const int kend = min(it.kv_end, it.pos_begin + t + 1);
+    const int rpos = it.pos_begin + t;
+    const uint64_t rel = a.row_mask ? a.row_mask[row] : ~0ull;  // token tree
     const float* qrow = qp + (row * hq + qh) * D;
     float m_run = kNegInf, l_run = 0.f, acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
     for (int kb = it.kv_begin; kb < kend; kb += 64) {
       const int j = kb + lane;
-      const bool valid = j < kend;
+      const int dd = rpos - j;
+      const bool valid = j < kend && !((unsigned)dd < 64u && !((rel >> dd) & 1ull));
       const int blk = valid ? bt_row[j >> 4] : 0;
       float s = kNegInf;
       if (valid) {
@@ -55,8 +58,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         for (int c = 0; c < D; ++c) dot = fmaf(qrow[c], kr[(c >> 2) * 64 + (c & 3)], dot);
         s = dot * a.scale;
       }
-      const float m_new = fmaxf(m_run, wave_max(s));  // finite: key kb is visible
-      const float alpha = expf(m_run - m_new);
+      // a window can hide every key (a token tree over a KV partition)
+      const float m_new = fmaxf(m_run, wave_max(s));
+      const float alpha = m_new == kNegInf ? 1.f : expf(m_run - m_new);
       const float p = valid ? expf(s - m_new) : 0.f;
       l_run = l_run * alpha + wave_sum(p);
 #pragma unroll

@@ -20,6 +20,7 @@ struct AttnArgs {
   void* out;
   float* lse;                    // may be null
   const pmattn_work_item* items; // this launch's first task
+  const uint64_t* row_mask;      // [R] token-tree masks, or null: every row causal
   float* part_o;                 // [records][d]
   float* part_lse;               // [records]
   int32_t item_count;

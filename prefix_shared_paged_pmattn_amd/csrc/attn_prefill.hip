@@ -170,10 +170,11 @@ __device__ __forceinline__ void keep_compute_branch() {
 
 // One 32-key score tile: S^T = K.Q^T, mask, online softmax with lazy
 // rescale, then O^T += V^T.P^T.
-template <int D>
+template <int D, bool TREE>
 __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const bf16x8 (&qop)[D / 16],
                                              f32x16 (&o)[D / 32], float& m_used, float& l_part,
-                                             bool mask, int lim, float sl2, int i32, int h) {
+                                             bool mask, int lim, float sl2, int i32, int h,
+                                             uint64_t rel, int dpos) {
   constexpr int KSTEPS = D / 16, DT = D / 32;
   const uint16_t* kl = lds;
   const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
@@ -189,6 +190,15 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
     // visible iff key < lim (lim = min(pos + 1, kv_end) - c0 for this lane's row)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = key_off(kt, r, h) < lim ? s[r] : kNegInf;
+    if constexpr (TREE) {
+      // token tree: bit k of rel = the key k positions before the row's own
+      // position is visible (dpos = that position - c0)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dd = dpos - key_off(kt, r, h);
+        s[r] = ((unsigned)dd < 64u && !((rel >> dd) & 1ull)) ? kNegInf : s[r];
+      }
+    }
   }
   float mx = s[0];
 #pragma unroll
@@ -224,15 +234,17 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
   }
 }
 
-template <int D>
+template <int D, bool TREE>
 __device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 (&qop)[D / 16],
                                               f32x16 (&o)[D / 32], float& m_used, float& l_part,
-                                              bool mask, int lim, float sl2, int i32, int h) {
+                                              bool mask, int lim, float sl2, int i32, int h,
+                                              uint64_t rel, int dpos) {
 #if PMATTN_PF_TILE_OUTER
 #pragma unroll
   for (int kt = 0; kt < Cfg<D>::NTILE; ++kt)
-    compute_tile<D>(lds, kt, qop, o, m_used, l_part, mask, lim, sl2, i32, h);
+    compute_tile<D, TREE>(lds, kt, qop, o, m_used, l_part, mask, lim, sl2, i32, h, rel, dpos);
 #else
+  static_assert(!TREE, "token trees take the tile-outer path");
   constexpr int KSTEPS = D / 16, DT = D / 32, NT = Cfg<D>::NTILE;
   const uint16_t* kl = lds;
   const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
@@ -298,7 +310,7 @@ __device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 
 #endif
 }
 
-template <int D>
+template <int D, bool TREE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PMATTN_PF_WAVES, PMATTN_PF_WAVES)))
 void attn_prefill_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 16, DT = D / 32, CHUNK = Cfg<D>::CHUNK;
@@ -339,6 +351,9 @@ void attn_prefill_kernel(AttnArgs a) {
   const int nch = (kv_end - it.kv_begin + CHUNK - 1) / CHUNK;
   const int min_pos = it.pos_begin;  // first token of the task
   const int row_lim = min(pos + 1, kv_end);
+  uint64_t rel = ~0ull;
+  if constexpr (TREE)
+    if (row_valid) rel = a.row_mask[it.row_begin + t];
   const float sl2 = a.scale_log2;
 
   // physical ids of the chunk's blocks; blocks past the last one repeat it
@@ -364,9 +379,10 @@ void attn_prefill_kernel(AttnArgs a) {
     }
     issue_barrier();
     const uint16_t* cur = lds + (c & 1) * Cfg<D>::STAGE;
-    // a chunk every row of the task sees whole needs no mask
-    const bool mask = c0 + CHUNK - 1 > min_pos || c0 + CHUNK > kv_end;
-    compute_chunk<D>(cur, qop, o, m_used, l_part, mask, row_lim - c0, sl2, i32, h);
+    // a chunk every row of the task sees whole needs no mask; in a token tree
+    // that excludes the 64 keys before the task's first row
+    const bool mask = c0 + CHUNK - 1 > min_pos - (TREE ? 64 : 0) || c0 + CHUNK > kv_end;
+    compute_chunk<D, TREE>(cur, qop, o, m_used, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
     if (more) stage_store<D>(lds + ((c + 1) & 1) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
     __syncthreads();
   }
@@ -408,10 +424,14 @@ void attn_prefill_kernel(AttnArgs a) {
 hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
   const dim3 grid(a.item_count), block(256);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((attn_prefill_kernel<128>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_prefill_kernel<64>), grid, block, 0, st, a);
+  const bool tree = a.row_mask != nullptr;
+  if (head_dim == 128) {
+    if (tree) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<128, false>), grid, block, 0, st, a);
+  } else {
+    if (tree) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_prefill_kernel<64, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

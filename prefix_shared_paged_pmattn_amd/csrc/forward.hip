@@ -99,6 +99,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.block_table = block_table_dev;
   a.out = out;
   a.lse = lse;
+  a.row_mask = P.row_mask.empty() ? nullptr : reinterpret_cast<const uint64_t*>(ws + P.off_row_mask);
   a.part_o = reinterpret_cast<float*>(ws + P.off_part_o);
   a.part_lse = reinterpret_cast<float*>(ws + P.off_part_lse);
   a.bt_stride = P.bt_stride;

@@ -132,6 +132,54 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       }
   }
 
+  // ---- speculative token trees: per-row visibility of the 64 keys before it --
+  // Bit k of a row's mask stands for the key k positions back. Ancestors (and
+  // the row itself) set their bits; keys below q_start are context and always
+  // visible, so every bit past the row's own index is set too. Chains (parent
+  // r - 1) give all ones, the causal rule.
+  if (d->tree_parent && rows > 0) {
+    bool any_tree = false;
+    int64_t r0 = 0;
+    for (int s = 0; s < B; ++s) {
+      const int ql = d->q_len[s];
+      bool chain = true;
+      for (int r = 0; r < ql; ++r) {
+        const int32_t par = d->tree_parent[r0 + r];
+        if (par < -1 || par >= r)
+          return fail(PMATTN_E_INVALID, "tree_parent must lie in [-1, row) at sequence " +
+                                            std::to_string(s) + " row " + std::to_string(r));
+        chain = chain && par == r - 1;
+      }
+      if (!chain && ql > kMaxTreeRows)
+        return fail(PMATTN_E_UNSUPPORTED, "a token tree holds at most 64 rows (sequence " +
+                                              std::to_string(s) + ")");
+      any_tree = any_tree || !chain;
+      r0 += ql;
+    }
+    if (any_tree) {
+      P.row_mask.assign(rows, ~0ull);
+      std::vector<uint64_t> anc;  // bit a: row a of the sequence is an ancestor-or-self
+      r0 = 0;
+      for (int s = 0; s < B; ++s) {
+        const int ql = d->q_len[s];
+        bool chain = true;
+        for (int r = 0; r < ql; ++r) chain = chain && d->tree_parent[r0 + r] == r - 1;
+        if (!chain) {
+          anc.assign(ql, 0);
+          for (int r = 0; r < ql; ++r) {
+            const int32_t par = d->tree_parent[r0 + r];
+            anc[r] = (par < 0 ? 0ull : anc[par]) | (1ull << r);
+            uint64_t m = r < 63 ? ~0ull << (r + 1) : 0ull;
+            for (int a = 0; a <= r; ++a)
+              if (anc[r] >> a & 1ull) m |= 1ull << (r - a);
+            P.row_mask[r0 + r] = m;
+          }
+        }
+        r0 += ql;
+      }
+    }
+  }
+
   // ---- tiles: runs of query tokens whose G heads fit one task --------------
   // A sequence whose rows fit one wave task (q_len * G <= 64) is one tile;
   // longer ones are cut into runs of 128/G tokens for the workgroup kernel.
@@ -261,7 +309,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // ---- workspace layout and the upload image --------------------------------
   P.off_items = 0;
   P.off_merge = align_up(P.off_items + P.items.size() * sizeof(pmattn_work_item), kAlign);
-  P.off_part_o = align_up(P.off_merge + P.merge_rows.size() * sizeof(pmattn_merge_row), kAlign);
+  P.off_row_mask = align_up(P.off_merge + P.merge_rows.size() * sizeof(pmattn_merge_row), kAlign);
+  P.off_part_o = align_up(P.off_row_mask + P.row_mask.size() * sizeof(uint64_t), kAlign);
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
   P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
   P.upload_blob.assign(P.off_part_o, 0);
@@ -271,6 +320,9 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (!P.merge_rows.empty())
     std::memcpy(P.upload_blob.data() + P.off_merge, P.merge_rows.data(),
                 P.merge_rows.size() * sizeof(pmattn_merge_row));
+  if (!P.row_mask.empty())
+    std::memcpy(P.upload_blob.data() + P.off_row_mask, P.row_mask.data(),
+                P.row_mask.size() * sizeof(uint64_t));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -330,6 +382,7 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->num_merge_rows = (int32_t)P.merge_rows.size();
   t->merge_rows = P.merge_rows.data();
   t->num_part_records = P.num_records;
+  t->row_tree_mask = P.row_mask.empty() ? nullptr : P.row_mask.data();
   return PMATTN_OK;
 }
 

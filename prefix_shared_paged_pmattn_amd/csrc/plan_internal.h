@@ -22,6 +22,7 @@ constexpr int kMaxTaskRows = 128;
 constexpr int kNumClasses = 4;
 constexpr int kClassRows[kNumClasses] = {16, 32, 64, 128};
 constexpr int kMaxSplits = 256;
+constexpr int kMaxTreeRows = 64;
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -39,8 +40,11 @@ struct Plan {
   std::vector<int32_t> class_rows, class_begin;
   std::vector<pmattn_merge_row> merge_rows;
   int32_t num_records = 0;
-  // workspace layout (bytes): [items | merge rows | partial O | partial lse]
-  size_t off_items = 0, off_merge = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+  // tree masks, one per row, present only when some sequence is a tree
+  std::vector<uint64_t> row_mask;
+  // workspace layout (bytes): [items | merge rows | row masks | partial O | partial lse]
+  size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_part_o = 0, off_part_lse = 0,
+         ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 

@@ -36,7 +36,8 @@ def make_plan(b, **kw):
     return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, num_pool_blocks=b.num_pool_blocks,
                    num_q_heads=b.num_q_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                    dtype=b.dtype, scale=b.scale,
-                   num_kv_splits=kw.pop("num_kv_splits", b.num_kv_splits), **kw)
+                   num_kv_splits=kw.pop("num_kv_splits", b.num_kv_splits),
+                   tree_parent=kw.pop("tree_parent", b.tree_parent), **kw)
 
 
 def run_gpu(b, dev=None, out_fill=float("nan"), **plan_kw):

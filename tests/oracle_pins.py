@@ -327,9 +327,81 @@ def pin_convexity(attend):
         assert np.all(out[row, 0] <= vals.max(axis=0) + 1e-15)
 
 
+def _linearized(b, s, path):
+    """One causal sequence: sequence s's context followed, at consecutive
+    positions, by the K/V and queries of the tree rows ``path`` (context end
+    first). Built by plain copying, in fresh pool blocks."""
+    qs = int(b.q_start[s])
+    n = qs + len(path)
+    nb = -(-n // 16)
+    src = [(int(b.block_table[s, j // 16]), j % 16) for j in range(qs)]
+    src += [(int(b.block_table[s, (qs + a) // 16]), (qs + a) % 16) for a in path]
+    k_tok = wl.k_token_major(b.k_pool)
+    k_new = np.zeros((nb,) + k_tok.shape[1:], k_tok.dtype)
+    v_new = np.zeros((nb,) + b.v_pool.shape[1:], b.v_pool.dtype)
+    for j, (blk, slot) in enumerate(src):
+        k_new[j // 16, :, j % 16, :] = k_tok[blk, :, slot, :]
+        v_new[j // 16, :, :, j % 16] = b.v_pool[blk, :, :, slot]
+    first = int(np.sum(b.q_len[:s]))
+    return b.replace(q_len=np.array([len(path)], np.int32), seq_len=np.array([n], np.int32),
+                     q_start=np.array([qs], np.int32), block_table=np.arange(nb, dtype=np.int32)[None],
+                     num_pool_blocks=nb, q=b.q[[first + a for a in path]],
+                     k_pool=wl.k_pool_layout(k_new, b.dtype), v_pool=v_new, tree_parent=None)
+
+
+def _tree_batch(seed=41, dtype="bf16"):
+    return wl.custom([dict(q_len=9, seq_len=50, q_start=41, tree=wl.random_tree(9, 3)),
+                      dict(q_len=1, seq_len=20),
+                      dict(q_len=12, seq_len=30, q_start=18, tree=wl.random_tree(12, 4, max_depth=3)),
+                      dict(q_len=4, seq_len=7, q_start=3),
+                      dict(q_len=5, seq_len=37, q_start=32, tree=[-1, -1, -1, -1, -1])],
+                     hq=4, hkv=2, d=16, dtype=dtype, seed=seed)
+
+
+def pin_tree_linearization(attend):
+    """Token-tree verification: every draft row gives what ordinary causal
+    attention gives for the sequence made of the context and that row's own
+    path through the tree (its ancestors, then itself, at consecutive
+    positions). A chain of parents is exactly the causal batch."""
+    for dtype in ("bf16", "f32"):
+        b = _tree_batch(dtype=dtype)
+        out, lse = attend(b)
+        off = b.row_offsets()
+        for s in range(b.num_seqs):
+            par = b.tree_parent[off[s]:off[s + 1]]
+            for r in range(int(b.q_len[s])):
+                path, a = [], r
+                while a >= 0:
+                    path.append(a)
+                    a = int(par[a])
+                o, l = attend(_linearized(b, s, path[::-1]))
+                assert np.allclose(o[-1], out[off[s] + r], rtol=0, atol=1e-13), (dtype, s, r)
+                assert np.allclose(l[-1], lse[off[s] + r], rtol=0, atol=1e-13), (dtype, s, r)
+        chain = b.replace(tree_parent=np.concatenate(
+            [np.arange(-1, int(q) - 1, dtype=np.int32) for q in b.q_len]))
+        o1, l1 = attend(chain)
+        o2, l2 = attend(b.replace(tree_parent=None))
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def pin_split_merge(mod):
     """Partial results over random disjoint key partitions (some empty), merged by
-    log-sum-exp, equal the unsplit result; the merge is order independent."""
+    log-sum-exp, equal the unsplit result; the merge is order independent. The
+    same holds for token-tree rows, whose partitions may hide every key."""
+    tb = _tree_batch(seed=43)
+    t_o, t_l = mod.attend(tb)
+    rng = np.random.Generator(np.random.PCG64(1))
+    for _ in range(4):
+        los, his = [], []
+        for s in range(tb.num_seqs):
+            n = int(tb.q_start[s] + tb.q_len[s])
+            cut = int(rng.integers(0, n + 1))
+            los.append([0, cut])
+            his.append([cut, n])
+        los, his = np.array(los), np.array(his)
+        parts = [mod.attend_partitioned(tb, los[:, p], his[:, p]) for p in range(2)]
+        mo, ml = mod.merge_partitions(np.array([p[0] for p in parts]), np.array([p[1] for p in parts]))
+        assert np.allclose(mo, t_o, rtol=0, atol=1e-13) and np.allclose(ml, t_l, rtol=0, atol=1e-13)
     b = wl.custom([dict(q_len=5, seq_len=70, q_start=60), dict(q_len=1, seq_len=33),
                    dict(q_len=3, seq_len=20, q_start=3)], hq=4, hkv=2, d=16, seed=31)
     ref_o, ref_l = mod.attend(b)
@@ -379,4 +451,4 @@ def pin_split_merge(mod):
 
 ALL_PINS = [pin_single_key, pin_equal_scores, pin_two_keys, pin_golden, pin_brute_force_sdpa,
             pin_mpmath, pin_shared_equals_private, pin_class_independence, pin_gqa_replication,
-            pin_convexity]
+            pin_convexity, pin_tree_linearization]

@@ -49,6 +49,26 @@ def _batch_cases():
         "mixed-classes": (dict(hq=8, hkv=2, d=128), [S(q_len=50, seq_len=300, q_start=250), S(q_len=1, seq_len=700),
                                                      S(q_len=5, seq_len=405), S(q_len=1, seq_len=33),
                                                      S(q_len=130, seq_len=130)], 0),
+        # speculative token trees: one-wave classes 16/32/64, workgroup tasks,
+        # partitions inside the tree, G = 8 at d = 64, star and chain shapes
+        "tree-wave-classes": (dict(hq=8, hkv=2, d=128), [S(q_len=4, seq_len=300, tree=wl.random_tree(4, 1)),
+                                                         S(q_len=8, seq_len=208, q_start=200, tree=wl.random_tree(8, 2)),
+                                                         S(q_len=16, seq_len=516, q_start=500,
+                                                           tree=wl.random_tree(16, 3, max_depth=4)),
+                                                         S(q_len=1, seq_len=90), S(q_len=5, seq_len=77)], 0),
+        "tree-workgroup": (dict(hq=8, hkv=2, d=128), [S(q_len=64, seq_len=1064, q_start=1000,
+                                                        tree=wl.random_tree(64, 4, max_depth=6)),
+                                                      S(q_len=40, seq_len=73, q_start=33, tree=wl.random_tree(40, 5))], 0),
+        "tree-splits": (dict(hq=8, hkv=2, d=128), [S(q_len=12, seq_len=60, q_start=48, tree=wl.random_tree(12, 6)),
+                                                   S(q_len=64, seq_len=80, q_start=16, tree=wl.random_tree(64, 7)),
+                                                   S(q_len=3, seq_len=45, q_start=42, tree=[-1, -1, 1])], 5),
+        "tree-g8-d64": (dict(hq=16, hkv=2, d=64), [S(q_len=8, seq_len=40, q_start=32, tree=[-1, 0, 0, 1, 1, 2, -1, 6]),
+                                                   S(q_len=30, seq_len=130, q_start=100, tree=wl.random_tree(30, 8))], 0),
+        "tree-star-chain-mixed": (dict(hq=8, hkv=2, d=128), [S(q_len=16, seq_len=116, q_start=100, tree=[-1] * 16),
+                                                             S(q_len=10, seq_len=30, q_start=20, tree=list(range(-1, 9))),
+                                                             S(q_len=60, seq_len=400, q_start=340), S(q_len=1, seq_len=500),
+                                                             S(q_len=33, seq_len=1033, q_start=1000,
+                                                               tree=wl.random_tree(33, 9, max_depth=3))], 0),
     }
 
 
@@ -67,6 +87,14 @@ def test_small_batches(name):
 
 def test_config1_f32_plumbing():
     b = wl.config(1)
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
+
+
+def test_f32_token_tree():
+    b = wl.custom([dict(q_len=9, seq_len=50, q_start=41, tree=wl.random_tree(9, 11)),
+                   dict(q_len=1, seq_len=20), dict(q_len=20, seq_len=36, q_start=16, tree=wl.random_tree(20, 12))],
+                  hq=4, hkv=2, d=64, dtype="f32", seed=5, num_kv_splits=4)
     out, lse = run_gpu(b)
     compare(b, out, lse)
 
@@ -149,6 +177,23 @@ def test_work_order_does_not_change_bits():
     for seed in (1, 2, 99):
         o, l = run_gpu(b, dev, work_shuffle_seed=seed)
         assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l)
+
+
+def test_token_tree_order_and_poison_bitwise():
+    """Token trees with split partitions: work-list shuffles and poison in slots
+    no row can see leave every bit unchanged."""
+    b = wl.custom([dict(q_len=20, seq_len=120, q_start=100, tree=wl.random_tree(20, 21)),
+                   dict(q_len=64, seq_len=70, q_start=6, tree=wl.random_tree(64, 22, max_depth=5)),
+                   dict(q_len=1, seq_len=77), dict(q_len=6, seq_len=50, q_start=40, tree=[-1, 0, 0, 1, 2, -1])],
+                  hq=8, hkv=2, d=128, seed=23, extra_blocks=2, num_kv_splits=3)
+    dev = to_device(b)
+    ref_o, ref_l = run_gpu(b, dev)
+    compare(b, ref_o, ref_l)
+    for seed in (3, 7):
+        o, l = run_gpu(b, dev, work_shuffle_seed=seed)
+        assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l)
+    o, l = run_gpu(wl.with_poison(b, float("nan")))
+    assert np.array_equal(o, ref_o) and np.array_equal(l, ref_l)
 
 
 def test_shared_blocks_equal_private_copies_bitwise():

@@ -21,6 +21,9 @@ MUTANTS = {
     "v-layout-token-major": ("v = v_pool[blk, kv_head, :, off]", "v = v_pool[blk, kv_head, :, :].reshape(len(j), -1)[:, :k_pool.shape[-1]]"),
     "k-layout-token-major": ("k = k_pool[blk, kv_head, :, off, :]",
                              "k = k_pool[blk, kv_head].reshape(len(j), BLOCK, -1)[np.arange(len(j)), off]"),
+    "tree-mask-dropped": ("visible &= _tree_visibility(b, s, r_glob - row_off[s], n_keys)", "pass"),
+    "tree-only-self": ("            a = int(parent[a])", "            a = -1"),
+    "tree-context-short": ("vis[:, :min(qs, n_keys)] = True", "vis[:, :max(0, min(qs, n_keys) - 1)] = True"),
     "scale-dropped": ("scores = scale * (qf[:, h, :] @ kk.T)", "scores = (qf[:, h, :] @ kk.T)"),
     "k-v-swapped": ("scores = scale * (qf[:, h, :] @ kk.T)", "scores = scale * (qf[:, h, :] @ vv.T)"),
     "no-normalisation": ("o[has] = (w[has] @ vv) / l[has, None]", "o[has] = (w[has] @ vv)"),

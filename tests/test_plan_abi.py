@@ -20,7 +20,7 @@ def make_plan(b, **kw):
     return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, num_pool_blocks=b.num_pool_blocks,
                    num_q_heads=b.num_q_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                    dtype=b.dtype, scale=b.scale, num_kv_splits=kw.pop("num_kv_splits", b.num_kv_splits),
-                   **kw)
+                   tree_parent=kw.pop("tree_parent", b.tree_parent), **kw)
 
 
 def check_plan(b, p, num_cus=0):
@@ -172,6 +172,60 @@ def test_error_paths():
                       dtype=0, scale=1.0)                  # null arrays
     assert lib.pmattn_plan(ctypes.byref(d), ctypes.byref(h)) == INV
     assert lib.pmattn_plan(None, ctypes.byref(h)) == INV
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tree_masks_match_replica(seed):
+    rng = np.random.Generator(np.random.PCG64(100 + seed))
+    seqs = []
+    for k in range(int(rng.integers(1, 6))):
+        kind = int(rng.integers(0, 4))
+        ql = int(rng.integers(1, 65))
+        qs = int(rng.integers(0, 200))
+        spec = dict(q_len=ql, seq_len=qs + ql + int(rng.integers(0, 20)), q_start=qs)
+        if kind == 0:
+            spec["tree"] = wl.random_tree(ql, seed * 10 + k)
+        elif kind == 1:
+            spec["tree"] = wl.random_tree(ql, seed * 10 + k, max_depth=int(rng.integers(1, 5)))
+        elif kind == 2:
+            spec["q_len"] = ql = int(rng.integers(1, 200))      # causal, may exceed 64 rows
+            spec["seq_len"] = qs + ql
+        seqs.append(spec)
+    seqs.append(dict(q_len=6, seq_len=40, tree=[-1, 0, 1, 1, 0, -1]))
+    b = wl.custom(seqs, hq=8, hkv=2, d=64, values=False)
+    p = make_plan(b)
+    check_plan(b, p)
+    t = p.tables()
+    want = R.row_tree_masks(b.q_len, b.tree_parent)
+    assert want is not None and t["row_tree_mask"] is not None
+    assert np.array_equal(t["row_tree_mask"], want)
+    # the same batch declared causal (or with chain parents) carries no masks
+    assert make_plan(b, tree_parent=None).tables()["row_tree_mask"] is None
+    chain = np.concatenate([np.arange(-1, int(q) - 1) for q in b.q_len])
+    assert make_plan(b, tree_parent=chain).tables()["row_tree_mask"] is None
+
+
+def test_tree_errors():
+    b = wl.custom([dict(q_len=3, seq_len=40), dict(q_len=70, seq_len=90)], hq=4, hkv=2, d=64,
+                  values=False)
+    kw = _desc_kwargs(b)
+    ok = np.concatenate([[-1, 0, 0], np.arange(-1, 69)])
+    pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, tree_parent=ok, **kw)  # 70-row chain
+    for bad_first, status, text in (([-1, 1, 0], _lib.E_INVALID, "tree_parent"),
+                                    ([-2, 0, 0], _lib.E_INVALID, "tree_parent"),
+                                    ([0, 0, 0], _lib.E_INVALID, "tree_parent")):
+        tp = ok.copy()
+        tp[:3] = bad_first
+        with pytest.raises(pm.PmattnError) as e:
+            pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, tree_parent=tp, **kw)
+        assert e.value.status == status and text in str(e.value)
+    tp = ok.copy()
+    tp[3 + 5] = 2                      # the 70-row sequence stops being a chain
+    with pytest.raises(pm.PmattnError) as e:
+        pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, tree_parent=tp, **kw)
+    assert e.value.status == _lib.E_UNSUPPORTED and "64" in str(e.value)
+    with pytest.raises(ValueError):
+        pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, tree_parent=ok[:-1], **kw)
 
 
 def test_unused_table_entries_are_not_validated():

@@ -108,6 +108,10 @@ class Batch:
     q: np.ndarray
     k_pool: np.ndarray
     v_pool: np.ndarray
+    # None: every row causal. Else int32 [R]: per query row, its parent row in
+    # a speculative token tree (within the sequence; -1 = hangs off the
+    # context). Rows are the tree's nodes in topological order.
+    tree_parent: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -202,16 +206,50 @@ def custom(seqs: Sequence[dict], *, hq: int = 4, hkv: int = 2, d: int = 64, dtyp
            scale: Optional[float] = None, extra_blocks: int = 0, name: str = "custom",
            values: bool = True) -> Batch:
     """Small hand-specified batch. ``seqs`` entries need ``q_len, seq_len`` and
-    optionally ``q_start`` (default ``seq_len - q_len``) and ``nodes``."""
+    optionally ``q_start`` (default ``seq_len - q_len``), ``nodes`` and
+    ``tree`` (parent of each of the q_len rows; sequences without one are
+    chains, i.e. causal)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     specs = []
     for s in seqs:
         specs.append(dict(q_len=int(s["q_len"]), seq_len=int(s["seq_len"]),
                           q_start=int(s.get("q_start", s["seq_len"] - s["q_len"])),
                           nodes=list(s.get("nodes", []))))
-    return _assemble(name, specs, dict(node_blocks or {}), hq=hq, hkv=hkv, d=d, dtype=dtype,
-                     rng=rng, num_kv_splits=num_kv_splits, scale=scale, extra_blocks=extra_blocks,
-                     values=values)
+    b = _assemble(name, specs, dict(node_blocks or {}), hq=hq, hkv=hkv, d=d, dtype=dtype,
+                  rng=rng, num_kv_splits=num_kv_splits, scale=scale, extra_blocks=extra_blocks,
+                  values=values)
+    if any("tree" in s for s in seqs):
+        parents = []
+        for s in seqs:
+            ql = int(s["q_len"])
+            tree = s.get("tree", list(range(-1, ql - 1)))
+            if len(tree) != ql:
+                raise ValueError("a tree needs one parent per query row")
+            parents.extend(int(x) for x in tree)
+        b = b.replace(tree_parent=np.array(parents, dtype=np.int32))
+    return b
+
+
+def random_tree(n: int, seed: int, max_depth: Optional[int] = None) -> List[int]:
+    """Parents of an n-node token tree in topological order: node r hangs off a
+    uniformly drawn earlier node or the context (-1), with depth <= max_depth."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    parents, depth = [], []
+    for r in range(n):
+        cands = [-1] + [a for a in range(r) if max_depth is None or depth[a] + 1 < max_depth]
+        p = int(cands[int(rng.integers(0, len(cands)))])
+        parents.append(p)
+        depth.append(1 if p < 0 else depth[p] + 1)
+    return parents
+
+
+def tree_ancestors(parents: Sequence[int], r: int) -> List[int]:
+    """Rows on the path from row r up to the context, r included."""
+    out = []
+    while r >= 0:
+        out.append(r)
+        r = int(parents[r])
+    return out
 
 
 # --------------------------------------------------------------------------
@@ -224,6 +262,7 @@ CONFIG_NAMES = {
     3: "fewshot-256x128-on-shared-2048",
     4: "mixed-prefill-decode-verify-radix",
     5: "long-decode-8x32k-paired-turns",
+    6: "tree-verify-64seq-32node",
 }
 
 
@@ -254,6 +293,16 @@ def config(idx: int, seed: Optional[int] = None, values: bool = True) -> Batch:
         nodes = {("pair", p): 1536 for p in range(4)}
         return _assemble(name, seqs, nodes, hq=64, hkv=8, d=128, dtype="bf16", rng=rng,
                          num_kv_splits=16, **kw)
+    if idx == 6:
+        # Tree-based speculative verification (XY-Serve review, Figure 8 caption):
+        # 64 sequences, context U{512..4096}, each verifying a 32-node draft tree
+        # of depth <= 6 whose parents are drawn uniformly among earlier nodes.
+        ctx = rng.integers(512, 4096, size=64, endpoint=True)
+        tree_seeds = rng.integers(0, 2 ** 31, size=64)
+        seqs = [dict(q_len=32, seq_len=int(c) + 32, q_start=int(c), nodes=[]) for c in ctx]
+        b = _assemble(name, seqs, {}, hq=32, hkv=8, d=128, dtype="bf16", rng=rng, **kw)
+        parents = [p for t in tree_seeds for p in random_tree(32, int(t), max_depth=6)]
+        return b.replace(tree_parent=np.array(parents, dtype=np.int32))
     raise KeyError(idx)
 
 
@@ -383,9 +432,14 @@ def algorithmic_work(b: Batch, with_lse: bool = True) -> dict:
     unique = int(vis.sum())
     logical = int(sum(int(b.q_start[s] + b.q_len[s]) for s in range(b.num_seqs) if b.q_len[s] > 0))
     pairs = 0
+    off = b.row_offsets()
     for s in range(b.num_seqs):
         ql, qs = int(b.q_len[s]), int(b.q_start[s])
-        pairs += ql * (qs + 1) + ql * (ql - 1) // 2
+        if b.tree_parent is None:
+            pairs += ql * (qs + 1) + ql * (ql - 1) // 2
+        else:
+            par = b.tree_parent[off[s]:off[s] + ql]
+            pairs += sum(qs + len(tree_ancestors(par, r)) for r in range(ql))
     e = b.elem_bytes
     hq, hkv, d, r = b.num_q_heads, b.num_kv_heads, b.head_dim, b.num_rows
     kv_bytes = unique * 2 * hkv * d * e
