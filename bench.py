@@ -103,6 +103,79 @@ def cpu_baseline(batch, work, min_seconds=10.0):
                        f"exp single-threaded); host os.cpu_count()={os.cpu_count()}")
 
 
+def bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt):
+    """Time pmattn_kv_append: this step's K/V rows written into their pool slots.
+    Algorithmic bytes: the new rows read once and written once (2 x R x Hkv x d
+    x 2 tensors x element size)."""
+    import ctypes
+
+    import torch
+    rng = np.random.Generator(np.random.PCG64(1000 + args.config))
+    shape = (b.num_rows, b.num_kv_heads, b.head_dim)
+    kn_h = rng.standard_normal(shape).astype(np.float32)
+    vn_h = rng.standard_normal(shape).astype(np.float32)
+    if b.dtype == "bf16":
+        import workloads as wl
+        kn_h, vn_h = wl.f32_to_bf16_bits(kn_h), wl.f32_to_bf16_bits(vn_h)
+    kn, vn = conv(kn_h).to(dev), conv(vn_h).to(dev)
+    t = time.perf_counter()
+    p = make_plan()
+    plan_us = (time.perf_counter() - t) * 1e6
+    stream = torch.cuda.current_stream(dev)
+    ws = pm.kv_append(p, kn, vn, bt, kp, vp, None, stream)
+    lib = pm._lib.load()
+    vptr = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+    c_args = (p.handle, vptr(kn), vptr(vn), vptr(bt), vptr(kp), vptr(vp), vptr(ws), ws.numel(),
+              ctypes.c_void_p(int(stream.cuda_stream)))
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+    for _ in range(args.warmup):
+        torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+        if lib.pmattn_kv_append(*c_args):
+            raise RuntimeError(lib.pmattn_last_error().decode())
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        if not args.no_flush:
+            torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+        evs[k][0].record(stream)
+        st = lib.pmattn_kv_append(*c_args)
+        evs[k][1].record(stream)
+        if st:
+            raise RuntimeError(lib.pmattn_last_error().decode())
+    torch.cuda.synchronize()
+    ms = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    nbytes = 2 * 2 * b.num_rows * b.num_kv_heads * b.head_dim * b.elem_bytes
+    value = nbytes / (ms * 1e-3) / 1e9
+    units = p.tables()["append_units"].shape[0]
+    log(f"[bench] append: {units} units, {nbytes} B; {ms * 1e3:.2f} us per append; {value:.1f} GB/s "
+        f"= {100 * value / HBM_PEAK_GBS:.1f}% of hbm peak")
+    res = dict(metric="KV append GB/s (% HBM roofline), paged pool", value=value, unit="GB/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=ms, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype=b.dtype, data="synthetic",
+               config=dict(workload=b.name + "+kv-append", query_rows=b.num_rows, kv_heads=b.num_kv_heads,
+                           head_dim=b.head_dim, append_units=int(units), algorithmic_bytes=nbytes,
+                           cache_flush_between_steps=not args.no_flush),
+               roofline=dict(bound="hbm", achieved=value, peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=value / HBM_PEAK_GBS, traffic=None),
+               plan_host_us=plan_us)
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(b.num_rows, 256)
+        sub = b.replace(q_len=np.minimum(b.q_len, np.maximum(0, n - np.concatenate(
+            [[0], np.cumsum(b.q_len)[:-1]]))).astype(np.int32))
+        r = int(sub.q_len.sum())
+        t0 = time.perf_counter()
+        oracle.append_kv(sub, kn_h[:r], vn_h[:r])
+        dt = time.perf_counter() - t0
+        sb = 2 * 2 * r * b.num_kv_heads * b.head_dim * b.elem_bytes
+        res["cpu_baseline"] = dict(value=sb / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                                   sample=f"first {r} query rows of the batch, one run of {dt:.2f} s, "
+                                          "pure-Python slot writes (single thread)")
+        log(f"[bench] cpu baseline {res['cpu_baseline']['value']:.4f} GB/s")
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +186,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--num-kv-splits", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
+    ap.add_argument("--op", choices=("attention", "append"), default="attention",
+                    help="attention: pmattn_forward (default); append: pmattn_kv_append of the "
+                         "batch's query rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -165,6 +241,9 @@ def main():
                        num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
                        scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus,
                        tree_parent=b.tree_parent)
+
+    if args.op == "append":
+        return bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt)
 
     plan_times = []
     for _ in range(20):

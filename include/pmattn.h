@@ -155,6 +155,18 @@ typedef struct pmattn_merge_row {
   int32_t q_head;
 } pmattn_merge_row;
 
+/* One unit of the KV append (pmattn_kv_append): query tokens
+ * [row_begin, row_begin + n_tok) of sequence `seq` land in slots
+ * slot_begin .. slot_begin + n_tok - 1 of the sequence's logical block
+ * `block_index` (physical id block_table[seq][block_index]); n_tok <= 16. */
+typedef struct pmattn_append_unit {
+  int32_t seq;
+  int32_t row_begin;
+  int32_t n_tok;
+  int32_t block_index;
+  int32_t slot_begin;
+} pmattn_append_unit;
+
 /* Read-only views of a plan's canonical tables (owned by the plan, valid
  * until pmattn_plan_destroy). */
 typedef struct pmattn_plan_tables {
@@ -179,6 +191,8 @@ typedef struct pmattn_plan_tables {
    * (as far as the tree is concerned; d >= 64 and keys below q_start always
    * are). Rows of causal sequences hold all ones. */
   const uint64_t* row_tree_mask;
+  int32_t num_append_units;
+  const pmattn_append_unit* append_units;  /* [num_append_units], sequence order */
 } pmattn_plan_tables;
 
 /* Build a plan on the host. Validates the batch (see pmattn_plan_desc),
@@ -251,6 +265,26 @@ pmattn_status pmattn_forward_merge(pmattn_plan_t plan, void* out, float* lse, vo
 pmattn_status pmattn_merge_lse(int32_t num_parts, int32_t num_rows, int32_t num_heads,
                                int32_t head_dim, const float* part_o, const float* part_lse,
                                void* out, int32_t out_dtype, float* lse, void* stream);
+
+/* Write this step's keys and values into their pool slots: the step before
+ * attention (XY-Serve review, "Core claim" and Figure 7: new tokens' K/V go
+ * into paged blocks named by the block table; PagedAttention by title).
+ * Query row r of sequence s, at position pos = q_start[s] + r, goes to slot
+ * pos % 16 of physical block block_table[s][pos / 16], for every kv head:
+ * k_pool[blk][h][c / x][pos % 16][c % x] = k_new[row][h][c] and
+ * v_pool[blk][h][c][pos % 16] = v_new[row][h][c] (layouts above).
+ * Device pointers (caller-owned): k_new, v_new [R][Hkv][d] of the plan's
+ * element type; block_table_dev as for pmattn_forward; k_pool, v_pool are
+ * written in place (only the slots of this step's rows); workspace as for
+ * pmattn_forward (the work units travel in it). Asynchronous on `stream`.
+ * A slot written here must belong to its sequence alone: if another sequence
+ * of the plan can see it, or two rows write it, the call fails with
+ * PMATTN_E_INVALID (copy such blocks first: copy-on-write). Errors:
+ * PMATTN_E_INVALID (null pointer, shared target slot), PMATTN_E_WORKSPACE,
+ * PMATTN_E_HIP. */
+pmattn_status pmattn_kv_append(pmattn_plan_t plan, const void* k_new, const void* v_new,
+                               const int32_t* block_table_dev, void* k_pool, void* v_pool,
+                               void* workspace, size_t ws_bytes, void* stream);
 
 /* Thread-local message describing the last failure on this thread ("" if none). */
 const char* pmattn_last_error(void);

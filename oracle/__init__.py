@@ -11,6 +11,7 @@ Contents
                   block table, explicit causal mask, softmax, output and
                   log-sum-exp, all in float64; plus attention over a key
                   partition and the log-sum-exp merge of partitions.
+``kv_cache``      the KV append: this step's K/V written into their pool slots.
 ``plan_replica``  an independent Python statement of the planner's canonical
                   tables (row -> sequence/position, KV partitions) and the
                   coverage rule every work list must satisfy.
@@ -21,6 +22,7 @@ mpmath evaluation); none is "parity unpinned".
 """
 from .attention import (attend, attend_partitioned, decode_values, gather_kv, merge_partitions,
                         partition_bounds)
+from .kv_cache import append_kv
 
-__all__ = ["attend", "attend_partitioned", "decode_values", "gather_kv", "merge_partitions",
-           "partition_bounds"]
+__all__ = ["append_kv", "attend", "attend_partitioned", "decode_values", "gather_kv",
+           "merge_partitions", "partition_bounds"]

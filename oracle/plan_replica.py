@@ -78,6 +78,23 @@ def row_tree_masks(q_len, tree_parent):
     return np.array(masks, dtype=np.uint64)
 
 
+def append_units(q_len, q_start):
+    """KV append units: each sequence's new tokens cut at block boundaries,
+    as (seq, first row, tokens, logical block, first slot), sequence order."""
+    out = []
+    row = 0
+    for s, (ql, qs) in enumerate(zip(q_len, q_start)):
+        ql, qs = int(ql), int(qs)
+        t = 0
+        while t < ql:
+            pos = qs + t
+            n = min(ql - t, BLOCK - pos % BLOCK)
+            out.append((s, row + t, n, pos // BLOCK, pos % BLOCK))
+            t += n
+        row += ql
+    return np.array(out, dtype=np.int32).reshape(-1, 5)
+
+
 def token_tiles(q_len, q_start, group):
     """Runs of query tokens one task holds: a sequence with q_len * G <= 64
     rows is one tile (rows class 16, 32 or 64); a longer one is cut into runs

@@ -20,7 +20,7 @@ import numpy as np
 
 from . import _lib as L
 
-__all__ = ["Plan", "PmattnError", "plan", "forward", "forward_tasks", "forward_merge", "merge_lse",
+__all__ = ["Plan", "PmattnError", "plan", "forward", "forward_tasks", "forward_merge", "merge_lse", "kv_append",
            "version", "BF16", "F32"]
 
 BF16, F32 = L.BF16, L.F32
@@ -103,7 +103,10 @@ class Plan:
             class_begin=arr(t.class_begin, t.num_classes + 1), merge_rows=merge,
             num_part_records=int(t.num_part_records),
             row_tree_mask=(np.ctypeslib.as_array(t.row_tree_mask, shape=(t.num_rows,)).copy()
-                           if t.row_tree_mask and t.num_rows else None))
+                           if t.row_tree_mask and t.num_rows else None),
+            append_units=(np.ctypeslib.as_array(ctypes.cast(t.append_units, ctypes.POINTER(ctypes.c_int32)),
+                                                shape=(t.num_append_units * 5,)).reshape(-1, 5).copy()
+                          if t.num_append_units else np.zeros((0, 5), np.int32)))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the work list into ``workspace``."""
@@ -177,7 +180,7 @@ def _elem_dtype(code):
     return torch.bfloat16 if code == BF16 else torch.float32
 
 
-def _forward_args(p: Plan, q, k_pool, v_pool, block_table, out, lse, workspace):
+def _forward_args(p: Plan, q, k_pool, v_pool, block_table, out, lse, workspace, stream):
     torch = _torch()
     s = p.shape
     et = _elem_dtype(s["dtype"])
@@ -196,12 +199,23 @@ def _forward_args(p: Plan, q, k_pool, v_pool, block_table, out, lse, workspace):
             raise ValueError(f"{name} has {t.numel()} elements, expected {'' if exact else '>= '}{n}")
         if t.data_ptr() % 16:
             raise ValueError(f"{name} must be 16-byte aligned")
-    if workspace is None:
-        workspace = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=q.device)
+    return _workspace(p, workspace, q, stream)
+
+
+def _workspace(p: Plan, workspace, like, stream):
+    """The caller's workspace (checked), or a fresh one with the plan uploaded:
+    memory just taken from the allocator may have held anything, including an
+    earlier copy of this plan's tables at the same address."""
+    torch = _torch()
+    fresh = workspace is None
+    if fresh:
+        workspace = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=like.device)
     _need_dev(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < p.workspace_bytes:
         raise ValueError(f"workspace has {ws_bytes} bytes, plan needs {p.workspace_bytes}")
+    if fresh:
+        p.upload(workspace, stream)
     return workspace, ws_bytes
 
 
@@ -214,7 +228,7 @@ def forward(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=No
     ``[blocks][Hkv][d/x][16][x]`` (x = 16 bytes / element size); v_pool ``[blocks][Hkv][d][16]`` (element type of
     the plan); block_table int32 ``[B][stride]``; lse float32 ``[R][Hq]`` or
     None; workspace: a uint8 tensor of at least ``p.workspace_bytes``."""
-    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace)
+    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace, stream)
     _check(L.load().pmattn_forward(p.handle, _vp(q), _vp(k_pool), _vp(v_pool), _vp(block_table),
                                    _vp(out), _vp(lse), _vp(workspace), ws_bytes,
                                    _stream_ptr(stream, q)))
@@ -224,10 +238,38 @@ def forward(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=No
 def forward_tasks(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=None,
                   stream=None):
     """``pmattn_forward_tasks``: pass 1 of :func:`forward` (the tile tasks)."""
-    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace)
+    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace, stream)
     _check(L.load().pmattn_forward_tasks(p.handle, _vp(q), _vp(k_pool), _vp(v_pool),
                                          _vp(block_table), _vp(out), _vp(lse), _vp(workspace),
                                          ws_bytes, _stream_ptr(stream, q)))
+    return workspace
+
+
+def kv_append(p: Plan, k_new, v_new, block_table, k_pool, v_pool, workspace=None, stream=None):
+    """``pmattn_kv_append``: write this step's K/V rows (``k_new``, ``v_new``
+    ``[R][Hkv][d]``, the plan's element type) into their pool slots, in place."""
+    torch = _torch()
+    s = p.shape
+    et = _elem_dtype(s["dtype"])
+    r, hkv, d = s["num_rows"], s["hkv"], s["d"]
+    pool_elems = s["num_pool_blocks"] * hkv * 16 * d
+    for t, name, dt, n, exact in ((k_new, "k_new", et, r * hkv * d, True),
+                                  (v_new, "v_new", et, r * hkv * d, True),
+                                  (k_pool, "k_pool", et, pool_elems, False),
+                                  (v_pool, "v_pool", et, pool_elems, False),
+                                  (block_table, "block_table", torch.int32,
+                                   s["num_seqs"] * s["bt_stride"], True)):
+        _need_dev(t, name)
+        if t.dtype != dt:
+            raise ValueError(f"{name} must have dtype {dt}, got {t.dtype}")
+        if (t.numel() != n) if exact else (t.numel() < n):
+            raise ValueError(f"{name} has {t.numel()} elements, expected {'' if exact else '>= '}{n}")
+        if t.data_ptr() % 16:
+            raise ValueError(f"{name} must be 16-byte aligned")
+    workspace, ws_bytes = _workspace(p, workspace, k_pool, stream)
+    _check(L.load().pmattn_kv_append(p.handle, _vp(k_new), _vp(v_new), _vp(block_table),
+                                     _vp(k_pool), _vp(v_pool), _vp(workspace), ws_bytes,
+                                     _stream_ptr(stream, k_pool)))
     return workspace
 
 

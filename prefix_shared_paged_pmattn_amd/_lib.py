@@ -63,6 +63,8 @@ class PlanTables(ctypes.Structure):
         ("merge_rows", ctypes.POINTER(MergeRow)),
         ("num_part_records", ctypes.c_int32),
         ("row_tree_mask", ctypes.POINTER(ctypes.c_uint64)),
+        ("num_append_units", ctypes.c_int32),
+        ("append_units", ctypes.c_void_p),
     ]
 
 
@@ -88,6 +90,9 @@ SIGNATURES = [
                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    ("pmattn_kv_append", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     ("pmattn_last_error", ctypes.c_char_p, []),
     ("pmattn_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("pmattn_version", ctypes.c_char_p, []),

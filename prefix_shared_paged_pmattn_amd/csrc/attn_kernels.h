@@ -44,10 +44,23 @@ struct MergeArgs {
   int32_t implicit_rows;         // implicit layout: rows
 };
 
+struct AppendArgs {
+  const void* k_new;               // [R][Hkv][d]
+  const void* v_new;               // [R][Hkv][d]
+  const int32_t* block_table;
+  void* k_pool;
+  void* v_pool;
+  const pmattn_append_unit* units;
+  int32_t unit_count;
+  int32_t bt_stride;
+  int32_t hkv;
+};
+
 // Host launchers (forward.hip).
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
+hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st);
 
 }  // namespace pmattn

@@ -71,6 +71,17 @@ pmattn_status pmattn_plan_upload(pmattn_plan_t plan, void* workspace, size_t ws_
   return upload(plan->p, workspace, static_cast<hipStream_t>(stream));
 }
 
+// Upload the plan's tables into `workspace` unless this plan put them there last.
+static pmattn_status ensure_uploaded(const Plan& P, void* workspace, hipStream_t st) {
+  bool need_upload;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws_owner.find(workspace);
+    need_upload = it == g_ws_owner.end() || it->second != P.id;
+  }
+  return need_upload ? upload(P, workspace, st) : PMATTN_OK;
+}
+
 static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
                                const void* v_pool, const int32_t* block_table_dev, void* out,
                                float* lse, void* workspace, size_t ws_bytes, void* stream) {
@@ -81,14 +92,8 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     return fail(PMATTN_E_INVALID, "q, k_pool, v_pool, block_table, out and workspace must be non-NULL");
   if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  bool need_upload;
   {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    auto it = g_ws_owner.find(workspace);
-    need_upload = it == g_ws_owner.end() || it->second != P.id;
-  }
-  if (need_upload) {
-    pmattn_status s = upload(P, workspace, st);
+    pmattn_status s = ensure_uploaded(P, workspace, st);
     if (s != PMATTN_OK) return s;
   }
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -194,6 +199,35 @@ pmattn_status pmattn_forward_merge(pmattn_plan_t plan, void* out, float* lse, vo
                                    size_t ws_bytes, void* stream) {
   clear_error();
   return run_merge(plan, out, lse, workspace, ws_bytes, stream);
+}
+
+pmattn_status pmattn_kv_append(pmattn_plan_t plan, const void* k_new, const void* v_new,
+                               const int32_t* block_table_dev, void* k_pool, void* v_pool,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!plan) return fail(PMATTN_E_INVALID, "plan is NULL");
+  const Plan& P = plan->p;
+  if (!P.append_conflict.empty()) return fail(PMATTN_E_INVALID, P.append_conflict);
+  if (P.append_units.empty()) return PMATTN_OK;
+  if (!k_new || !v_new || !block_table_dev || !k_pool || !v_pool || !workspace)
+    return fail(PMATTN_E_INVALID, "k_new, v_new, block_table, k_pool, v_pool and workspace must be non-NULL");
+  if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  pmattn_status s = ensure_uploaded(P, workspace, st);
+  if (s != PMATTN_OK) return s;
+  AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_table = block_table_dev;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.units = reinterpret_cast<const pmattn_append_unit*>(static_cast<unsigned char*>(workspace) + P.off_append);
+  a.unit_count = (int32_t)P.append_units.size();
+  a.bt_stride = P.bt_stride;
+  a.hkv = P.hkv;
+  hipError_t e = launch_kv_append(P.head_dim, P.dtype, a, st);
+  if (e != hipSuccess) return hip_fail(e, "kv append kernel launch");
+  return PMATTN_OK;
 }
 
 pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_pool,

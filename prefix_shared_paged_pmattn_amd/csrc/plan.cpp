@@ -180,6 +180,59 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     }
   }
 
+  // ---- KV append units and their copy-on-write check ------------------------
+  // A unit is the run of a sequence's new tokens that falls into one block.
+  // Every slot written must be visible to its own sequence alone.
+  {
+    struct Target {
+      int32_t blk, seq;
+      uint32_t slots;  // bit o: slot o is written
+    };
+    std::vector<Target> targets;
+    int64_t r0 = 0;
+    for (int s = 0; s < B; ++s) {
+      const int ql = d->q_len[s], qs = d->q_start[s];
+      const int32_t* bt = d->block_table + (int64_t)s * d->bt_stride;
+      for (int t = 0; t < ql;) {
+        const int pos = qs + t, j = pos / kBlock, o = pos % kBlock;
+        const int n = std::min(ql - t, kBlock - o);
+        P.append_units.push_back(pmattn_append_unit{s, (int32_t)(r0 + t), n, j, o});
+        targets.push_back(Target{bt[j], s, ((1u << n) - 1u) << o});
+        t += n;
+      }
+      r0 += ql;
+    }
+    std::sort(targets.begin(), targets.end(),
+              [](const Target& a, const Target& b) { return a.blk < b.blk; });
+    std::vector<uint64_t> filter(1024, 0);  // 65536-bit filter on the low id bits
+    for (const Target& x : targets) filter[(x.blk & 0xFFFF) >> 6] |= 1ull << (x.blk & 63);
+    for (size_t i = 1; i < targets.size() && P.append_conflict.empty(); ++i)
+      if (targets[i].blk == targets[i - 1].blk && (targets[i].slots & targets[i - 1].slots))
+        P.append_conflict = "two query rows write the same pool slot (block " +
+                            std::to_string(targets[i].blk) + ")";
+    for (int s = 0; s < B && P.append_conflict.empty() && !targets.empty(); ++s) {
+      const int64_t kv = (int64_t)d->q_start[s] + d->q_len[s];
+      if (d->q_len[s] == 0) continue;
+      const int32_t* bt = d->block_table + (int64_t)s * d->bt_stride;
+      const int64_t nb = (kv + kBlock - 1) / kBlock;
+      for (int64_t j = 0; j < nb; ++j) {
+        const int32_t blk = bt[j];
+        if (!(filter[(blk & 0xFFFF) >> 6] >> (blk & 63) & 1ull)) continue;
+        const uint32_t seen = j + 1 < nb ? 0xFFFFu : (1u << (kv - j * kBlock)) - 1u;
+        auto it = std::lower_bound(targets.begin(), targets.end(), blk,
+                                   [](const Target& a, int32_t b) { return a.blk < b; });
+        for (; it != targets.end() && it->blk == blk; ++it)
+          if (it->seq != s && (it->slots & seen)) {
+            P.append_conflict = "sequence " + std::to_string(s) + " can see pool slots that sequence " +
+                                std::to_string(it->seq) + " appends to (block " +
+                                std::to_string(blk) + "): copy the block first";
+            break;
+          }
+        if (!P.append_conflict.empty()) break;
+      }
+    }
+  }
+
   // ---- tiles: runs of query tokens whose G heads fit one task --------------
   // A sequence whose rows fit one wave task (q_len * G <= 64) is one tile;
   // longer ones are cut into runs of 128/G tokens for the workgroup kernel.
@@ -310,7 +363,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.off_items = 0;
   P.off_merge = align_up(P.off_items + P.items.size() * sizeof(pmattn_work_item), kAlign);
   P.off_row_mask = align_up(P.off_merge + P.merge_rows.size() * sizeof(pmattn_merge_row), kAlign);
-  P.off_part_o = align_up(P.off_row_mask + P.row_mask.size() * sizeof(uint64_t), kAlign);
+  P.off_append = align_up(P.off_row_mask + P.row_mask.size() * sizeof(uint64_t), kAlign);
+  P.off_part_o = align_up(P.off_append + P.append_units.size() * sizeof(pmattn_append_unit), kAlign);
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
   P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
   P.upload_blob.assign(P.off_part_o, 0);
@@ -323,6 +377,9 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (!P.row_mask.empty())
     std::memcpy(P.upload_blob.data() + P.off_row_mask, P.row_mask.data(),
                 P.row_mask.size() * sizeof(uint64_t));
+  if (!P.append_units.empty())
+    std::memcpy(P.upload_blob.data() + P.off_append, P.append_units.data(),
+                P.append_units.size() * sizeof(pmattn_append_unit));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -383,6 +440,8 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->merge_rows = P.merge_rows.data();
   t->num_part_records = P.num_records;
   t->row_tree_mask = P.row_mask.empty() ? nullptr : P.row_mask.data();
+  t->num_append_units = (int32_t)P.append_units.size();
+  t->append_units = P.append_units.data();
   return PMATTN_OK;
 }
 

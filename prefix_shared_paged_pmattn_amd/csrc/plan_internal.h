@@ -42,9 +42,14 @@ struct Plan {
   int32_t num_records = 0;
   // tree masks, one per row, present only when some sequence is a tree
   std::vector<uint64_t> row_mask;
-  // workspace layout (bytes): [items | merge rows | row masks | partial O | partial lse]
-  size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_part_o = 0, off_part_lse = 0,
-         ws_bytes = 0;
+  // KV append units; a non-empty message marks a target slot that another
+  // sequence can see (or two rows write): the append refuses such a plan
+  std::vector<pmattn_append_unit> append_units;
+  std::string append_conflict;
+  // workspace layout (bytes):
+  // [items | merge rows | row masks | append units | partial O | partial lse]
+  size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_part_o = 0,
+         off_part_lse = 0, ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 

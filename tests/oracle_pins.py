@@ -449,6 +449,41 @@ def pin_split_merge(mod):
     assert np.allclose(mo, ref_o, rtol=0, atol=1e-13)
 
 
+def pin_append(append_kv, gather_kv):
+    """The KV append stores each new row so that gathering its position gives it
+    back (the gather is pinned by the attention pins), leaves every other pool
+    element unchanged, and agrees with the token-major view of the K blocks."""
+    for dtype, d in (("bf16", 16), ("f32", 8), ("bf16", 24)):
+        b = wl.custom([dict(q_len=5, seq_len=40, q_start=14), dict(q_len=1, seq_len=17),
+                       dict(q_len=20, seq_len=36, q_start=16), dict(q_len=0, seq_len=9)],
+                      hq=4, hkv=2, d=d, dtype=dtype, seed=51, extra_blocks=2)
+        rng = np.random.Generator(np.random.PCG64(52))
+        new_k = _store(b, rng.standard_normal((b.num_rows, 2, d)))
+        new_v = _store(b, rng.standard_normal((b.num_rows, 2, d)))
+        kp, vp = append_kv(b, new_k, new_v)
+        changed_k = np.zeros(kp.shape, bool)
+        changed_v = np.zeros(vp.shape, bool)
+        k_tok = wl.k_token_major(kp)
+        off = b.row_offsets()
+        for s in range(b.num_seqs):
+            n = int(b.q_start[s] + b.q_len[s])
+            for g in range(2):
+                kk, vv = gather_kv(kp, vp, b.block_table[s], g, n, dtype)
+                for r in range(int(b.q_len[s])):
+                    pos = int(b.q_start[s]) + r
+                    row = off[s] + r
+                    assert np.array_equal(kk[pos], _vals(b, new_k[row, g])), (dtype, s, r)
+                    assert np.array_equal(vv[pos], _vals(b, new_v[row, g])), (dtype, s, r)
+                    blk, slot = b.block_table[s, pos // 16], pos % 16
+                    assert np.array_equal(k_tok[blk, g, slot], new_k[row, g])
+                    changed_v[blk, g, :, slot] = True
+                    x = kp.shape[-1]
+                    changed_k[blk, g, :, slot, :] = True
+                    assert x == wl.k_group(d, dtype)
+        assert np.array_equal(kp[~changed_k], b.k_pool[~changed_k])
+        assert np.array_equal(vp[~changed_v], b.v_pool[~changed_v])
+
+
 ALL_PINS = [pin_single_key, pin_equal_scores, pin_two_keys, pin_golden, pin_brute_force_sdpa,
             pin_mpmath, pin_shared_equals_private, pin_class_independence, pin_gqa_replication,
             pin_convexity, pin_tree_linearization]

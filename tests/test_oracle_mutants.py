@@ -70,3 +70,26 @@ def test_unmutated_copy_passes():
     for pin in P.ALL_PINS:
         pin(mod.attend)
     P.pin_split_merge(mod)
+
+
+SRC_KV = os.path.join(ROOT, "oracle", "kv_cache.py")
+KV_MUTANTS = {
+    "append-slot-off-by-one": ("slot = pos % BLOCK", "slot = (pos + 1) % BLOCK"),
+    "append-block-from-row": ("blk = int(b.block_table[s, pos // BLOCK])", "blk = int(b.block_table[s, r // BLOCK])"),
+    "append-k-token-major": ("k_pool[blk, h, c // x, slot, c % x] = k_new[row, h, c]",
+                             "k_pool.reshape(k_pool.shape[0], k_pool.shape[1], BLOCK, -1)[blk, h, slot, c] = k_new[row, h, c]"),
+    "append-v-heads-swapped": ("v_pool[blk, h, c, slot] = v_new[row, h, c]",
+                               "v_pool[blk, h, c, slot] = v_new[row, b.num_kv_heads - 1 - h, c]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(KV_MUTANTS))
+def test_append_mutant_is_caught(name):
+    import oracle
+    old, new = KV_MUTANTS[name]
+    src = open(SRC_KV).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {name}"
+    mod = types.ModuleType(f"oracle_kv_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    with pytest.raises(Exception):     # noqa: B017 - any failure counts as caught
+        P.pin_append(mod.append_kv, oracle.gather_kv)

@@ -65,3 +65,7 @@ def test_rows_subset_matches_full():
     rows = [11, 0, 6, 8]
     o2, l2 = oracle.attend(b, rows=rows)
     assert np.allclose(o2, o[rows], rtol=0, atol=1e-15) and np.allclose(l2, l[rows], rtol=0, atol=1e-15)
+
+
+def test_kv_append_pins():
+    P.pin_append(oracle.append_kv, oracle.gather_kv)

@@ -228,6 +228,49 @@ def test_tree_errors():
         pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, tree_parent=ok[:-1], **kw)
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
+def test_append_units_match_replica(cfg):
+    b = wl.config(cfg, values=False)
+    t = make_plan(b).tables()
+    want = R.append_units(b.q_len, b.q_start)
+    assert np.array_equal(t["append_units"], want)
+    # the units cover every query row exactly once, within one block each
+    assert int(want[:, 2].sum()) == b.num_rows and (want[:, 2] + want[:, 4] <= 16).all()
+
+
+def _append_status(p):
+    """pmattn_kv_append's verdict on a plan, with every pointer NULL: a plan that
+    writes shared slots is refused before anything else is looked at."""
+    lib = _lib.load()
+    st = lib.pmattn_kv_append(p.handle, None, None, None, None, None, None, 0, None)
+    return st, lib.pmattn_last_error().decode()
+
+
+def test_append_refuses_shared_target_slots():
+    # two sequences share block "a" (their first 16 tokens)
+    b = wl.custom([dict(q_len=1, seq_len=20, nodes=["a"]), dict(q_len=1, seq_len=30, nodes=["a"])],
+                  node_blocks={"a": 1}, hq=4, hkv=2, d=64, values=False)
+    st, msg = _append_status(make_plan(b))
+    assert st == _lib.E_INVALID and "non-NULL" in msg          # private targets: only NULLs are wrong
+    # sequence 0 appends at position 10, inside the shared block that sequence 1 sees whole
+    b2 = b.replace(q_start=np.array([10, 29], np.int32), seq_len=np.array([11, 30], np.int32))
+    st, msg = _append_status(make_plan(b2))
+    assert st == _lib.E_INVALID and "copy the block first" in msg
+    # sequence 1 appends at position 7 of the shared block, which sequence 0 sees
+    b3 = b.replace(q_start=np.array([10, 7], np.int32), seq_len=np.array([11, 8], np.int32))
+    st, msg = _append_status(make_plan(b3))
+    assert st == _lib.E_INVALID and "copy the block first" in msg
+    # a sharer without query rows reads nothing, so the append is allowed
+    b4 = b.replace(q_start=np.array([10, 3], np.int32), seq_len=np.array([11, 4], np.int32),
+                   q_len=np.array([1, 0], np.int32))
+    st, msg = _append_status(make_plan(b4))
+    assert "non-NULL" in msg
+    # two rows writing one slot
+    b5 = b.replace(q_start=np.array([5, 5], np.int32), seq_len=np.array([6, 6], np.int32))
+    st, msg = _append_status(make_plan(b5))
+    assert st == _lib.E_INVALID and "same pool slot" in msg
+
+
 def test_unused_table_entries_are_not_validated():
     # entries past the visible blocks may be anything (here -1); rows of length 0 read nothing
     b = wl.custom([dict(q_len=1, seq_len=20, q_start=5), dict(q_len=0, seq_len=33)], hq=2, hkv=1,
