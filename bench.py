@@ -103,6 +103,47 @@ def cpu_baseline(batch, work, min_seconds=10.0):
                        f"exp single-threaded); host os.cpu_count()={os.cpu_count()}")
 
 
+def bench_radix(args):
+    """Host cost of the radix cache manager on a workload's requests. Token ids
+    follow the block sharing of the batch: blocks shared between sequences get
+    the same ids, so cached prefixes match exactly where the workload shares.
+    Each timed round admits every request, publishes it, and releases it."""
+    import workloads as wl
+    from prefix_shared_paged_pmattn_amd.radix import RadixCache
+    b = wl.config(args.config, values=False)
+    reqs = []
+    for s in range(b.num_seqs):
+        n = int(b.seq_len[s])
+        blocks = b.block_table[s, :(n + 15) // 16]
+        toks = (np.repeat(blocks.astype(np.int64), 16)[:n] * 16 + np.arange(n) % 16) % (1 << 30)
+        reqs.append(toks.astype(np.int32))
+    need = sum((len(t) + 15) // 16 for t in reqs)
+    times, cached = [], 0
+    for rnd in range(args.warmup + args.steps):
+        cache = RadixCache(need + 16)
+        t0 = time.perf_counter()
+        ids = []
+        for t in reqs:
+            sid, cl, _, _ = cache.admit(t)
+            cache.publish(sid)
+            ids.append(sid)
+            if rnd == 0:
+                cached += cl
+        for sid in ids:
+            cache.release(sid)
+        if rnd >= args.warmup:
+            times.append(time.perf_counter() - t0)
+    us = statistics.median(times) / len(reqs) * 1e6
+    tok = sum(len(t) for t in reqs)
+    log(f"[bench] radix: {len(reqs)} requests, {tok} tokens, {cached} reused; {us:.1f} us per request "
+        f"(admit + publish + release, binding overhead included)")
+    print(json.dumps(dict(metric="radix cache us per request (host)", value=us, unit="us/request", n_gpus=0,
+                          steps=args.steps, warmup=args.warmup, higher_is_better=False, dtype="int32",
+                          data="synthetic", config=dict(workload=b.name + "+radix", requests=len(reqs),
+                                                        tokens=tok, reused_tokens=cached),
+                          host_cores=1)), flush=True)
+
+
 def bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt):
     """Time pmattn_kv_append: this step's K/V rows written into their pool slots.
     Algorithmic bytes: the new rows read once and written once (2 x R x Hkv x d
@@ -186,9 +227,10 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--num-kv-splits", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
-    ap.add_argument("--op", choices=("attention", "append"), default="attention",
+    ap.add_argument("--op", choices=("attention", "append", "radix"), default="attention",
                     help="attention: pmattn_forward (default); append: pmattn_kv_append of the "
-                         "batch's query rows")
+                         "batch's query rows; radix: host radix-cache admit/publish/release of "
+                         "the batch's requests (no GPU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -196,6 +238,9 @@ def main():
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is a design note only)", file=sys.stderr)
         sys.exit(2)
+
+    if args.op == "radix":
+        return bench_radix(args)
 
     import torch
     import prefix_shared_paged_pmattn_amd as pm

@@ -72,7 +72,8 @@ typedef enum pmattn_status {
   PMATTN_E_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, block size, dtype) */
   PMATTN_E_WORKSPACE = 3,    /* workspace too small */
   PMATTN_E_HIP = 4,          /* a HIP runtime call failed; see pmattn_last_error() */
-  PMATTN_E_NOMEM = 5         /* host allocation failed */
+  PMATTN_E_NOMEM = 5,        /* host allocation failed */
+  PMATTN_E_CAPACITY = 6      /* the block pool is exhausted (pmattn_radix.h) */
 } pmattn_status;
 
 typedef enum pmattn_dtype { PMATTN_BF16 = 0, PMATTN_F32 = 1 } pmattn_dtype;

@@ -7,7 +7,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpmattn.so")
 
-OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_NOMEM = range(6)
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP, E_NOMEM, E_CAPACITY = range(7)
 BF16, F32 = 0, 1
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -69,6 +69,16 @@ class PlanTables(ctypes.Structure):
 
 
 # (name, restype, argtypes) for every function the header declares.
+class BlockCopy(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("src", "dst", "slots")]
+
+
+class RadixStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("free_blocks", ctypes.c_int32),
+                ("tree_nodes", ctypes.c_int32), ("tree_tokens", ctypes.c_int32),
+                ("live_seqs", ctypes.c_int32), ("evicted_nodes", ctypes.c_int64)]
+
+
 SIGNATURES = [
     ("pmattn_plan", ctypes.c_int, [ctypes.POINTER(PlanDesc), ctypes.POINTER(ctypes.c_void_p)]),
     ("pmattn_plan_destroy", None, [ctypes.c_void_p]),
@@ -93,6 +103,24 @@ SIGNATURES = [
     ("pmattn_kv_append", ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("pmattn_radix_create", ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]),
+    ("pmattn_radix_destroy", None, [ctypes.c_void_p]),
+    ("pmattn_radix_admit", ctypes.c_int, [ctypes.c_void_p, _i32p, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                          _i32p, ctypes.c_int32, ctypes.POINTER(BlockCopy),
+                                          ctypes.POINTER(ctypes.c_int32)]),
+    ("pmattn_radix_extend", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p, ctypes.c_int32,
+                                           _i32p, ctypes.c_int32]),
+    ("pmattn_radix_publish", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("pmattn_radix_release", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("pmattn_radix_match", ctypes.c_int, [ctypes.c_void_p, _i32p, ctypes.c_int32,
+                                          ctypes.POINTER(ctypes.c_int32)]),
+    ("pmattn_radix_stats_get", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(RadixStats)]),
+    ("pmattn_radix_block_refs", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_int32)]),
+    ("pmattn_copy_blocks", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_void_p]),
     ("pmattn_last_error", ctypes.c_char_p, []),
     ("pmattn_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("pmattn_version", ctypes.c_char_p, []),

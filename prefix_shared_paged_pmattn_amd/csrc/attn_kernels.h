@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "pmattn.h"
+#include "pmattn_radix.h"
 
 namespace pmattn {
 
@@ -62,5 +63,7 @@ hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
 hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st);
+hipError_t launch_copy_blocks(int head_dim, int dtype, const pmattn_block_copy* copies, int n,
+                              void* k_pool, void* v_pool, int hkv, hipStream_t st);
 
 }  // namespace pmattn

@@ -230,6 +230,21 @@ pmattn_status pmattn_kv_append(pmattn_plan_t plan, const void* k_new, const void
   return PMATTN_OK;
 }
 
+pmattn_status pmattn_copy_blocks(const pmattn_block_copy* copies_dev, int32_t num_copies,
+                                 void* k_pool, void* v_pool, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t dtype, void* stream) {
+  clear_error();
+  if (num_copies < 0 || num_kv_heads < 1) return fail(PMATTN_E_INVALID, "num_copies < 0 or num_kv_heads < 1");
+  if (head_dim != 64 && head_dim != 128) return fail(PMATTN_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (dtype != PMATTN_BF16 && dtype != PMATTN_F32) return fail(PMATTN_E_UNSUPPORTED, "unknown dtype");
+  if (num_copies == 0) return PMATTN_OK;
+  if (!copies_dev || !k_pool || !v_pool) return fail(PMATTN_E_INVALID, "NULL pointer");
+  hipError_t e = launch_copy_blocks(head_dim, dtype, copies_dev, num_copies, k_pool, v_pool, num_kv_heads,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "block copy kernel launch");
+  return PMATTN_OK;
+}
+
 pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table_dev, void* out,
                              float* lse, void* workspace, size_t ws_bytes, void* stream) {

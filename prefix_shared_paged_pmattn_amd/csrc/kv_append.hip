@@ -14,6 +14,7 @@
 //     of that channel, as 16-byte stores when the unit covers the block.
 // Pure data movement: HBM bound, 2 x (K + V) bytes of the new rows.
 #include "attn_kernels.h"
+#include "pmattn_radix.h"
 
 namespace pmattn {
 namespace {
@@ -56,7 +57,47 @@ __global__ __launch_bounds__(128) void kv_append_kernel(AppendArgs a) {
   }
 }
 
+// Copy-on-write of pool blocks: one 128-thread workgroup per (order, kv head)
+// copies slots [0, slots) of block src into block dst, K and V.
+template <typename T, int D>
+__global__ __launch_bounds__(128) void copy_blocks_kernel(const pmattn_block_copy* copies, void* k_pool,
+                                                          void* v_pool, int hkv) {
+  constexpr int X = 16 / sizeof(T), NG = D / X;
+  const cint_p cp = (cint_p)(copies + blockIdx.x);
+  const int64_t src = cp[0], dst = cp[1];
+  const int slots = cp[2];
+  const int h = blockIdx.y;
+  const int64_t so = (src * hkv + h) * (int64_t)(16 * D), dso = (dst * hkv + h) * (int64_t)(16 * D);
+  const T* ks = static_cast<const T*>(k_pool) + so;
+  T* kd = static_cast<T*>(k_pool) + dso;
+  for (int idx = threadIdx.x; idx < NG * slots; idx += 128) {
+    const int g = idx / slots, o = idx - g * slots;
+    *reinterpret_cast<uint4*>(kd + g * (16 * X) + o * X) =
+        *reinterpret_cast<const uint4*>(ks + g * (16 * X) + o * X);
+  }
+  const T* vs = static_cast<const T*>(v_pool) + so;
+  T* vd = static_cast<T*>(v_pool) + dso;
+  for (int idx = threadIdx.x; idx < D * slots; idx += 128) {
+    const int c = idx / slots, o = idx - c * slots;
+    vd[c * 16 + o] = vs[c * 16 + o];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(int head_dim, int dtype, const pmattn_block_copy* copies, int n,
+                              void* k_pool, void* v_pool, int hkv, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(n, hkv), block(128);
+  if (dtype == PMATTN_BF16) {
+    if (head_dim == 128) hipLaunchKernelGGL((copy_blocks_kernel<uint16_t, 128>), grid, block, 0, st, copies, k_pool, v_pool, hkv);
+    else hipLaunchKernelGGL((copy_blocks_kernel<uint16_t, 64>), grid, block, 0, st, copies, k_pool, v_pool, hkv);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((copy_blocks_kernel<float, 128>), grid, block, 0, st, copies, k_pool, v_pool, hkv);
+    else hipLaunchKernelGGL((copy_blocks_kernel<float, 64>), grid, block, 0, st, copies, k_pool, v_pool, hkv);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st) {
   if (a.unit_count <= 0) return hipSuccess;

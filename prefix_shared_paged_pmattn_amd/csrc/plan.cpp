@@ -455,6 +455,7 @@ const char* pmattn_status_str(pmattn_status s) {
     case PMATTN_E_WORKSPACE: return "PMATTN_E_WORKSPACE";
     case PMATTN_E_HIP: return "PMATTN_E_HIP";
     case PMATTN_E_NOMEM: return "PMATTN_E_NOMEM";
+    case PMATTN_E_CAPACITY: return "PMATTN_E_CAPACITY";
   }
   return "PMATTN_E_UNKNOWN";
 }

@@ -91,3 +91,21 @@ def test_append_refuses_shared_slots_on_device():
     dev = to_device(b)
     with pytest.raises(pm.PmattnError):
         pm.kv_append(make_plan(b), _conv(b, kn).cuda(), _conv(b, vn).cuda(), dev["bt"], dev["k"], dev["v"])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_copy_blocks_bit_exact(dtype, d):
+    import torch
+    from prefix_shared_paged_pmattn_amd.radix import copy_blocks
+    b = wl.custom([S(q_len=1, seq_len=16 * 9)], hq=4, hkv=2, d=d, dtype=dtype, seed=4)
+    dev = to_device(b)
+    copies = [(0, 5, 7), (3, 1, 16), (8, 2, 1), (6, 7, 13)]
+    copy_blocks(copies, dev["k"], dev["v"], b.num_kv_heads, d, dtype)
+    torch.cuda.synchronize()
+    kt = wl.k_token_major(b.k_pool)
+    want_k, want_v = kt.copy(), b.v_pool.copy()
+    for src, dst, slots in copies:
+        want_k[dst, :, :slots, :] = kt[src, :, :slots, :]
+        want_v[dst, :, :, :slots] = b.v_pool[src, :, :, :slots]
+    assert np.array_equal(_back(b, dev["k"]), wl.k_pool_layout(want_k, dtype))
+    assert np.array_equal(_back(b, dev["v"]), want_v)

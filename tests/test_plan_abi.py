@@ -291,10 +291,13 @@ def test_empty_batch():
 
 
 def test_library_exports_every_declared_symbol():
-    header = open(os.path.join(ROOT, "include", "pmattn.h")).read()
-    declared = set(re.findall(r"\b(pmattn_[a-z_]+)\s*\(", header))
+    import glob
+    declared = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        declared |= set(re.findall(r"\b(pmattn_[a-z_]+)\s*\(", open(h).read()))
     declared -= {"pmattn_plan_s"}
-    assert {"pmattn_plan", "pmattn_forward", "pmattn_merge_lse"} <= declared
+    assert {"pmattn_plan", "pmattn_forward", "pmattn_merge_lse", "pmattn_kv_append",
+            "pmattn_radix_admit", "pmattn_copy_blocks"} <= declared
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in sorted(declared):
         assert hasattr(lib, name), name
