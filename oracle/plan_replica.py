@@ -95,6 +95,35 @@ def append_units(q_len, q_start):
     return np.array(out, dtype=np.int32).reshape(-1, 5)
 
 
+def build_batch(kinds, context, pending, token_budget, reserved, max_chunk):
+    """Rows each request gets in one step under the token budget (XY-Serve
+    review, Figure 6 caption: chunks stay within the budget, long prefills are
+    cut, slots are reserved for decode and speculative tokens). The reading:
+    decode (kind 1) and verify (kind 2) requests first, in order, each whole if
+    it still fits the budget; then prefill requests (kind 0), in order, share
+    min(budget - reserved, budget - rows used), each taking min(pending,
+    max_chunk, rows left); the first one cut short ends the prefills."""
+    q = [0] * len(kinds)
+    used = 0
+    for i, (k, pe) in enumerate(zip(kinds, pending)):
+        if k != 0 and used + pe <= token_budget:
+            q[i] = int(pe)
+            used += int(pe)
+    left = min(token_budget - reserved, token_budget - used)
+    for i, (k, pe) in enumerate(zip(kinds, pending)):
+        if left <= 0:
+            break
+        if k != 0 or pe == 0:
+            continue
+        want = min(int(pe), max_chunk)
+        take = min(want, left)
+        q[i] = take
+        left -= take
+        if take < want:
+            break
+    return np.array(q, dtype=np.int32)
+
+
 def token_tiles(q_len, q_start, group):
     """Runs of query tokens one task holds: a sequence with q_len * G <= 64
     rows is one tile (rows class 16, 32 or 64); a longer one is cut into runs

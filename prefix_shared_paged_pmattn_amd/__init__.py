@@ -20,7 +20,7 @@ import numpy as np
 
 from . import _lib as L
 
-__all__ = ["Plan", "PmattnError", "plan", "forward", "forward_tasks", "forward_merge", "merge_lse", "kv_append",
+__all__ = ["Plan", "PmattnError", "plan", "forward", "forward_tasks", "forward_merge", "merge_lse", "kv_append", "build_batch",
            "version", "BF16", "F32"]
 
 BF16, F32 = L.BF16, L.F32
@@ -243,6 +243,26 @@ def forward_tasks(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, worksp
                                          _vp(block_table), _vp(out), _vp(lse), _vp(workspace),
                                          ws_bytes, _stream_ptr(stream, q)))
     return workspace
+
+
+PREFILL, DECODE, VERIFY = 0, 1, 2
+
+
+def build_batch(kinds, context, pending, *, token_budget: int, reserved: int, max_chunk: int) -> np.ndarray:
+    """``pmattn_build_batch``: query rows each request gets this step (host only)."""
+    k, c, pe = _i32(kinds), _i32(context), _i32(pending)
+    n = int(k.shape[0])
+    if c.shape != (n,) or pe.shape != (n,):
+        raise ValueError("kinds, context and pending must have one entry per request")
+    reqs = (L.Request * max(n, 1))()
+    for i in range(n):
+        reqs[i] = L.Request(int(k[i]), int(c[i]), int(pe[i]))
+    q = np.zeros(max(n, 1), np.int32)
+    total = ctypes.c_int32()
+    bud = L.Budget(int(token_budget), int(reserved), int(max_chunk))
+    _check(L.load().pmattn_build_batch(reqs, n, ctypes.byref(bud), q.ctypes.data_as(L._i32p),
+                                       ctypes.byref(total)))
+    return q[:n].copy()
 
 
 def kv_append(p: Plan, k_new, v_new, block_table, k_pool, v_pool, workspace=None, stream=None):

@@ -79,6 +79,14 @@ class RadixStats(ctypes.Structure):
                 ("live_seqs", ctypes.c_int32), ("evicted_nodes", ctypes.c_int64)]
 
 
+class Request(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("kind", "context", "pending")]
+
+
+class Budget(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("token_budget", "reserved", "max_chunk")]
+
+
 SIGNATURES = [
     ("pmattn_plan", ctypes.c_int, [ctypes.POINTER(PlanDesc), ctypes.POINTER(ctypes.c_void_p)]),
     ("pmattn_plan_destroy", None, [ctypes.c_void_p]),
@@ -121,6 +129,8 @@ SIGNATURES = [
     ("pmattn_copy_blocks", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_void_p]),
+    ("pmattn_build_batch", ctypes.c_int, [ctypes.POINTER(Request), ctypes.c_int32, ctypes.POINTER(Budget),
+                                          _i32p, ctypes.POINTER(ctypes.c_int32)]),
     ("pmattn_last_error", ctypes.c_char_p, []),
     ("pmattn_status_str", ctypes.c_char_p, [ctypes.c_int]),
     ("pmattn_version", ctypes.c_char_p, []),

@@ -21,7 +21,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
 HIP_SOURCES = ["attn_bf16.hip", "attn_prefill.hip", "attn_f32_merge.hip", "kv_append.hip", "forward.hip"]
-CXX_SOURCES = ["plan.cpp", "radix.cpp"]
+CXX_SOURCES = ["plan.cpp", "radix.cpp", "batch.cpp"]
 
 HIP_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall",
