@@ -227,6 +227,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--num-kv-splits", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
+    ap.add_argument("--cascade", type=int, choices=(0, 1, 2), default=2,
+                    help="shared-prefix cascade for decode/verify rows (plan option): 0 off, "
+                         "1 every shared run, 2 automatic")
     ap.add_argument("--op", choices=("attention", "append", "radix"), default="attention",
                     help="attention: pmattn_forward (default); append: pmattn_kv_append of the "
                          "batch's query rows; radix: host radix-cache admit/publish/release of "
@@ -285,7 +288,7 @@ def main():
                        num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
                        num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
                        scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus,
-                       tree_parent=b.tree_parent)
+                       tree_parent=b.tree_parent, cascade=args.cascade)
 
     if args.op == "append":
         return bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt)
@@ -372,7 +375,7 @@ def main():
         achieved = work["bytes"] / (ms_task * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved / HBM_PEAK_GBS,
-                    traffic=None if args.num_kv_splits is not None or args.num_cus
+                    traffic=None if args.num_kv_splits is not None or args.num_cus or args.cascade != 2
                     else measured_traffic(args.config))
     log(f"[bench] value {value:.1f} {unit}; dominant kernel (tasks pass) {achieved:.1f} {roof['unit']} "
         f"= {100 * roof['frac']:.1f}% of {roof['bound']} peak")
@@ -382,7 +385,7 @@ def main():
                vs_baseline=None, dtype=b.dtype, data="synthetic",
                config=dict(workload=b.name, num_seqs=b.num_seqs, query_rows=b.num_rows,
                            q_heads=b.num_q_heads, kv_heads=b.num_kv_heads, head_dim=b.head_dim,
-                           block_size=16, kv_splits=b.num_kv_splits or "auto",
+                           block_size=16, kv_splits=b.num_kv_splits or "auto", cascade=args.cascade,
                            unique_kv_bytes=work["kv_bytes_unique"],
                            logical_kv_bytes=work["kv_bytes_logical"], flop=work["flop"],
                            algorithmic_bytes=work["bytes"], cache_flush_between_steps=not args.no_flush),

@@ -106,7 +106,22 @@ typedef enum pmattn_dtype { PMATTN_BF16 = 0, PMATTN_F32 = 1 } pmattn_dtype;
  *              speculative verification, XY-Serve review, Figure 8 caption and
  *              "Significance"; Medusa and SpecInfer by title). A chain (parent
  *              r - 1) is the causal rule. A sequence whose parents are not a
- *              chain holds at most 64 rows. */
+ *              chain holds at most 64 rows.
+ *  cascade     0: off. 1 or 2: shared-prefix cascade (two-phase attention) for
+ *              sequences whose rows fit one wave task (q_len * Hq/Hkv <= 64,
+ *              i.e. decode and verify): runs of leading physical blocks that
+ *              two or more of them share, and that lie wholly before each
+ *              one's first query row, are attended once for all sharers (their
+ *              rows gathered into one virtual sequence); each sharer then
+ *              attends only to the keys after its deepest shared run, and the
+ *              log-sum-exp merge joins the parts (SGLang review, "Core claim":
+ *              shared prefixes computed once; XY-Serve review "Core claim":
+ *              prefix reuse). The result is the same attention. 1 makes a
+ *              group of every such run; 2 (automatic) only of runs shared by
+ *              at least 8 sequences over at least 64 blocks since the group
+ *              above (shorter or narrower sharing is served by the caches and
+ *              measured slower with the extra merge); a run left out is folded
+ *              into the groups below it. */
 typedef struct pmattn_plan_desc {
   int32_t num_seqs;
   const int32_t* q_len;
@@ -125,6 +140,7 @@ typedef struct pmattn_plan_desc {
   int32_t num_cus;
   uint64_t work_shuffle_seed;
   const int32_t* tree_parent;
+  int32_t cascade;
 } pmattn_plan_desc;
 
 typedef struct pmattn_plan_s* pmattn_plan_t;
@@ -146,8 +162,10 @@ typedef struct pmattn_work_item {
   int32_t part;
 } pmattn_work_item;
 
-/* One output row (row, q_head) assembled from nparts partial records
- * rec0, rec0 + rec_stride, ... by the log-sum-exp merge. */
+/* One output row (row, q_head) assembled from nparts partial records by the
+ * log-sum-exp merge: records rec0, rec0 + rec_stride, ... when rec_stride > 0;
+ * when rec_stride == -1 (rows of cascade sharers), the record ids are
+ * rec_index[rec0 .. rec0 + nparts) of the plan tables. */
 typedef struct pmattn_merge_row {
   int32_t rec0;
   int32_t rec_stride;
@@ -194,6 +212,22 @@ typedef struct pmattn_plan_tables {
   const uint64_t* row_tree_mask;
   int32_t num_append_units;
   const pmattn_append_unit* append_units;  /* [num_append_units], sequence order */
+  const int32_t* class_cascade;     /* [num_classes] 1: tasks of virtual (cascade) sequences */
+  /* cascade virtual sequences: keys [cascade_lo, cascade_hi) of block-table
+   * row cascade_seq, rows virtual_row_src[cascade_row_begin .. + cascade_rows),
+   * cascade_splits KV partitions each. Tasks of cascade classes index rows in
+   * this virtual row space (row_begin) and take positions past cascade_hi. */
+  int32_t num_cascade;
+  const int32_t* cascade_lo;
+  const int32_t* cascade_hi;
+  const int32_t* cascade_seq;
+  const int32_t* cascade_row_begin;
+  const int32_t* cascade_rows;
+  const int32_t* cascade_splits;
+  int32_t num_virtual_rows;
+  const int32_t* virtual_row_src;   /* [num_virtual_rows] the real query row of each */
+  int32_t num_rec_index;
+  const int32_t* rec_index;         /* record ids of indirect merge rows */
 } pmattn_plan_tables;
 
 /* Build a plan on the host. Validates the batch (see pmattn_plan_desc),

@@ -248,3 +248,153 @@ def check_coverage(items, q_len, q_start, num_kv_heads):
         "coverage does not end at the row's position"
     same = key[1:] == key[:-1]
     assert (hi[:-1][same] == lo[1:][same]).all(), "gap or overlap between tasks of one row"
+
+
+CASCADE_AUTO_MEMBERS = 8
+CASCADE_AUTO_BLOCKS = 64
+
+
+def cascade_groups(q_len, q_start, block_table, group, mode=1):
+    """Shared-prefix runs of the cascade, in planner order, and each
+    sequence's first own key.
+
+    Candidates are sequences whose rows fit one wave task (q_len * G <= 64)
+    with at least one whole block before their first query row. From the root,
+    the candidates are bucketed by their block id at the current block index
+    (ascending ids); a bucket of two or more extends its run while every member
+    still has a whole block there with the same id, becomes a group
+    (lo, hi, first member, members) and is searched further from its run's end.
+    All groups of one search step are recorded before descending, and the
+    first bucket is searched first. A member's own keys start at the end of
+    its deepest run. Mode 2 (automatic) makes a group only of runs with at
+    least 8 members spanning at least 64 blocks since the nearest group above;
+    a run left out is folded into the ranges of the groups below it.
+    """
+    n = len(q_len)
+    share = [int(q_start[s]) // BLOCK for s in range(n)]
+    own_lo = np.zeros(n, np.int64)
+    cands = [s for s in range(n) if q_len[s] > 0 and int(q_len[s]) * group <= MAX_WAVE_ROWS and share[s] >= 1]
+    min_members = CASCADE_AUTO_MEMBERS if mode == 2 else 2
+    min_blocks = CASCADE_AUTO_BLOCKS if mode == 2 else 1
+    groups = []
+    stack = [(cands, 0, 0)]
+    while stack:
+        mem, depth, cover = stack.pop()
+        buckets = {}
+        for m in mem:
+            if share[m] > depth:
+                buckets.setdefault(int(block_table[m][depth]), []).append(m)
+        kids = []
+        for blk in sorted(buckets):
+            bm = buckets[blk]
+            if len(bm) < 2:
+                continue
+            end = depth + 1
+            while all(share[m] > end and block_table[m][end] == block_table[bm[0]][end] for m in bm):
+                end += 1
+            kid_cover = cover
+            if len(bm) >= min_members and end - cover >= min_blocks:
+                groups.append((cover * BLOCK, end * BLOCK, bm[0], list(bm)))
+                for m in bm:
+                    own_lo[m] = end * BLOCK
+                kid_cover = end
+            kids.append((bm, end, kid_cover))
+        stack.extend(reversed(kids))
+    return groups, own_lo
+
+
+def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0, num_cus=0,
+               cascade=False):
+    """Units of work (real sequences, then cascade groups) with their tiles and
+    KV partitions, by the same rules as ``token_tiles`` / ``num_splits`` /
+    ``split_ranges`` applied to each unit's own key range [lo, hi).
+
+    Returns dict(units=[...], vrow_src=array, groups=[...]); a unit is
+    dict(virt, seq, rows, row0, pos0, lo, hi, tiles=[(t0, nt, cls, kv_end)],
+    splits, bounds=[[lo, hi), ...]).
+    """
+    groups, own_lo = (cascade_groups(q_len, q_start, block_table, group, int(cascade)) if cascade
+                      else ([], np.zeros(len(q_len), np.int64)))
+    first = np.concatenate([[0], np.cumsum(np.asarray(q_len, np.int64))[:-1]]).astype(np.int64)
+    units = []
+    for s in range(len(q_len)):
+        units.append(dict(virt=False, seq=s, rows=int(q_len[s]), row0=int(first[s]), pos0=int(q_start[s]),
+                          lo=int(own_lo[s]), hi=int(q_start[s]) + int(q_len[s])))
+    vrow_src = []
+    for lo, hi, ts, mem in groups:
+        r0 = len(vrow_src)
+        for m in mem:
+            vrow_src.extend(range(int(first[m]), int(first[m]) + int(q_len[m])))
+        units.append(dict(virt=True, seq=ts, rows=len(vrow_src) - r0, row0=r0, pos0=hi, lo=lo, hi=hi))
+    tok_wg = max(1, MAX_TASK_ROWS // group)
+    for u in units:
+        u["tiles"] = []
+        if u["rows"] == 0:
+            continue
+        end = (lambda t0, nt, u=u: u["hi"] if u["virt"] else u["pos0"] + t0 + nt)
+        if u["rows"] * group <= MAX_WAVE_ROWS:
+            cls = next(c for c in CLASS_ROWS if u["rows"] * group <= c)
+            u["tiles"].append((0, u["rows"], cls, end(0, u["rows"])))
+        else:
+            for t0 in range(0, u["rows"], tok_wg):
+                nt = min(tok_wg, u["rows"] - t0)
+                u["tiles"].append((t0, nt, MAX_TASK_ROWS, end(t0, nt)))
+    if num_kv_splits > 0:
+        for u in units:
+            u["splits"] = num_kv_splits if u["rows"] else 0
+    else:
+        total = [0, 0]
+        for u in units:
+            u["last"], u["kind"] = 0, 0
+            for _, _, cls, kv_end in u["tiles"]:
+                k = 1 if cls > MAX_WAVE_ROWS else 0
+                c = -(-(kv_end - u["lo"]) // BLOCK) * (2 + cls // 16)
+                total[k] += c * num_kv_heads
+                u["last"] = max(u["last"], c)
+                u["kind"] = k
+        cus = num_cus if num_cus > 0 else 256
+        quantum = [max(MIN_QUANTUM, -(-total[0] // (cus * TASKS_PER_CU))),
+                   max(MIN_QUANTUM, -(-total[1] // (cus * WG_TASKS_PER_CU)))]
+        for u in units:
+            nblk = -(-(u["hi"] - u["lo"]) // BLOCK)
+            u["splits"] = max(1, min(-(-u["last"] // quantum[u["kind"]]), MAX_AUTO_SPLITS, nblk)) if u["rows"] else 0
+    for u in units:
+        u["bounds"] = []
+        if u["splits"]:
+            nblk = -(-(u["hi"] - u["lo"]) // BLOCK)
+            chunk = max(1, -(-nblk // u["splits"]))
+            for p in range(u["splits"]):
+                u["bounds"].append((min(u["lo"] + p * chunk * BLOCK, u["hi"]),
+                                    min(u["lo"] + (p + 1) * chunk * BLOCK, u["hi"])))
+    return dict(units=units, vrow_src=np.array(vrow_src, np.int32), groups=groups)
+
+
+def check_coverage_cascade(items, class_cascade, class_begin, vrow_src, q_len, q_start, num_kv_heads):
+    """Coverage for plans with cascade classes: tasks of cascade classes hold
+    virtual rows (mapped to real rows by vrow_src) over keys they see whole;
+    every visible (row, kv head, key) must be covered by exactly one task."""
+    row_seq, row_pos = row_tables(q_len, q_start)
+    nrows = row_seq.shape[0]
+    iv = []   # (row, kvh, lo, hi)
+    for c in range(len(class_cascade)):
+        for it in items[class_begin[c]:class_begin[c + 1]]:
+            seq, kvh, r0, nt, p0, lo, hi = (int(x) for x in it[:7])
+            for t in range(nt):
+                if class_cascade[c]:
+                    row = int(vrow_src[r0 + t])
+                    assert hi <= row_pos[row], "cascade task reads keys at or past a member row"
+                    iv.append((row, kvh, lo, hi))
+                else:
+                    assert row_seq[r0 + t] == seq and row_pos[r0 + t] == p0 + t
+                    h = min(hi, p0 + t + 1)
+                    if lo < h:
+                        iv.append((r0 + t, kvh, lo, h))
+    iv.sort()
+    cur = {}
+    for row, kvh, lo, hi in iv:
+        want = cur.get((row, kvh), 0)
+        assert lo == want, f"gap or overlap at row {row} kv head {kvh}: {want} vs {lo}"
+        cur[(row, kvh)] = hi
+    for row in range(nrows):
+        for g in range(num_kv_heads):
+            assert cur.get((row, g), 0) == int(row_pos[row]) + 1, f"row {row} kv head {g} not covered"

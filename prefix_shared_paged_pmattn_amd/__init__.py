@@ -106,7 +106,15 @@ class Plan:
                            if t.row_tree_mask and t.num_rows else None),
             append_units=(np.ctypeslib.as_array(ctypes.cast(t.append_units, ctypes.POINTER(ctypes.c_int32)),
                                                 shape=(t.num_append_units * 5,)).reshape(-1, 5).copy()
-                          if t.num_append_units else np.zeros((0, 5), np.int32)))
+                          if t.num_append_units else np.zeros((0, 5), np.int32)),
+            class_cascade=arr(t.class_cascade, t.num_classes),
+            cascade=dict(lo=arr(t.cascade_lo, t.num_cascade), hi=arr(t.cascade_hi, t.num_cascade),
+                         seq=arr(t.cascade_seq, t.num_cascade),
+                         row_begin=arr(t.cascade_row_begin, t.num_cascade),
+                         rows=arr(t.cascade_rows, t.num_cascade),
+                         splits=arr(t.cascade_splits, t.num_cascade)),
+            virtual_row_src=arr(t.virtual_row_src, t.num_virtual_rows),
+            rec_index=arr(t.rec_index, t.num_rec_index))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the work list into ``workspace``."""
@@ -118,10 +126,11 @@ class Plan:
 
 def plan(q_len, seq_len, q_start, block_table, *, num_pool_blocks: int, num_q_heads: int,
          num_kv_heads: int, head_dim: int, dtype="bf16", scale: float, num_kv_splits: int = 0,
-         num_cus: int = 0, work_shuffle_seed: int = 0, tree_parent=None) -> Plan:
+         num_cus: int = 0, work_shuffle_seed: int = 0, tree_parent=None, cascade: int = 2) -> Plan:
     """``pmattn_plan`` over host arrays (int32-convertible). ``tree_parent``:
     None, or one int per query row (parent row within its sequence, -1 for the
-    context) for speculative token trees."""
+    context) for speculative token trees. ``cascade``: 0 off, 1 every shared
+    prefix run of decode/verify sequences, 2 (default) automatic."""
     ql, sl, qs = _i32(q_len), _i32(seq_len), _i32(q_start)
     bt = _i32(block_table)
     if bt.ndim != 2:
@@ -142,7 +151,7 @@ def plan(q_len, seq_len, q_start, block_table, *, num_pool_blocks: int, num_q_he
                    head_dim=int(head_dim), dtype=_dtype_code(dtype), scale=float(scale),
                    num_kv_splits=int(num_kv_splits), num_cus=int(num_cus),
                    work_shuffle_seed=int(work_shuffle_seed),
-                   tree_parent=i32p(tp) if tp is not None else None)
+                   tree_parent=i32p(tp) if tp is not None else None, cascade=int(cascade))
     h = ctypes.c_void_p()
     _check(L.load().pmattn_plan(ctypes.byref(d), ctypes.byref(h)))
     shape = dict(num_seqs=b, num_rows=int(ql.sum()), bt_stride=int(bt.shape[1]),

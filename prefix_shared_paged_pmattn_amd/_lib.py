@@ -32,6 +32,7 @@ class PlanDesc(ctypes.Structure):
         ("num_cus", ctypes.c_int32),
         ("work_shuffle_seed", ctypes.c_uint64),
         ("tree_parent", _i32p),
+        ("cascade", ctypes.c_int32),
     ]
 
 
@@ -65,6 +66,18 @@ class PlanTables(ctypes.Structure):
         ("row_tree_mask", ctypes.POINTER(ctypes.c_uint64)),
         ("num_append_units", ctypes.c_int32),
         ("append_units", ctypes.c_void_p),
+        ("class_cascade", _i32p),
+        ("num_cascade", ctypes.c_int32),
+        ("cascade_lo", _i32p),
+        ("cascade_hi", _i32p),
+        ("cascade_seq", _i32p),
+        ("cascade_row_begin", _i32p),
+        ("cascade_rows", _i32p),
+        ("cascade_splits", _i32p),
+        ("num_virtual_rows", ctypes.c_int32),
+        ("virtual_row_src", _i32p),
+        ("num_rec_index", ctypes.c_int32),
+        ("rec_index", _i32p),
     ]
 
 
@@ -147,6 +160,15 @@ def load() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -m prefix_shared_paged_pmattn_amd.build` "
                 "(there is no fallback implementation)")
+        # torch ships its own HIP runtime under the same soname
+        # (libamdhip64.so.7) as /opt/rocm's, and the dynamic loader keeps the
+        # first one loaded. Load torch's first, so that torch and this library
+        # share one runtime whatever the caller touches first; the other order
+        # left torch without a usable device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:  # pragma: no cover - host-only use without torch
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         for name, res, args in SIGNATURES:
             fn = getattr(lib, name)

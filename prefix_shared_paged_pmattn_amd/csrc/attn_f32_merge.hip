@@ -127,16 +127,30 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     row = w / a.hq;
     qh = w - (int)row * a.hq;
   }
-  const float* po = a.part_o + rec0 * D + lane * V;
+  // record id of partial p0 + lane: strided (rec0 + p * stride) or listed
+  // (rec_index[rec0 + p], rows of cascade sharers); partial u's id reaches
+  // every lane by a broadcast
+  const bool listed = stride < 0;
+  auto rec_of = [&](int p0) -> int64_t {
+    const int p = p0 + lane;
+    if (p >= np) return 0;
+    return listed ? (int64_t)a.rec_index[rec0 + p] : rec0 + (int64_t)p * stride;
+  };
+  const int64_t rid0 = rec_of(0);
+  const float* po = a.part_o + lane * V;
   float pre[kPre][V];
 #pragma unroll
-  for (int u = 0; u < kPre; ++u)
+  for (int u = 0; u < kPre; ++u) {
+    const int64_t ru = __shfl(rid0, u);
 #pragma unroll
-    for (int v = 0; v < V; ++v) pre[u][v] = u < np ? po[(int64_t)u * stride * D + v] : 0.f;
-  const float l0 = lane < np ? a.part_lse[rec0 + lane * stride] : kNegInf;
+    for (int v = 0; v < V; ++v) pre[u][v] = u < np ? po[ru * D + v] : 0.f;
+  }
+  const float l0 = lane < np ? a.part_lse[rid0] : kNegInf;
   float mx = l0;
-  for (int p0 = 64; p0 < np; p0 += 64)
-    if (p0 + lane < np) mx = fmaxf(mx, a.part_lse[rec0 + (p0 + lane) * stride]);
+  for (int p0 = 64; p0 < np; p0 += 64) {
+    const int64_t r = rec_of(p0);
+    if (p0 + lane < np) mx = fmaxf(mx, a.part_lse[r]);
+  }
   mx = wave_max(mx);
   float acc[V], tot = 0.f;
 #pragma unroll
@@ -144,8 +158,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (mx != kNegInf) {
     for (int p0 = 0; p0 < np; p0 += 64) {
       const int pn = min(64, np - p0);
+      const int64_t rid = p0 == 0 ? rid0 : rec_of(p0);
       float l = l0;
-      if (p0 > 0) l = lane < pn ? a.part_lse[rec0 + (p0 + lane) * stride] : kNegInf;
+      if (p0 > 0) l = lane < pn ? a.part_lse[rid] : kNegInf;
       const float wt = (l == kNegInf) ? 0.f : expf(l - mx);
       tot += wave_sum(wt);
       int q = 0;
@@ -161,9 +176,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       for (; q + 8 <= pn; q += 8) {
         float src[8][V];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 8; ++u) {
+          const int64_t ru = __shfl(rid, q + u);
 #pragma unroll
-          for (int v = 0; v < V; ++v) src[u][v] = po[(int64_t)(p0 + q + u) * stride * D + v];
+          for (int v = 0; v < V; ++v) src[u][v] = po[ru * D + v];
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const float wu = __shfl(wt, q + u);
@@ -173,9 +190,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       }
       for (; q < pn; ++q) {
         const float wu = __shfl(wt, q);
+        const int64_t ru = __shfl(rid, q);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-          const float x = po[(int64_t)(p0 + q) * stride * D + v];
+          const float x = po[ru * D + v];
           acc[v] = fmaf(wu, wu != 0.f ? x : 0.f, acc[v]);
         }
       }

@@ -37,6 +37,7 @@ struct MergeArgs {
   const float* part_o;
   const float* part_lse;
   const pmattn_merge_row* rows;  // null: implicit [P][rows][H] layout
+  const int32_t* rec_index;      // record ids of listed merge rows (rec_stride < 0)
   void* out;
   float* lse;
   int32_t count;                 // output (row, head) pairs
@@ -63,6 +64,9 @@ hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
 hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st);
+// Copy the query rows src_rows[0..n) of q ([R][row_elems]) into dst ([n][row_elems]).
+hipError_t launch_gather_rows(const void* q, const int32_t* src_rows, int n, int row_bytes, void* dst,
+                              hipStream_t st);
 hipError_t launch_copy_blocks(int head_dim, int dtype, const pmattn_block_copy* copies, int n,
                               void* k_pool, void* v_pool, int hkv, hipStream_t st);
 

@@ -114,10 +114,25 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.scale = P.scale;
   a.scale_log2 = P.scale * kLog2e;
   const pmattn_work_item* items = reinterpret_cast<const pmattn_work_item*>(ws + P.off_items);
+  // cascade: gather the virtual sequences' query rows first (same stream, so
+  // every class launched after it, on either stream, sees them)
+  void* qv = ws + P.off_qv;
+  if (!P.vrow_src.empty()) {
+    const int row_bytes = P.hq * P.head_dim * (P.dtype == PMATTN_BF16 ? 2 : 4);
+    hipError_t e = launch_gather_rows(q, reinterpret_cast<const int32_t*>(ws + P.off_vrow),
+                                      (int)P.vrow_src.size(), row_bytes, qv, st);
+    if (e != hipSuccess) return hip_fail(e, "row gather kernel launch");
+  }
   auto launch_class = [&](size_t c, hipStream_t s) -> hipError_t {
     AttnArgs ac = a;
     ac.items = items + P.class_begin[c];
     ac.item_count = P.class_begin[c + 1] - P.class_begin[c];
+    if (P.class_cascade[c]) {
+      // virtual rows: gathered queries; their keys all lie below every
+      // member's first row, so no tree mask applies
+      ac.q = qv;
+      ac.row_mask = nullptr;
+    }
     if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);
     if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
     return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, s);
@@ -177,6 +192,7 @@ static pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* 
   m.part_o = reinterpret_cast<const float*>(ws + P.off_part_o);
   m.part_lse = reinterpret_cast<const float*>(ws + P.off_part_lse);
   m.rows = reinterpret_cast<const pmattn_merge_row*>(ws + P.off_merge);
+  m.rec_index = reinterpret_cast<const int32_t*>(ws + P.off_rec_index);
   m.out = out;
   m.lse = lse;
   m.count = (int32_t)P.merge_rows.size();
@@ -272,6 +288,7 @@ pmattn_status pmattn_merge_lse(int32_t num_parts, int32_t num_rows, int32_t num_
   m.part_o = part_o;
   m.part_lse = part_lse;
   m.rows = nullptr;
+  m.rec_index = nullptr;
   m.out = out;
   m.lse = lse;
   m.count = num_rows * num_heads;

@@ -12,6 +12,7 @@
 //
 // Pure host code: no HIP call, so every rule here is testable on a CPU.
 #include <algorithm>
+#include <map>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -37,6 +38,10 @@ constexpr int64_t kWgTasksPerCu = 4;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;
 constexpr int kMaxAutoSplits = 64;
+// Automatic cascade: a shared run becomes a group only with this many members
+// and this many blocks (measured on the pages' workloads).
+constexpr int kCascadeAutoMembers = 8;
+constexpr int kCascadeAutoBlocks = 64;
 
 int class_of_rows(int rows) {
   for (int c = 0; c < kNumClasses; ++c)
@@ -52,8 +57,9 @@ uint64_t splitmix64(uint64_t& s) {
 }
 
 struct Tile {
-  int32_t seq, tok_begin, n_tok, cls;
-  int32_t kv_end;  // position of the tile's last token + 1
+  int32_t seq;  // unit: a real sequence (< B) or a virtual cascade sequence
+  int32_t tok_begin, n_tok, cls;
+  int32_t kv_end;  // one past the tile's last visible key
 };
 }  // namespace
 
@@ -85,6 +91,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (d->num_kv_splits < 0 || d->num_kv_splits > kMaxSplits)
     return fail(PMATTN_E_INVALID, "num_kv_splits must be in 0..256");
   if (d->num_cus < 0) return fail(PMATTN_E_INVALID, "num_cus must be >= 0");
+  if (d->cascade < 0 || d->cascade > 2) return fail(PMATTN_E_INVALID, "cascade must be 0, 1 or 2");
   if (d->num_pool_blocks < 0) return fail(PMATTN_E_INVALID, "num_pool_blocks < 0");
   if (B > 0 && d->bt_stride < 1) return fail(PMATTN_E_INVALID, "bt_stride must be >= 1");
 
@@ -233,109 +240,241 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     }
   }
 
-  // ---- tiles: runs of query tokens whose G heads fit one task --------------
-  // A sequence whose rows fit one wave task (q_len * G <= 64) is one tile;
-  // longer ones are cut into runs of 128/G tokens for the workgroup kernel.
-  const int tok_per_wg = std::max(1, kMaxTaskRows / G);
-  std::vector<Tile> tiles;
+  // ---- cascade: shared prefix runs of decode/verify sequences -----------------
+  // Sequences whose rows fit one wave task and whose leading physical blocks
+  // coincide are grouped like a radix tree over block ids. Each run of blocks
+  // shared by two or more of them, lying wholly before every member's first
+  // query row, becomes a virtual sequence: its rows are all members' rows, its
+  // keys the run. The members then attend only to the keys after their
+  // deepest run, and the log-sum-exp merge joins the parts.
   std::vector<int32_t> row_off(B + 1, 0);
   for (int s = 0; s < B; ++s) row_off[s + 1] = row_off[s] + d->q_len[s];
-  for (int s = 0; s < B; ++s) {
-    const int ql = d->q_len[s];
+  std::vector<int32_t> own_lo(B, 0);  // first key of each sequence's own range
+  std::vector<char> member(B, 0);
+  struct VSeq {
+    int32_t lo, hi, table_seq, row_begin, rows;
+  };
+  std::vector<VSeq> vseqs;
+  if (d->cascade) {
+    auto bt = [&](int s, int j) { return d->block_table[(int64_t)s * d->bt_stride + j]; };
+    auto shareable = [&](int s) { return d->q_start[s] / kBlock; };  // blocks before the first row
+    std::vector<int32_t> cands;
+    for (int s = 0; s < B; ++s)
+      if (d->q_len[s] > 0 && (int64_t)d->q_len[s] * G <= kMaxWaveRows && shareable(s) >= 1) cands.push_back(s);
+    // automatic mode: only runs that enough sequences share over enough
+    // blocks become groups (measured: pairs, and runs of a few hundred
+    // tokens, are already served by the caches and lose to the extra merge);
+    // a run left out is folded into its descendants' ranges (cover_lo)
+    const int min_members = d->cascade == 2 ? kCascadeAutoMembers : 2;
+    const int min_blocks = d->cascade == 2 ? kCascadeAutoBlocks : 1;
+    struct Node {
+      std::vector<int32_t> mem;
+      int32_t depth, cover_lo;
+    };
+    std::vector<Node> stack;
+    stack.push_back(Node{cands, 0, 0});
+    std::vector<std::vector<int32_t>> members;
+    while (!stack.empty()) {
+      Node node = std::move(stack.back());
+      stack.pop_back();
+      const int32_t depth = node.depth;
+      std::map<int32_t, std::vector<int32_t>> buckets;
+      for (int32_t m : node.mem)
+        if (shareable(m) > depth) buckets[bt(m, depth)].push_back(m);
+      std::vector<Node> kids;
+      for (auto& kv : buckets) {
+        const std::vector<int32_t>& bm = kv.second;
+        if (bm.size() < 2) continue;
+        int32_t L = depth + 1;
+        for (;;) {
+          bool same = true;
+          for (int32_t m : bm) same = same && shareable(m) > L && bt(m, L) == bt(bm[0], L);
+          if (!same) break;
+          ++L;
+        }
+        int32_t cover = node.cover_lo;
+        if ((int)bm.size() >= min_members && L - node.cover_lo >= min_blocks) {
+          vseqs.push_back(VSeq{node.cover_lo * kBlock, L * kBlock, bm[0], 0, 0});
+          members.push_back(bm);
+          for (int32_t m : bm) {
+            own_lo[m] = L * kBlock;
+            member[m] = 1;
+          }
+          cover = L;
+        }
+        kids.push_back(Node{bm, L, cover});
+      }
+      for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back(std::move(*it));
+    }
+    for (size_t v = 0; v < vseqs.size(); ++v) {
+      vseqs[v].row_begin = (int32_t)P.vrow_src.size();
+      for (int32_t m : members[v])
+        for (int32_t r = 0; r < d->q_len[m]; ++r) P.vrow_src.push_back(row_off[m] + r);
+      vseqs[v].rows = (int32_t)P.vrow_src.size() - vseqs[v].row_begin;
+      P.cascade_lo.push_back(vseqs[v].lo);
+      P.cascade_hi.push_back(vseqs[v].hi);
+      P.cascade_seq.push_back(vseqs[v].table_seq);
+      P.cascade_row_begin.push_back(vseqs[v].row_begin);
+      P.cascade_rows.push_back(vseqs[v].rows);
+    }
+  }
+  const int V = (int)vseqs.size();
+  const int U = B + V;  // units: the real sequences, then the virtual ones
+  auto unit_rows = [&](int u) { return u < B ? d->q_len[u] : vseqs[u - B].rows; };
+  auto unit_lo = [&](int u) { return u < B ? own_lo[u] : vseqs[u - B].lo; };
+  auto unit_hi = [&](int u) { return u < B ? d->q_start[u] + d->q_len[u] : vseqs[u - B].hi; };
+
+  // ---- tiles: runs of query tokens whose G heads fit one task --------------
+  // A unit whose rows fit one wave task (rows * G <= 64) is one tile; longer
+  // ones are cut into runs of 128/G tokens for the workgroup kernel.
+  const int tok_per_wg = std::max(1, kMaxTaskRows / G);
+  std::vector<Tile> tiles;
+  for (int u = 0; u < U; ++u) {
+    const int ql = unit_rows(u);
     if (ql == 0) continue;
+    auto kv_end = [&](int t0, int nt) { return u < B ? d->q_start[u] + t0 + nt : vseqs[u - B].hi; };
     if ((int64_t)ql * G <= kMaxWaveRows) {
-      tiles.push_back(Tile{s, 0, ql, class_of_rows(ql * G), d->q_start[s] + ql});
+      tiles.push_back(Tile{u, 0, ql, class_of_rows(ql * G), kv_end(0, ql)});
       continue;
     }
     for (int t0 = 0; t0 < ql; t0 += tok_per_wg) {
       const int nt = std::min(tok_per_wg, ql - t0);
-      tiles.push_back(Tile{s, t0, nt, kNumClasses - 1, d->q_start[s] + t0 + nt});
+      tiles.push_back(Tile{u, t0, nt, kNumClasses - 1, kv_end(t0, nt)});
     }
   }
 
-  // ---- KV partitions per sequence ----------------------------------------
-  P.num_splits.assign(B, 0);
+  // ---- KV partitions per unit ------------------------------------------------
+  std::vector<int32_t> usplits(U, 0);
   if (d->num_kv_splits > 0) {
-    for (int s = 0; s < B; ++s) P.num_splits[s] = d->q_len[s] > 0 ? d->num_kv_splits : 0;
+    for (int u = 0; u < U; ++u) usplits[u] = unit_rows(u) > 0 ? d->num_kv_splits : 0;
   } else {
     // Two resource classes are balanced separately: wave tasks (<= 64 rows,
-    // KV-stream bound) and workgroup tasks (128 rows, MFMA bound). A
-    // sequence's partition count is ceil(cost of its largest tile / quantum
-    // of its class).
+    // KV-stream bound) and workgroup tasks (128 rows, MFMA bound). A unit's
+    // partition count is ceil(cost of its largest tile / quantum of its class).
     int64_t total[2] = {0, 0};
-    std::vector<int64_t> last_cost(B, 0);
-    std::vector<int> seq_kind(B, 0);
+    std::vector<int64_t> last_cost(U, 0);
+    std::vector<int> unit_kind(U, 0);
     for (const Tile& t : tiles) {
       const int kind = kClassRows[t.cls] > kMaxWaveRows ? 1 : 0;
-      const int64_t c = (int64_t)((t.kv_end + kBlock - 1) / kBlock) * unit_cost(t.cls);
+      const int64_t c = (int64_t)((t.kv_end - unit_lo(t.seq) + kBlock - 1) / kBlock) * unit_cost(t.cls);
       total[kind] += c * d->num_kv_heads;
       last_cost[t.seq] = std::max(last_cost[t.seq], c);
-      seq_kind[t.seq] = kind;
+      unit_kind[t.seq] = kind;
     }
     const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
     const int64_t target[2] = {cus * kTasksPerCu, cus * kWgTasksPerCu};
     int64_t quantum[2];
     for (int k = 0; k < 2; ++k)
       quantum[k] = std::max(kMinQuantum, (total[k] + target[k] - 1) / target[k]);
-    for (int s = 0; s < B; ++s) {
-      if (d->q_len[s] == 0) continue;
-      const int64_t nblk = (d->q_start[s] + d->q_len[s] + kBlock - 1) / kBlock;
-      const int64_t q = quantum[seq_kind[s]];
-      int64_t p = (last_cost[s] + q - 1) / q;
+    for (int u = 0; u < U; ++u) {
+      if (unit_rows(u) == 0) continue;
+      const int64_t nblk = (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
+      const int64_t q = quantum[unit_kind[u]];
+      int64_t p = (last_cost[u] + q - 1) / q;
       p = std::min<int64_t>(std::min<int64_t>(p, kMaxAutoSplits), nblk);
-      P.num_splits[s] = (int32_t)std::max<int64_t>(1, p);
+      usplits[u] = (int32_t)std::max<int64_t>(1, p);
     }
   }
-  P.split_offset.assign(B + 1, 0);
-  for (int s = 0; s < B; ++s) P.split_offset[s + 1] = P.split_offset[s] + P.num_splits[s];
-  P.split_begin.resize(P.split_offset[B]);
-  P.split_end.resize(P.split_offset[B]);
-  for (int s = 0; s < B; ++s) {
-    const int np = P.num_splits[s];
+  std::vector<int32_t> uoff(U + 1, 0), ubeg, uend;
+  for (int u = 0; u < U; ++u) uoff[u + 1] = uoff[u] + usplits[u];
+  ubeg.resize(uoff[U]);
+  uend.resize(uoff[U]);
+  for (int u = 0; u < U; ++u) {
+    const int np = usplits[u];
     if (!np) continue;
-    const int64_t kv = (int64_t)d->q_start[s] + d->q_len[s];
-    const int64_t nblk = (kv + kBlock - 1) / kBlock;
+    const int64_t lo = unit_lo(u), kv = unit_hi(u);
+    const int64_t nblk = (kv - lo + kBlock - 1) / kBlock;
     const int64_t chunk = std::max<int64_t>(1, (nblk + np - 1) / np);
     for (int p = 0; p < np; ++p) {
-      P.split_begin[P.split_offset[s] + p] = (int32_t)std::min<int64_t>(p * chunk * kBlock, kv);
-      P.split_end[P.split_offset[s] + p] = (int32_t)std::min<int64_t>((p + 1) * chunk * kBlock, kv);
+      ubeg[uoff[u] + p] = (int32_t)std::min<int64_t>(lo + p * chunk * kBlock, kv);
+      uend[uoff[u] + p] = (int32_t)std::min<int64_t>(lo + (p + 1) * chunk * kBlock, kv);
     }
   }
+  P.num_splits.assign(usplits.begin(), usplits.begin() + B);
+  P.split_offset.assign(uoff.begin(), uoff.begin() + B + 1);
+  P.split_begin.assign(ubeg.begin(), ubeg.begin() + uoff[B]);
+  P.split_end.assign(uend.begin(), uend.begin() + uoff[B]);
+  P.cascade_splits.assign(usplits.begin() + B, usplits.end());
 
   // ---- tasks, partial records and merge rows --------------------------------
-  std::vector<std::vector<pmattn_work_item>> by_class(kNumClasses);
+  // Rows of cascade members collect their records from several tasks: their
+  // merge rows list record ids (rec_stride -1) instead of a stride.
+  std::vector<std::vector<pmattn_work_item>> by_class(2 * kNumClasses);
+  std::vector<int32_t> member_slot(P.num_rows, -1);
+  int32_t n_member_rows = 0;
+  for (int s = 0; s < B; ++s)
+    if (member[s])
+      for (int r = 0; r < d->q_len[s]; ++r) member_slot[row_off[s] + r] = n_member_rows++;
+  // records of cascade sharers' rows: one entry per (tile, kv head), expanded
+  // into rec_index below (count per (row, head), then fill)
+  struct Listed {
+    int64_t rec_base;
+    int32_t parts, trows, row0, g;
+    bool virt;
+  };
+  std::vector<Listed> listed_blocks;
   int64_t records = 0;
   for (const Tile& t : tiles) {
+    const int u = t.seq;
+    const bool virt = u >= B;
     const int trows = t.n_tok * G;
-    const int base = P.split_offset[t.seq];
+    const int base = uoff[u];
     int k = 0;
-    for (int p = 0; p < P.num_splits[t.seq]; ++p)
-      if (P.split_begin[base + p] < std::min(P.split_end[base + p], t.kv_end)) ++k;
+    for (int p = 0; p < usplits[u]; ++p)
+      if (ubeg[base + p] < std::min(uend[base + p], t.kv_end)) ++k;
+    const bool listed = virt || member[u];
+    const bool recs = k > 1 || listed;
+    const int32_t row0 = virt ? vseqs[u - B].row_begin + t.tok_begin : row_off[u] + t.tok_begin;
     for (int g = 0; g < d->num_kv_heads; ++g) {
       const int64_t rec_base = records;
-      if (k > 1) records += (int64_t)k * trows;
+      if (recs) records += (int64_t)k * trows;
       int made = 0;
-      for (int p = 0; p < P.num_splits[t.seq]; ++p) {
-        const int32_t lo = P.split_begin[base + p];
-        const int32_t hi = std::min(P.split_end[base + p], t.kv_end);
+      for (int p = 0; p < usplits[u]; ++p) {
+        const int32_t lo = ubeg[base + p];
+        const int32_t hi = std::min(uend[base + p], t.kv_end);
         if (lo >= hi) continue;
         pmattn_work_item it;
-        it.seq = t.seq;
+        it.seq = virt ? vseqs[u - B].table_seq : u;
         it.kv_head = g;
-        it.row_begin = row_off[t.seq] + t.tok_begin;
+        it.row_begin = row0;
         it.n_tok = t.n_tok;
-        it.pos_begin = d->q_start[t.seq] + t.tok_begin;
+        it.pos_begin = virt ? vseqs[u - B].hi + t.tok_begin : d->q_start[u] + t.tok_begin;
         it.kv_begin = lo;
         it.kv_end = hi;
-        it.part = k > 1 ? (int32_t)(rec_base + (int64_t)made * trows) : -1;
-        by_class[t.cls].push_back(it);
+        it.part = recs ? (int32_t)(rec_base + (int64_t)made * trows) : -1;
+        by_class[t.cls + (virt ? kNumClasses : 0)].push_back(it);
         ++made;
       }
-      if (k > 1)
+      if (listed && made) listed_blocks.push_back(Listed{rec_base, made, trows, row0, g, virt});
+      if (k > 1 && !listed)
         for (int m = 0; m < trows; ++m)
-          P.merge_rows.push_back(pmattn_merge_row{(int32_t)(rec_base + m), trows, k,
-                                                  row_off[t.seq] + t.tok_begin + m / G, g * G + m % G});
+          P.merge_rows.push_back(pmattn_merge_row{(int32_t)(rec_base + m), trows, k, row0 + m / G, g * G + m % G});
     }
+  }
+  if (n_member_rows > 0) {
+    const size_t keys = (size_t)n_member_rows * d->num_q_heads;
+    auto key_of = [&](const Listed& lb, int m) {
+      const int32_t row = lb.virt ? P.vrow_src[lb.row0 + m / G] : lb.row0 + m / G;
+      return (size_t)member_slot[row] * d->num_q_heads + lb.g * G + m % G;
+    };
+    std::vector<int32_t> start(keys + 1, 0);
+    for (const Listed& lb : listed_blocks)
+      for (int m = 0; m < lb.trows; ++m) start[key_of(lb, m) + 1] += lb.parts;
+    for (size_t k = 0; k < keys; ++k) start[k + 1] += start[k];
+    P.rec_index.resize(start[keys]);
+    std::vector<int32_t> fill(start.begin(), start.end() - 1);
+    for (const Listed& lb : listed_blocks)
+      for (int m = 0; m < lb.trows; ++m) {
+        int32_t& at = fill[key_of(lb, m)];
+        for (int p = 0; p < lb.parts; ++p) P.rec_index[at++] = (int32_t)(lb.rec_base + (int64_t)p * lb.trows + m);
+      }
+    for (int s = 0; s < B; ++s)
+      if (member[s])
+        for (int r = 0; r < d->q_len[s]; ++r)
+          for (int h = 0; h < d->num_q_heads; ++h) {
+            const size_t k = (size_t)member_slot[row_off[s] + r] * d->num_q_heads + h;
+            P.merge_rows.push_back(pmattn_merge_row{start[k], -1, start[k + 1] - start[k], row_off[s] + r, h});
+          }
   }
   if (records > INT32_MAX / 2) return fail(PMATTN_E_INVALID, "too many partial records");
   P.num_records = (int32_t)records;
@@ -343,19 +482,20 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // ---- order: largest estimated cost first within each class (LPT) --------
   uint64_t rng = d->work_shuffle_seed;
   P.class_begin.push_back(0);
-  for (int c = 0; c < kNumClasses; ++c) {
+  for (int c = 0; c < 2 * kNumClasses; ++c) {
     auto& v = by_class[c];
     if (v.empty()) continue;
     std::vector<int64_t> cost(v.size());
     for (size_t i = 0; i < v.size(); ++i)
-      cost[i] = (int64_t)((v[i].kv_end - v[i].kv_begin + kBlock - 1) / kBlock) * unit_cost(c);
+      cost[i] = (int64_t)((v[i].kv_end - v[i].kv_begin + kBlock - 1) / kBlock) * unit_cost(c % kNumClasses);
     std::vector<size_t> idx(v.size());
     std::iota(idx.begin(), idx.end(), 0);
     std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
     if (d->work_shuffle_seed)
       for (size_t i = idx.size(); i > 1; --i) std::swap(idx[i - 1], idx[splitmix64(rng) % i]);
     for (size_t i : idx) P.items.push_back(v[i]);
-    P.class_rows.push_back(kClassRows[c]);
+    P.class_rows.push_back(kClassRows[c % kNumClasses]);
+    P.class_cascade.push_back(c >= kNumClasses ? 1 : 0);
     P.class_begin.push_back((int32_t)P.items.size());
   }
 
@@ -364,10 +504,14 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.off_merge = align_up(P.off_items + P.items.size() * sizeof(pmattn_work_item), kAlign);
   P.off_row_mask = align_up(P.off_merge + P.merge_rows.size() * sizeof(pmattn_merge_row), kAlign);
   P.off_append = align_up(P.off_row_mask + P.row_mask.size() * sizeof(uint64_t), kAlign);
-  P.off_part_o = align_up(P.off_append + P.append_units.size() * sizeof(pmattn_append_unit), kAlign);
+  P.off_rec_index = align_up(P.off_append + P.append_units.size() * sizeof(pmattn_append_unit), kAlign);
+  P.off_vrow = align_up(P.off_rec_index + P.rec_index.size() * sizeof(int32_t), kAlign);
+  P.off_qv = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
+  const size_t elem = P.dtype == PMATTN_BF16 ? 2 : 4;
+  P.off_part_o = align_up(P.off_qv + P.vrow_src.size() * (size_t)P.hq * P.head_dim * elem, kAlign);
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
   P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
-  P.upload_blob.assign(P.off_part_o, 0);
+  P.upload_blob.assign(P.off_qv, 0);
   if (!P.items.empty())
     std::memcpy(P.upload_blob.data() + P.off_items, P.items.data(),
                 P.items.size() * sizeof(pmattn_work_item));
@@ -380,6 +524,10 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (!P.append_units.empty())
     std::memcpy(P.upload_blob.data() + P.off_append, P.append_units.data(),
                 P.append_units.size() * sizeof(pmattn_append_unit));
+  if (!P.rec_index.empty())
+    std::memcpy(P.upload_blob.data() + P.off_rec_index, P.rec_index.data(), P.rec_index.size() * sizeof(int32_t));
+  if (!P.vrow_src.empty())
+    std::memcpy(P.upload_blob.data() + P.off_vrow, P.vrow_src.data(), P.vrow_src.size() * sizeof(int32_t));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -442,6 +590,18 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->row_tree_mask = P.row_mask.empty() ? nullptr : P.row_mask.data();
   t->num_append_units = (int32_t)P.append_units.size();
   t->append_units = P.append_units.data();
+  t->class_cascade = P.class_cascade.data();
+  t->num_cascade = (int32_t)P.cascade_lo.size();
+  t->cascade_lo = P.cascade_lo.data();
+  t->cascade_hi = P.cascade_hi.data();
+  t->cascade_seq = P.cascade_seq.data();
+  t->cascade_row_begin = P.cascade_row_begin.data();
+  t->cascade_rows = P.cascade_rows.data();
+  t->cascade_splits = P.cascade_splits.data();
+  t->num_virtual_rows = (int32_t)P.vrow_src.size();
+  t->virtual_row_src = P.vrow_src.data();
+  t->num_rec_index = (int32_t)P.rec_index.size();
+  t->rec_index = P.rec_index.data();
   return PMATTN_OK;
 }
 

@@ -37,19 +37,24 @@ struct Plan {
   std::vector<int32_t> row_seq, row_pos;
   std::vector<int32_t> num_splits, split_offset, split_begin, split_end;
   std::vector<pmattn_work_item> items;
-  std::vector<int32_t> class_rows, class_begin;
+  std::vector<int32_t> class_rows, class_begin, class_cascade;
   std::vector<pmattn_merge_row> merge_rows;
   int32_t num_records = 0;
   // tree masks, one per row, present only when some sequence is a tree
   std::vector<uint64_t> row_mask;
+  // cascade (shared-prefix) virtual sequences, their rows, and the record
+  // lists of the rows they merge into
+  std::vector<int32_t> cascade_lo, cascade_hi, cascade_seq, cascade_row_begin, cascade_rows,
+      cascade_splits, vrow_src, rec_index;
   // KV append units; a non-empty message marks a target slot that another
   // sequence can see (or two rows write): the append refuses such a plan
   std::vector<pmattn_append_unit> append_units;
   std::string append_conflict;
-  // workspace layout (bytes):
-  // [items | merge rows | row masks | append units | partial O | partial lse]
-  size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_part_o = 0,
-         off_part_lse = 0, ws_bytes = 0;
+  // workspace layout (bytes): [items | merge rows | row masks | append units |
+  // record index | virtual row sources | gathered Q of virtual rows |
+  // partial O | partial lse]; everything before the gathered Q is uploaded
+  size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_rec_index = 0,
+         off_vrow = 0, off_qv = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 

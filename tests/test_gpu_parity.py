@@ -292,3 +292,51 @@ def test_forward_rejects_mis_sized_tensors():
     with pytest.raises(ValueError):
         pm.forward(p, dev["q"], dev["k"], dev["v"], dev["bt"], out,
                    workspace=torch.zeros(16, dtype=torch.uint8, device="cuda:0"))
+
+
+def _cascade_cases():
+    S = dict
+    nb = {"a": 4, "b": 2, "c": 3, "d": 1}
+    return {
+        # decode rows over nested shared runs, plus prefill and private rows
+        "nested-decode": (dict(hq=8, hkv=2, d=128), nb, 0, [
+            S(q_len=1, seq_len=130, nodes=["a", "b"]), S(q_len=1, seq_len=101, nodes=["a", "b"]),
+            S(q_len=1, seq_len=200, nodes=["a", "c"]), S(q_len=1, seq_len=97, nodes=["a"]),
+            S(q_len=5, seq_len=150, nodes=["a", "c"]), S(q_len=40, seq_len=140, q_start=100, nodes=["a", "c"]),
+            S(q_len=1, seq_len=300)]),
+        "verify-trees-splits": (dict(hq=8, hkv=2, d=128), nb, 3, [
+            S(q_len=6, seq_len=120, nodes=["a", "d"], tree=[-1, 0, 0, 1, 2, -1]),
+            S(q_len=12, seq_len=90, nodes=["a", "d"], tree=wl.random_tree(12, 4)),
+            S(q_len=1, seq_len=77, nodes=["a"]), S(q_len=1, seq_len=66, nodes=["a", "d"])]),
+        "g8-d64-many": (dict(hq=16, hkv=2, d=64), {"a": 6}, 0,
+                        [S(q_len=1, seq_len=100 + 7 * i, nodes=["a"]) for i in range(20)]),
+        "f32": (dict(hq=4, hkv=2, d=128, dtype="f32"), nb, 2, [
+            S(q_len=1, seq_len=100, nodes=["a", "b"]), S(q_len=2, seq_len=113, nodes=["a", "b"]),
+            S(q_len=1, seq_len=70, nodes=["a"])]),
+        "wide-group": (dict(hq=8, hkv=2, d=128), {"a": 8}, 0,
+                       [S(q_len=1, seq_len=129 + i, nodes=["a"]) for i in range(64)]),
+    }
+
+
+CASCADE = _cascade_cases()
+
+
+@pytest.mark.parametrize("name", sorted(CASCADE))
+def test_cascade_batches(name):
+    shape, nodes, splits, specs = CASCADE[name]
+    b = wl.custom(specs, node_blocks=nodes, seed=zlib.crc32(name.encode()) % 1000, num_kv_splits=splits,
+                  name="cascade-" + name, extra_blocks=2, **shape)
+    note(f"cascade case {name}: rows={b.num_rows}")
+    p = make_plan(b, cascade=1)
+    assert p.tables()["cascade"]["lo"].shape[0] > 0
+    out, lse = run_gpu(b, cascade=1)
+    compare(b, out, lse)
+
+
+def test_cascade_full_config5_and_order():
+    b = wl.config(5)
+    dev = to_device(b)
+    out, lse = run_gpu(b, dev, cascade=1)
+    compare(b, out, lse)
+    o2, l2 = run_gpu(b, dev, cascade=1, work_shuffle_seed=5)
+    assert np.array_equal(o2, out) and np.array_equal(l2, lse)

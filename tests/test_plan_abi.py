@@ -17,10 +17,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def make_plan(b, **kw):
+    """A plan of ``b``; the cascade is off unless asked for (cascade plans are
+    checked against the replica by ``_check_cascade_plan``)."""
     return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table, num_pool_blocks=b.num_pool_blocks,
                    num_q_heads=b.num_q_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
                    dtype=b.dtype, scale=b.scale, num_kv_splits=kw.pop("num_kv_splits", b.num_kv_splits),
-                   tree_parent=kw.pop("tree_parent", b.tree_parent), **kw)
+                   tree_parent=kw.pop("tree_parent", b.tree_parent), cascade=kw.pop("cascade", 0), **kw)
 
 
 def check_plan(b, p, num_cus=0):
@@ -269,6 +271,80 @@ def test_append_refuses_shared_target_slots():
     b5 = b.replace(q_start=np.array([5, 5], np.int32), seq_len=np.array([6, 6], np.int32))
     st, msg = _append_status(make_plan(b5))
     assert st == _lib.E_INVALID and "same pool slot" in msg
+
+
+def _check_cascade_plan(b, t, num_kv_splits=0, num_cus=0, mode=1):
+    grp = b.num_q_heads // b.num_kv_heads
+    rep = R.plan_units(b.q_len, b.q_start, b.block_table, b.num_kv_heads, grp, num_kv_splits, num_cus,
+                       cascade=mode)
+    units = rep["units"]
+    nb = b.num_seqs
+    virt = units[nb:]
+    assert t["cascade"]["lo"].tolist() == [u["lo"] for u in virt]
+    assert t["cascade"]["hi"].tolist() == [u["hi"] for u in virt]
+    assert t["cascade"]["seq"].tolist() == [u["seq"] for u in virt]
+    assert t["cascade"]["row_begin"].tolist() == [u["row0"] for u in virt]
+    assert t["cascade"]["rows"].tolist() == [u["rows"] for u in virt]
+    assert t["cascade"]["splits"].tolist() == [u["splits"] for u in virt]
+    assert np.array_equal(t["virtual_row_src"], rep["vrow_src"])
+    assert t["num_splits"].tolist() == [u["splits"] for u in units[:nb]]
+    lo = [x for u in units[:nb] for x, _ in u["bounds"]]
+    hi = [x for u in units[:nb] for _, x in u["bounds"]]
+    assert t["split_begin"].tolist() == lo and t["split_end"].tolist() == hi
+    R.check_coverage_cascade(t["items"], t["class_cascade"], t["class_begin"], t["virtual_row_src"],
+                             b.q_len, b.q_start, b.num_kv_heads)
+    # every output (row, head) is written once directly or merged once, and a
+    # merge row's records are exactly those its tasks write
+    written = {}
+    for c in range(len(t["class_rows"])):
+        for it in t["items"][t["class_begin"][c]:t["class_begin"][c + 1]]:
+            seq, kvh, r0, nt, p0, lo_, hi_, part = (int(x) for x in it[:8])
+            for tt in range(nt):
+                row = int(t["virtual_row_src"][r0 + tt]) if t["class_cascade"][c] else r0 + tt
+                for i in range(grp):
+                    key = (row, kvh * grp + i)
+                    written.setdefault(key, []).append(None if part < 0 else part + tt * grp + i)
+    merged = set()
+    for rec0, stride, npart, row, qh in t["merge_rows"]:
+        recs = (t["rec_index"][rec0:rec0 + npart].tolist() if stride < 0
+                else [rec0 + k * stride for k in range(npart)])
+        assert sorted(recs) == sorted(written[(int(row), int(qh))]), (row, qh)
+        merged.add((int(row), int(qh)))
+    for key, recs in written.items():
+        assert (None in recs) == (key not in merged) and (len(recs) == 1 or key in merged)
+
+
+@pytest.mark.parametrize("cfg", [1, 4, 5, 7])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_cascade_plans_match_replica(cfg, mode):
+    b = wl.config(cfg, values=False)
+    t = make_plan(b, cascade=mode).tables()
+    # mode 1 groups every shared run; the automatic mode leaves out the pairs
+    # of the long-decode batch and the tiny batch
+    assert (t["cascade"]["lo"].shape[0] > 0) == (mode == 1 or cfg in (4, 7))
+    _check_cascade_plan(b, t, b.num_kv_splits, mode=mode)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_cascade_random_batches(seed):
+    rng = np.random.Generator(np.random.PCG64(300 + seed))
+    nodes = {("n", k): int(rng.integers(1, 6)) for k in range(6)}
+    seqs = []
+    for _ in range(int(rng.integers(2, 14))):
+        path = [("n", 0)] + [("n", int(k)) for k in sorted(rng.choice(np.arange(1, 6), size=int(rng.integers(0, 3)),
+                                                                       replace=False))]
+        shared = sum(nodes[n] for n in path) * 16
+        ql = int(rng.choice([1, 1, 2, 5, 20, 40]))
+        extra = int(rng.integers(0, 50))
+        seqs.append(dict(q_len=ql, seq_len=shared + extra + ql, nodes=path))
+    b = wl.custom(seqs, node_blocks=nodes, hq=8, hkv=2, d=64, values=False)
+    for splits in (0, 3):
+        bb = b.replace(num_kv_splits=splits)
+        _check_cascade_plan(bb, make_plan(bb, cascade=1).tables(), splits)
+        _check_cascade_plan(bb, make_plan(bb, cascade=2).tables(), splits, mode=2)
+    # with the cascade off, the unit rules reproduce the plain tables
+    rep = R.plan_units(b.q_len, b.q_start, b.block_table, b.num_kv_heads, 4)
+    assert [u["splits"] for u in rep["units"]] == R.num_splits(b.q_len, b.q_start, b.num_kv_heads, 4).tolist()
 
 
 def test_unused_table_entries_are_not_validated():

@@ -263,6 +263,7 @@ CONFIG_NAMES = {
     4: "mixed-prefill-decode-verify-radix",
     5: "long-decode-8x32k-paired-turns",
     6: "tree-verify-64seq-32node",
+    7: "shared-prompt-decode-128seq-8k",
 }
 
 
@@ -303,6 +304,14 @@ def config(idx: int, seed: Optional[int] = None, values: bool = True) -> Batch:
         b = _assemble(name, seqs, {}, hq=32, hkv=8, d=128, dtype="bf16", rng=rng, **kw)
         parents = [p for t in tree_seeds for p in random_tree(32, int(t), max_depth=6)]
         return b.replace(tree_parent=np.array(parents, dtype=np.int32))
+    if idx == 7:
+        # Many requests on one long shared prompt (the SGLang review's few-shot /
+        # system-prompt sharing, at decode time): 128 sequences share an
+        # 8,192-token prefix, each with a private tail U{128..1024}, one decode
+        # row each; 32/8 heads, d 128.
+        tail = rng.integers(128, 1024, size=128, endpoint=True)
+        seqs = [dict(q_len=1, seq_len=8192 + int(t), q_start=8192 + int(t) - 1, nodes=["prompt"]) for t in tail]
+        return _assemble(name, seqs, {"prompt": 512}, hq=32, hkv=8, d=128, dtype="bf16", rng=rng, **kw)
     raise KeyError(idx)
 
 
