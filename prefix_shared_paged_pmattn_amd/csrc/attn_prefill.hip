@@ -25,10 +25,18 @@
 //   every row of the task take an unmasked path (Figure 11, mask-aware
 //   computation); V lanes of keys past the task's end are zeroed when the chunk
 //   is staged, so pool slots no row can see may hold NaN.
-// * Three waves per SIMD (168 VGPRs, 37 KiB of LDS per workgroup), so that
-//   LDS latency and one wave's softmax VALU hide behind the other waves' MFMA.
-//   Measured on the few-shot workload: 32-key chunks at 3 waves/SIMD beat
-//   64-key chunks at 2 waves/SIMD by 9%; 4 waves/SIMD spills.
+// * Occupancy is a template parameter: three waves per SIMD (168 VGPRs, 37
+//   KiB of LDS per workgroup) when the workgroup tasks have the chip to
+//   themselves, so that LDS latency and one wave's softmax VALU hide behind
+//   the other waves' MFMA; two when one-wave tasks of the same plan run
+//   beside them, and for token trees (whose masks spill at three). Measured:
+//   few-shot prefill 907 vs 813 TFLOP/s (3 vs 2), mixed batch 0.78 vs 0.84
+//   ms (2 vs 3), tree verify 2 waves 19% faster. 64-key chunks at 2 waves
+//   were 3% slower than 32-key ones.
+// * The register staging of the next chunk uses clang vector types: with
+//   HIP's uint4 the copies are memcpys of a union, the staging array stays
+//   in private memory and the backend moves it to LDS, so every chunk's loads
+//   were waited for right after issue (15% of the few-shot time).
 #include "attn_kernels.h"
 
 namespace pmattn {
@@ -40,14 +48,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleLog2 = 8.0f;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const int32_t __attribute__((address_space(4)))* cint_p;
 
 // Tuning knobs (compile-time); the defaults are the measured best.
 #ifndef PMATTN_PF_CHUNK
 #define PMATTN_PF_CHUNK 32
-#endif
-#ifndef PMATTN_PF_WAVES
-#define PMATTN_PF_WAVES 3
 #endif
 #ifndef PMATTN_PF_TILE_OUTER
 #define PMATTN_PF_TILE_OUTER 1
@@ -96,11 +102,24 @@ __device__ __forceinline__ pmattn_work_item load_item(const pmattn_work_item* it
 // carries PIECES 16-byte pieces of K and of V; consecutive threads read
 // consecutive 16-byte pieces of a block, so every wave load is 1 KiB
 // contiguous.
+// (clang vector types, not HIP's uint4: copies of the latter are memcpys of a
+// union that keep the array in private memory, which the backend then moves
+// to LDS.)
 template <int D>
 struct Stage {
-  uint4 k[Cfg<D>::PIECES];
-  uint4 v[Cfg<D>::PIECES];
+  u32x4 k[Cfg<D>::PIECES];
+  u32x4 v[Cfg<D>::PIECES];
 };
+
+// blk[b] for a per-thread b, as selects (a dynamic index would put blk in
+// private memory)
+template <int N>
+__device__ __forceinline__ int pick(const int (&blk)[N], int b) {
+  int r = blk[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = b == i ? blk[i] : r;
+  return r;
+}
 
 template <int D>
 __device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restrict__ kpool,
@@ -111,11 +130,11 @@ __device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restr
   for (int u = 0; u < P; ++u) {
     const int q = tid + 256 * u;
     const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-    const int64_t base = (int64_t)blk[b] * hkv + kvh;
+    const int64_t base = (int64_t)pick(blk, b) * hkv + kvh;
     // grouped K block [D/8][16 tokens][8]: channel group r / 16, token r % 16
-    st.k[u] = *reinterpret_cast<const uint4*>(kpool + base * 16 * D + 8 * r);
+    st.k[u] = *reinterpret_cast<const u32x4*>(kpool + base * 16 * D + 8 * r);
     // V block [D][16 tokens]: channel r / 2, half r % 2
-    st.v[u] = *reinterpret_cast<const uint4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
+    st.v[u] = *reinterpret_cast<const u32x4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
   }
 }
 
@@ -149,8 +168,8 @@ __device__ __forceinline__ void stage_store(uint16_t* lds, Stage<D>& st, int c0,
   for (int u = 0; u < P; ++u) {
     const int q = tid + 256 * u;
     const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-    *reinterpret_cast<uint4*>(kl + (16 * b + r % 16) * Cfg<D>::KROW + 8 * (r / 16)) = st.k[u];
-    *reinterpret_cast<uint4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = st.v[u];
+    *reinterpret_cast<u32x4*>(kl + (16 * b + r % 16) * Cfg<D>::KROW + 8 * (r / 16)) = st.k[u];
+    *reinterpret_cast<u32x4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = st.v[u];
   }
 }
 
@@ -310,8 +329,8 @@ __device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 
 #endif
 }
 
-template <int D, bool TREE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PMATTN_PF_WAVES, PMATTN_PF_WAVES)))
+template <int D, bool TREE, int WAVES>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void attn_prefill_kernel(AttnArgs a) {
   constexpr int KSTEPS = D / 16, DT = D / 32, CHUNK = Cfg<D>::CHUNK;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
@@ -421,17 +440,20 @@ void attn_prefill_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st) {
-  if (a.item_count <= 0) return hipSuccess;
+namespace {
+template <int D>
+void launch_d(const AttnArgs& a, bool concurrent, hipStream_t st) {
   const dim3 grid(a.item_count), block(256);
-  const bool tree = a.row_mask != nullptr;
-  if (head_dim == 128) {
-    if (tree) hipLaunchKernelGGL((attn_prefill_kernel<128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<128, false>), grid, block, 0, st, a);
-  } else {
-    if (tree) hipLaunchKernelGGL((attn_prefill_kernel<64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_prefill_kernel<64, false>), grid, block, 0, st, a);
-  }
+  if (a.row_mask) hipLaunchKernelGGL((attn_prefill_kernel<D, true, 2>), grid, block, 0, st, a);
+  else if (concurrent) hipLaunchKernelGGL((attn_prefill_kernel<D, false, 2>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((attn_prefill_kernel<D, false, 3>), grid, block, 0, st, a);
+}
+}  // namespace
+
+hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, bool concurrent, hipStream_t st) {
+  if (a.item_count <= 0) return hipSuccess;
+  if (head_dim == 128) launch_d<128>(a, concurrent, st);
+  else launch_d<64>(a, concurrent, st);
   return hipGetLastError();
 }
 

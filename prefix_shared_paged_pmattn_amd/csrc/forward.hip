@@ -123,6 +123,9 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
                                       (int)P.vrow_src.size(), row_bytes, qv, st);
     if (e != hipSuccess) return hip_fail(e, "row gather kernel launch");
   }
+  bool has_wg = false, has_wave = false;
+  for (int32_t rows : P.class_rows) (rows > kMaxWaveRows ? has_wg : has_wave) = true;
+  const bool concurrent = P.dtype == PMATTN_BF16 && has_wg && has_wave;
   auto launch_class = [&](size_t c, hipStream_t s) -> hipError_t {
     AttnArgs ac = a;
     ac.items = items + P.class_begin[c];
@@ -134,12 +137,10 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
       ac.row_mask = nullptr;
     }
     if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);
-    if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
+    if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, concurrent, s);
     return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, s);
   };
-  bool has_wg = false, has_wave = false;
-  for (int32_t rows : P.class_rows) (rows > kMaxWaveRows ? has_wg : has_wave) = true;
-  if (!(P.dtype == PMATTN_BF16 && has_wg && has_wave)) {
+  if (!concurrent) {
     for (size_t c = 0; c < P.class_rows.size(); ++c) {
       hipError_t e = launch_class(c, st);
       if (e != hipSuccess) return hip_fail(e, "attention kernel launch");

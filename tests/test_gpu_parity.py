@@ -45,6 +45,11 @@ def _batch_cases():
         "prefill-mha-long": (dict(hq=2, hkv=2, d=128), [S(q_len=200, seq_len=260, q_start=60)], 0),
         "prefill-d64-g8": (dict(hq=16, hkv=2, d=64), [S(q_len=33, seq_len=50, q_start=17), S(q_len=9, seq_len=9)], 0),
         "prefill-wg-tail-in-first-chunk": (dict(hq=8, hkv=2, d=128), [S(q_len=20, seq_len=23, q_start=3)], 0),
+        # workgroup tasks whose last waves hold few or no rows; a run of whole
+        # tasks followed by a one-token tail; d = 64 with rows a multiple of 128
+        "prefill-wg-sparse-waves": (dict(hq=8, hkv=1, d=128), [S(q_len=17, seq_len=300, q_start=283),
+                                                                 S(q_len=33, seq_len=33)], 0),
+        "prefill-wg-d64-exact": (dict(hq=4, hkv=1, d=64), [S(q_len=64, seq_len=100, q_start=36)], 2),
         # wave and workgroup tasks in one plan (run concurrently on two streams)
         "mixed-classes": (dict(hq=8, hkv=2, d=128), [S(q_len=50, seq_len=300, q_start=250), S(q_len=1, seq_len=700),
                                                      S(q_len=5, seq_len=405), S(q_len=1, seq_len=33),
