@@ -44,6 +44,7 @@ struct MergeArgs {
   int32_t hq;                    // heads per output row
   int32_t implicit_parts;        // implicit layout: P
   int32_t implicit_rows;         // implicit layout: rows
+  int32_t max_parts;             // largest partial count of any output (kernel choice)
 };
 
 struct AppendArgs {

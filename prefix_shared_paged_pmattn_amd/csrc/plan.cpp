@@ -499,6 +499,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     P.class_begin.push_back((int32_t)P.items.size());
   }
 
+  for (const pmattn_merge_row& mr : P.merge_rows) P.merge_max_parts = std::max(P.merge_max_parts, mr.nparts);
+
   // ---- workspace layout and the upload image --------------------------------
   P.off_items = 0;
   P.off_merge = align_up(P.off_items + P.items.size() * sizeof(pmattn_work_item), kAlign);

@@ -39,6 +39,7 @@ struct Plan {
   std::vector<pmattn_work_item> items;
   std::vector<int32_t> class_rows, class_begin, class_cascade;
   std::vector<pmattn_merge_row> merge_rows;
+  int32_t merge_max_parts = 0;  // largest nparts of any merge row
   int32_t num_records = 0;
   // tree masks, one per row, present only when some sequence is a tree
   std::vector<uint64_t> row_mask;
