@@ -26,7 +26,7 @@ MAX_WAVE_ROWS = 64
 MAX_TASK_ROWS = 128
 CLASS_ROWS = (16, 32, 64, 128)
 TASKS_PER_CU = 32
-WG_TASKS_PER_CU = 4
+WG_TASKS_PER_2CU = 3  # 1.5 workgroup tasks per CU
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
 
@@ -150,7 +150,7 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
     sequence with rows. Automatic: a task over n blocks costs n * (2 + rows/16)
     block units. Wave tasks (<= 64 rows) and workgroup tasks (128 rows) are
     balanced separately: each kind's quantum is its total cost over
-    (CUs x 32) wave tasks or (CUs x 4) workgroup tasks, at least 48 units; a
+    (CUs x 32) wave tasks or (CUs x 1.5) workgroup tasks, at least 48 units; a
     sequence gets ceil(cost of its largest tile / its kind's quantum)
     partitions, at most 64 and at most its number of blocks."""
     q_len = np.asarray(q_len, np.int64)
@@ -170,7 +170,7 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
         kind[s] = k
     cus = num_cus if num_cus > 0 else 256
     quantum = [max(MIN_QUANTUM, -(-total[k] // t)) for k, t in ((0, cus * TASKS_PER_CU),
-                                                                (1, cus * WG_TASKS_PER_CU))]
+                                                                (1, cus * WG_TASKS_PER_2CU // 2))]
     for s in range(q_len.shape[0]):
         if q_len[s] == 0:
             continue
@@ -354,7 +354,7 @@ def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0
                 u["kind"] = k
         cus = num_cus if num_cus > 0 else 256
         quantum = [max(MIN_QUANTUM, -(-total[0] // (cus * TASKS_PER_CU))),
-                   max(MIN_QUANTUM, -(-total[1] // (cus * WG_TASKS_PER_CU)))]
+                   max(MIN_QUANTUM, -(-total[1] // (cus * WG_TASKS_PER_2CU // 2)))]
         for u in units:
             nblk = -(-(u["hi"] - u["lo"]) // BLOCK)
             u["splits"] = max(1, min(-(-u["last"] // quantum[u["kind"]]), MAX_AUTO_SPLITS, nblk)) if u["rows"] else 0
