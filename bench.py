@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--num-kv-splits", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
+    ap.add_argument("--work-shuffle-seed", type=int, default=0,
+                    help="launch the tasks of each class in a seeded random order (0: cost order)")
     ap.add_argument("--cascade", type=int, choices=(0, 1, 2), default=2,
                     help="shared-prefix cascade for decode/verify rows (plan option): 0 off, "
                          "1 every shared run, 2 automatic")
@@ -288,7 +290,8 @@ def main():
                        num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
                        num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
                        scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus,
-                       tree_parent=b.tree_parent, cascade=args.cascade)
+                       work_shuffle_seed=args.work_shuffle_seed, tree_parent=b.tree_parent,
+                       cascade=args.cascade)
 
     if args.op == "append":
         return bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt)
@@ -375,7 +378,7 @@ def main():
         achieved = work["bytes"] / (ms_task * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=achieved / HBM_PEAK_GBS,
-                    traffic=None if args.num_kv_splits is not None or args.num_cus or args.cascade != 2
+                    traffic=None if args.num_kv_splits is not None or args.num_cus or args.work_shuffle_seed or args.cascade != 2
                     else measured_traffic(args.config))
     log(f"[bench] value {value:.1f} {unit}; dominant kernel (tasks pass) {achieved:.1f} {roof['unit']} "
         f"= {100 * roof['frac']:.1f}% of {roof['bound']} peak")

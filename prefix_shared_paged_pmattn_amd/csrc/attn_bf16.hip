@@ -36,6 +36,7 @@
 // lanes are zeroed before the PV product, so pool slots no row can see may
 // hold NaN (virtual padding, "Assumptions & free parameters").
 #include "attn_kernels.h"
+#include "plan_internal.h"
 
 namespace pmattn {
 namespace {
@@ -231,8 +232,9 @@ struct Depth {
 };
 
 // Tasks are independent; a workgroup holds four of them, one per wave (1- and
-// 2-wave workgroups measured the same or slower on the decode workloads).
-constexpr int kWavesPerWg = 4;
+// 2-wave workgroups measured the same or slower on the decode workloads). The
+// planner's dispatch order groups tasks by this count.
+constexpr int kWavesPerWg = kWaveTasksPerWg;
 
 template <int D, int NT, bool TREE>
 __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))

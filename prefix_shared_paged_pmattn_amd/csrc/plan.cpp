@@ -27,6 +27,39 @@ namespace {
 thread_local std::string g_last_error;
 std::atomic<uint64_t> g_next_plan_id{1};
 
+// XCD-aware dispatch order. K/V of (block, kv head) is read only by tasks of
+// that kv head, so all tasks of one kv head go to one XCD (kv heads spread
+// over several XCDs when there are fewer than kXcds, by sequence): every task
+// that reads a shared block finds it in the same L2. Each XCD keeps its tasks
+// in the given (cost-descending) order; workgroup slot i, which the hardware
+// gives to XCD i % kXcds, takes the next `per_wg` tasks of that XCD, topped up
+// from the XCD with the most tasks left once that one runs out (so that every
+// slot but the last holds exactly per_wg tasks).
+std::vector<size_t> xcd_order(const std::vector<pmattn_work_item>& v, const std::vector<size_t>& order,
+                              int per_wg, int hkv) {
+  const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;  // XCDs per kv head
+  std::vector<std::vector<size_t>> q(kXcds);
+  for (size_t i : order) {
+    const pmattn_work_item& it = v[i];
+    const int x = (hkv >= kXcds ? it.kv_head : it.kv_head * rep + it.seq % rep) % kXcds;
+    q[x].push_back(i);
+  }
+  std::vector<size_t> head(kXcds, 0), out;
+  out.reserve(order.size());
+  for (size_t slot = 0; out.size() < order.size(); ++slot) {
+    int x = (int)(slot % kXcds);
+    for (int k = 0; k < per_wg && out.size() < order.size(); ++k) {
+      if (head[x] == q[x].size()) {
+        size_t best = 0;
+        for (int y = 0; y < kXcds; ++y)
+          if (q[y].size() - head[y] > best) best = q[y].size() - head[y], x = y;
+      }
+      out.push_back(q[x][head[x]++]);
+    }
+  }
+  return out;
+}
+
 // Cost model for ordering and automatic splitting, in "block units": a task
 // over n KV blocks costs n * (2 + rows/16). The constant 2 stands for the
 // K/V stream of each block, the rows/16 term for its MFMA column tiles.
@@ -494,6 +527,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     std::vector<size_t> idx(v.size());
     std::iota(idx.begin(), idx.end(), 0);
     std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
+    idx = xcd_order(v, idx, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1,
+                    d->num_kv_heads);
     if (d->work_shuffle_seed)
       for (size_t i = idx.size(); i > 1; --i) std::swap(idx[i - 1], idx[splitmix64(rng) % i]);
     for (size_t i : idx) P.items.push_back(v[i]);

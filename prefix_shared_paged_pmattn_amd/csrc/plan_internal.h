@@ -21,6 +21,11 @@ constexpr int kMaxWaveRows = 64;
 constexpr int kMaxTaskRows = 128;
 constexpr int kNumClasses = 4;
 constexpr int kClassRows[kNumClasses] = {16, 32, 64, 128};
+// One-wave tasks run kWaveTasksPerWg to a workgroup (attn_bf16.hip).
+constexpr int kWaveTasksPerWg = 4;
+// Workgroups are dealt to the XCDs (accelerator dies, each with its own L2)
+// round-robin in workgroup order: workgroup i runs on XCD i % kXcds.
+constexpr int kXcds = 8;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxTreeRows = 64;
 constexpr size_t kAlign = 256;

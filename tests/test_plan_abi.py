@@ -106,14 +106,45 @@ def test_shuffle_changes_order_not_content():
     check_plan(b, make_plan(b, work_shuffle_seed=1234))
 
 
-def test_cost_order_is_descending_within_class():
-    b = wl.config(2, values=False)
+def _xcd_of(kv_head, seq, hkv, xcds=8):
+    """The XCD a task's kv head (and sequence) is meant for."""
+    if hkv >= xcds:
+        return kv_head % xcds
+    rep = -(-xcds // hkv)
+    return (kv_head * rep + seq % rep) % xcds
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_dispatch_order_is_xcd_aware_and_cost_descending(cfg):
+    """Workgroup slot i runs on XCD i % 8; every task of a kv head lands on that
+    head's XCD, except where a workgroup is topped up from another XCD at the
+    end of a queue (at most one workgroup per XCD here, since these workloads
+    give every kv head the same number of tasks), and each XCD's own tasks come
+    in non-increasing cost."""
+    b = wl.config(cfg, values=False)
     t = make_plan(b).tables()
     it = t["items"]
     for c in range(t["class_rows"].shape[0]):
-        blk = -(-(it[t["class_begin"][c]:t["class_begin"][c + 1], 6]
-                  - it[t["class_begin"][c]:t["class_begin"][c + 1], 5]) // 16)
-        assert (np.diff(blk) <= 0).all()
+        cls = it[t["class_begin"][c]:t["class_begin"][c + 1]]
+        per_wg = 4 if t["class_rows"][c] <= 64 else 1
+        slot_xcd = (np.arange(cls.shape[0]) // per_wg) % 8
+        want = np.array([_xcd_of(int(h), int(s_), b.num_kv_heads) for s_, h in zip(cls[:, 0], cls[:, 1])])
+        assert (slot_xcd != want).sum() <= 8 * per_wg
+        blk = -(-(cls[:, 6] - cls[:, 5]) // 16)
+        for x in range(8):
+            assert (np.diff(blk[want == x]) <= 0).all()
+
+
+def test_dispatch_order_with_few_kv_heads_is_a_permutation():
+    b = wl.custom([dict(q_len=1, seq_len=n) for n in (40, 300, 77, 1000, 5)], hq=8, hkv=2, d=128)
+    t = make_plan(b).tables()
+    it = t["items"]
+    # two kv heads: each spreads over 4 XCDs by sequence; the list still holds every task once
+    u = make_plan(b, work_shuffle_seed=99).tables()["items"]
+    assert sorted(map(tuple, it[:, :7].tolist())) == sorted(map(tuple, u[:, :7].tolist()))
+    first = it[: min(8 * 4, it.shape[0])]
+    xs = {_xcd_of(int(h), int(s_), 2) for s_, h in zip(first[:, 0], first[:, 1])}
+    assert len(xs) > 2  # more than one XCD per kv head is used
 
 
 def test_workspace_bytes():
