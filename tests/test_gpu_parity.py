@@ -161,6 +161,33 @@ def test_full_config4_sampled_rows():
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
+def test_full_config6_tree_verify_sampled_rows():
+    """The token-tree verify workload at full size, as bench.py launches it."""
+    b = wl.config(6)
+    off = b.row_offsets()
+    rng = np.random.Generator(np.random.PCG64(66))
+    seqs = rng.choice(len(b.q_len), 4, replace=False)
+    rows = np.unique(np.concatenate([np.arange(int(off[s]), int(off[s + 1])) for s in seqs] +
+                                    [rng.choice(b.num_rows, 32, replace=False)]))
+    note(f"config 6: {b.num_rows} rows, sampling {rows.size} (whole trees of sequences {sorted(seqs.tolist())})")
+    out, lse = run_gpu(b)
+    compare(b, out, lse, rows=rows)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_full_config7_shared_prompt_cascade_sampled_rows():
+    """The shared-prompt decode workload at full size with the automatic cascade."""
+    b = wl.config(7)
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = np.unique(np.concatenate([[0, b.num_rows - 1], rng.choice(b.num_rows, 14, replace=False)]))
+    p = make_plan(b)
+    assert p.tables()["cascade"]["lo"].shape[0] > 0, "the prompt should form a cascade group"
+    note(f"config 7: {b.num_rows} rows, sampling {rows.size}")
+    out, lse = run_gpu(b)
+    compare(b, out, lse, rows=rows)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
 def test_poison_in_invisible_slots_changes_nothing():
     b = wl.custom([dict(q_len=1, seq_len=37), dict(q_len=5, seq_len=50, q_start=41),
                    dict(q_len=20, seq_len=33, q_start=2), dict(q_len=3, seq_len=90, q_start=10)],
