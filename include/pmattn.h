@@ -228,6 +228,13 @@ typedef struct pmattn_plan_tables {
   const int32_t* virtual_row_src;   /* [num_virtual_rows] the real query row of each */
   int32_t num_rec_index;
   const int32_t* rec_index;         /* record ids of indirect merge rows */
+  /* Equal-work decode plans (every task a decode wave task, automatic splits,
+   * bf16, no cascade): the KV blocks of all sequences, laid end to end, are
+   * cut into equal pieces; wave w of the single class runs tasks
+   * [slot_begin[w], slot_begin[w + 1]) one after another. 0 / NULL otherwise
+   * (one task per wave). */
+  int32_t num_slots;
+  const int32_t* slot_begin;        /* [num_slots + 1] */
 } pmattn_plan_tables;
 
 /* Build a plan on the host. Validates the batch (see pmattn_plan_desc),

@@ -10,7 +10,8 @@ is checked against this file in two ways:
   number of KV partitions per sequence and their bounds) must match
   bit-exactly; the partition count rule and the token tiling restate the
   library's documented policy, the partition bounds follow the split-KV
-  reading in ``attention.partition_bounds``;
+  reading in ``attention.partition_bounds``, except in equal-work decode
+  plans (``stream_bounds``), whose cut points are the library's policy too;
 * the work list itself may come in any order, so it is checked by coverage:
   every (query row, query head, visible key) triple is covered by exactly one
   task and no task covers an invisible one.
@@ -29,6 +30,38 @@ TASKS_PER_CU = 32
 WG_TASKS_PER_2CU = 3  # 1.5 workgroup tasks per CU
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
+STREAM_WAVES_PER_CU = 4
+STREAM_MIN_BLOCKS = 16
+
+
+def stream_applies(q_len, group, dtype="bf16", num_kv_splits=0, virtual_units=0):
+    """Equal-work decode plans: bf16, automatic splits, no cascade group, and
+    every sequence with rows a single 16-row tile (q_len * G <= 16)."""
+    q_len = np.asarray(q_len, np.int64)
+    return (dtype == "bf16" and num_kv_splits == 0 and virtual_units == 0 and bool((q_len > 0).any())
+            and bool((q_len[q_len > 0] * group <= CLASS_ROWS[0]).all()))
+
+
+def stream_bounds(lo, hi, rows, num_kv_heads, num_cus=0):
+    """Partition bounds of every unit (key ranges [lo, hi), ``rows`` > 0 for
+    units with work) in an equal-work decode plan. The units' blocks are laid
+    end to end in unit order; pieces of L blocks, L = max(16, ceil(total /
+    (CUs x 4 / Hkv))), cut them; a unit's partitions are its parts of the
+    pieces it meets. Returns one list of (begin, end) per unit."""
+    nblk = [-(-(int(h) - int(l)) // BLOCK) if r > 0 else 0 for l, h, r in zip(lo, hi, rows)]
+    total = sum(nblk)
+    cus = num_cus if num_cus > 0 else 256
+    per_head = max(1, cus * STREAM_WAVES_PER_CU // num_kv_heads)
+    L = max(STREAM_MIN_BLOCKS, -(-total // per_head))
+    out, start = [], 0
+    for l, h, n in zip(lo, hi, nblk):
+        b = []
+        if n:
+            cuts = [0] + [c - start for c in range((start // L + 1) * L, start + n, L)] + [n]
+            b = [(min(int(l) + x * BLOCK, int(h)), min(int(l) + y * BLOCK, int(h))) for x, y in zip(cuts, cuts[1:])]
+        out.append(b)
+        start += n
+    return out
 
 
 def row_tables(q_len, q_start):
@@ -145,7 +178,7 @@ def token_tiles(q_len, q_start, group):
     return tiles
 
 
-def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
+def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0, dtype="bf16"):
     """KV partitions per sequence. Explicit: the requested count for every
     sequence with rows. Automatic: a task over n blocks costs n * (2 + rows/16)
     block units. Wave tasks (<= 64 rows) and workgroup tasks (128 rows) are
@@ -159,6 +192,9 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
     if num_kv_splits > 0:
         out[q_len > 0] = num_kv_splits
         return out
+    if stream_applies(q_len, group, dtype):
+        bounds = stream_bounds(np.zeros_like(q_start), q_start + q_len, q_len, num_kv_heads, num_cus)
+        return np.array([len(b) for b in bounds], np.int32)
     total = [0, 0]
     last = np.zeros(q_len.shape[0], np.int64)
     kind = np.zeros(q_len.shape[0], np.int64)
@@ -179,13 +215,26 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0):
     return out
 
 
-def split_ranges(q_len, q_start, splits):
-    """Concatenated [begin, end) of every sequence's partitions."""
+def seq_bounds(q_len, q_start, num_kv_heads, group, splits, num_cus=0, dtype="bf16", num_kv_splits=0):
+    """Every sequence's partition bounds: ``stream_bounds`` in equal-work
+    decode plans, ``partition_bounds`` (equal block chunks) otherwise."""
+    q_len = np.asarray(q_len, np.int64)
+    q_start = np.asarray(q_start, np.int64)
+    if stream_applies(q_len, group, dtype, num_kv_splits):
+        return [np.array(b, np.int64).reshape(-1, 2)
+                for b in stream_bounds(np.zeros_like(q_start), q_start + q_len, q_len, num_kv_heads, num_cus)]
+    return [partition_bounds(int(q_start[s] + q_len[s]), int(p)) if p else np.zeros((0, 2), np.int64)
+            for s, p in enumerate(splits)]
+
+
+def split_ranges(q_len, q_start, splits, bounds=None):
+    """Concatenated [begin, end) of every sequence's partitions (``bounds``:
+    per-sequence bounds from ``seq_bounds``; default equal chunks)."""
     lo, hi = [], []
     for s, p in enumerate(splits):
         if p == 0:
             continue
-        pb = partition_bounds(int(q_start[s] + q_len[s]), int(p))
+        pb = bounds[s] if bounds is not None else partition_bounds(int(q_start[s] + q_len[s]), int(p))
         lo.append(pb[:, 0])
         hi.append(pb[:, 1])
     if not lo:
@@ -193,14 +242,14 @@ def split_ranges(q_len, q_start, splits):
     return np.concatenate(lo).astype(np.int32), np.concatenate(hi).astype(np.int32)
 
 
-def expected_tasks(q_len, q_start, num_kv_heads, group, splits):
+def expected_tasks(q_len, q_start, num_kv_heads, group, splits, bounds=None):
     """The set of tasks (seq, kv_head, row_begin, n_tok, pos_begin, kv_begin,
     kv_end): every tile x kv head x non-empty partition, the partition clipped
     to the tile's last position."""
     first = np.concatenate([[0], np.cumsum(np.asarray(q_len, np.int64))[:-1]])
     tasks = set()
     for s, t0, nt, _, kv_end in token_tiles(q_len, q_start, group):
-        pb = partition_bounds(int(q_start[s] + q_len[s]), int(splits[s]))
+        pb = bounds[s] if bounds is not None else partition_bounds(int(q_start[s] + q_len[s]), int(splits[s]))
         for g in range(num_kv_heads):
             for lo, hi in pb:
                 hi = min(int(hi), kv_end)
@@ -304,7 +353,7 @@ def cascade_groups(q_len, q_start, block_table, group, mode=1):
 
 
 def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0, num_cus=0,
-               cascade=False):
+               cascade=False, dtype="bf16"):
     """Units of work (real sequences, then cascade groups) with their tiles and
     KV partitions, by the same rules as ``token_tiles`` / ``num_splits`` /
     ``split_ranges`` applied to each unit's own key range [lo, hi).
@@ -339,7 +388,13 @@ def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0
             for t0 in range(0, u["rows"], tok_wg):
                 nt = min(tok_wg, u["rows"] - t0)
                 u["tiles"].append((t0, nt, MAX_TASK_ROWS, end(t0, nt)))
-    if num_kv_splits > 0:
+    stream = stream_applies(q_len, group, dtype, num_kv_splits, len(groups))
+    if stream:
+        sb = stream_bounds([u["lo"] for u in units], [u["hi"] for u in units], [u["rows"] for u in units],
+                           num_kv_heads, num_cus)
+        for u, b in zip(units, sb):
+            u["splits"], u["bounds"] = len(b), b
+    elif num_kv_splits > 0:
         for u in units:
             u["splits"] = num_kv_splits if u["rows"] else 0
     else:
@@ -359,6 +414,8 @@ def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0
             nblk = -(-(u["hi"] - u["lo"]) // BLOCK)
             u["splits"] = max(1, min(-(-u["last"] // quantum[u["kind"]]), MAX_AUTO_SPLITS, nblk)) if u["rows"] else 0
     for u in units:
+        if stream:
+            continue
         u["bounds"] = []
         if u["splits"]:
             nblk = -(-(u["hi"] - u["lo"]) // BLOCK)

@@ -114,7 +114,8 @@ class Plan:
                          rows=arr(t.cascade_rows, t.num_cascade),
                          splits=arr(t.cascade_splits, t.num_cascade)),
             virtual_row_src=arr(t.virtual_row_src, t.num_virtual_rows),
-            rec_index=arr(t.rec_index, t.num_rec_index))
+            rec_index=arr(t.rec_index, t.num_rec_index),
+            slot_begin=arr(t.slot_begin, t.num_slots + 1) if t.num_slots else np.zeros(0, np.int32))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the work list into ``workspace``."""

@@ -78,6 +78,8 @@ class PlanTables(ctypes.Structure):
         ("virtual_row_src", _i32p),
         ("num_rec_index", ctypes.c_int32),
         ("rec_index", _i32p),
+        ("num_slots", ctypes.c_int32),
+        ("slot_begin", _i32p),
     ]
 
 

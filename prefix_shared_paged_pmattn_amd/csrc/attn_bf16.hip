@@ -236,14 +236,10 @@ struct Depth {
 // planner's dispatch order groups tasks by this count.
 constexpr int kWavesPerWg = kWaveTasksPerWg;
 
+// One task (item idx) on one wave.
 template <int D, int NT, bool TREE>
-__global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))
-void attn_bf16_kernel(AttnArgs a) {
+__device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
   constexpr int KS = D / 32, DT = D / 16;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * kWavesPerWg + wave;
-  if (idx >= a.item_count) return;
   const pmattn_work_item it = load_item(a.items, idx);
   const int i = lane & 15, g = lane >> 4;
   const int G = a.group, hq = a.hq, hkv = a.hkv, kvh = it.kv_head;
@@ -391,11 +387,40 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// Wave w of the launch runs task w, or, with a slot table (equal-work decode
+// plans, 16-row tasks only), its tasks [slot_begin[w], slot_begin[w + 1]) one
+// after another. (The loop stays out of the larger tiles, whose 64-row
+// variant it pushes into spilling.)
+template <int D, int NT, bool TREE>
+__global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT>::value, 8)))
+void attn_bf16_kernel(AttnArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * kWavesPerWg + wave;
+  if constexpr (NT != 1) {
+    if (w < a.item_count) run_task<D, NT, TREE>(a, w, lane);
+    return;
+  }
+  int first, last;
+  if (a.slot_begin) {
+    if (w >= a.slot_count) return;
+    const cint_p sb = (cint_p)a.slot_begin;
+    first = sb[w];
+    last = sb[w + 1];
+  } else {
+    if (w >= a.item_count) return;
+    first = w;
+    last = w + 1;
+  }
+  for (int idx = first; idx < last; ++idx) run_task<D, NT, TREE>(a, idx, lane);
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
-  const dim3 grid((a.item_count + kWavesPerWg - 1) / kWavesPerWg), block(64 * kWavesPerWg);
+  const int waves = a.slot_begin && class_rows <= 16 ? a.slot_count : a.item_count;
+  const dim3 grid((waves + kWavesPerWg - 1) / kWavesPerWg), block(64 * kWavesPerWg);
 #define PMATTN_LAUNCH(D, NT)                                                            \
   do {                                                                                 \
     if (a.row_mask) hipLaunchKernelGGL((attn_bf16_kernel<D, NT, true>), grid, block, 0, st, a); \

@@ -24,6 +24,9 @@ struct AttnArgs {
   const uint64_t* row_mask;      // [R] token-tree masks, or null: every row causal
   float* part_o;                 // [records][d]
   float* part_lse;               // [records]
+  const int32_t* slot_begin;     // one-wave kernel: wave w runs tasks [slot_begin[w], slot_begin[w+1]);
+                                 // null: wave w runs task w
+  int32_t slot_count;
   int32_t item_count;
   int32_t bt_stride;
   int32_t hq;

@@ -107,6 +107,8 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.row_mask = P.row_mask.empty() ? nullptr : reinterpret_cast<const uint64_t*>(ws + P.off_row_mask);
   a.part_o = reinterpret_cast<float*>(ws + P.off_part_o);
   a.part_lse = reinterpret_cast<float*>(ws + P.off_part_lse);
+  a.slot_begin = nullptr;
+  a.slot_count = 0;
   a.bt_stride = P.bt_stride;
   a.hq = P.hq;
   a.hkv = P.hkv;
@@ -130,6 +132,11 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     AttnArgs ac = a;
     ac.items = items + P.class_begin[c];
     ac.item_count = P.class_begin[c + 1] - P.class_begin[c];
+    if (!P.slot_begin.empty()) {
+      // equal-work decode plan: its single class runs one slot per wave
+      ac.slot_begin = reinterpret_cast<const int32_t*>(ws + P.off_slot);
+      ac.slot_count = (int32_t)P.slot_begin.size() - 1;
+    }
     if (P.class_cascade[c]) {
       // virtual rows: gathered queries; their keys all lie below every
       // member's first row, so no tree mask applies

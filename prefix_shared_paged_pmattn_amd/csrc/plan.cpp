@@ -60,6 +60,46 @@ std::vector<size_t> xcd_order(const std::vector<pmattn_work_item>& v, const std:
   return out;
 }
 
+// Dispatch order of an equal-work decode plan. Slot (g, j) is the run of tasks
+// of kv head g inside piece j, in unit order (each unit's partition p lies in
+// piece start_u / len + p). Slots go to XCDs like tasks in xcd_order (kv head
+// g on XCD g; with fewer than kXcds heads, piece j of head g on XCD
+// g * rep + j % rep), four slots per workgroup, topped up from the XCD with
+// the most slots left. Returns the task order and fills slot_begin.
+std::vector<size_t> stream_order(const std::vector<pmattn_work_item>& v, const std::vector<int64_t>& start,
+                                 int64_t len, int64_t pieces, int hkv, std::vector<int32_t>& slot_begin) {
+  const int64_t nslot = (int64_t)hkv * pieces;
+  std::vector<std::vector<size_t>> slot(nslot);
+  for (size_t i = 0; i < v.size(); ++i) {
+    const pmattn_work_item& it = v[i];
+    // partitions of a stream plan start at piece boundaries or at the unit's
+    // first key, so the first block tells the piece
+    const int64_t j = (start[it.seq] + it.kv_begin / kBlock) / len;
+    slot[(int64_t)it.kv_head * pieces + j].push_back(i);
+  }
+  const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;
+  std::vector<std::vector<int64_t>> q(kXcds);
+  for (int g = 0; g < hkv; ++g)
+    for (int64_t j = 0; j < pieces; ++j)
+      q[(hkv >= kXcds ? g : g * rep + (int)(j % rep)) % kXcds].push_back((int64_t)g * pieces + j);
+  std::vector<size_t> head(kXcds, 0), out;
+  out.reserve(v.size());
+  slot_begin.assign(1, 0);
+  for (int64_t taken = 0, wg = 0; taken < nslot; ++wg) {
+    int x = (int)(wg % kXcds);
+    for (int k = 0; k < kWaveTasksPerWg && taken < nslot; ++k, ++taken) {
+      if (head[x] == q[x].size()) {
+        size_t best = 0;
+        for (int y = 0; y < kXcds; ++y)
+          if (q[y].size() - head[y] > best) best = q[y].size() - head[y], x = y;
+      }
+      for (size_t i : slot[q[x][head[x]++]]) out.push_back(i);
+      slot_begin.push_back((int32_t)out.size());
+    }
+  }
+  return out;
+}
+
 // Cost model for ordering and automatic splitting, in "block units": a task
 // over n KV blocks costs n * (2 + rows/16). The constant 2 stands for the
 // K/V stream of each block, the rows/16 term for its MFMA column tiles.
@@ -71,6 +111,11 @@ int64_t unit_cost(int cls) { return 2 + kClassRows[cls] / 16; }
 // the mixed batch) ...
 constexpr int64_t kTasksPerCu = 32;
 constexpr int64_t kWgTasksPer2Cu = 3;
+// Equal-work decode: a plan whose tasks are all 16-row wave tasks (decode
+// rows) with automatic splits gives each of kStreamWavesPerCu waves per CU an
+// equal run of KV blocks of one kv head, never shorter than kStreamMinBlocks.
+constexpr int64_t kStreamWavesPerCu = 4;
+constexpr int64_t kStreamMinBlocks = 16;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;
 constexpr int kMaxAutoSplits = 64;
@@ -381,7 +426,30 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
 
   // ---- KV partitions per unit ------------------------------------------------
   std::vector<int32_t> usplits(U, 0);
-  if (d->num_kv_splits > 0) {
+  // Equal-work decode (stream) partitions. Units with rows, in order, laid end
+  // to end: unit u holds blocks [S_u, S_u + n_u) of the concatenation. Cut it
+  // into pieces of L blocks; a unit's partitions are its parts of the pieces
+  // it meets, and piece j of kv head g is the work of one wave.
+  bool stream = d->dtype == PMATTN_BF16 && d->num_kv_splits == 0 && V == 0 && !tiles.empty();
+  for (const Tile& t : tiles) stream = stream && t.cls == 0;
+  std::vector<int64_t> stream_start(U, 0);
+  int64_t stream_len = 0, stream_pieces = 0;
+  if (stream) {
+    int64_t total = 0;
+    for (int u = 0; u < U; ++u) {
+      stream_start[u] = total;
+      if (unit_rows(u) > 0) total += (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
+    }
+    const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
+    const int64_t per_head = std::max<int64_t>(1, cus * kStreamWavesPerCu / d->num_kv_heads);
+    stream_len = std::max(kStreamMinBlocks, (total + per_head - 1) / per_head);
+    stream_pieces = (total + stream_len - 1) / stream_len;
+    for (int u = 0; u < U; ++u) {
+      if (unit_rows(u) == 0) continue;
+      const int64_t n = (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
+      usplits[u] = (int32_t)((stream_start[u] + n - 1) / stream_len - stream_start[u] / stream_len + 1);
+    }
+  } else if (d->num_kv_splits > 0) {
     for (int u = 0; u < U; ++u) usplits[u] = unit_rows(u) > 0 ? d->num_kv_splits : 0;
   } else {
     // Two resource classes are balanced separately: wave tasks (<= 64 rows,
@@ -419,6 +487,18 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     const int np = usplits[u];
     if (!np) continue;
     const int64_t lo = unit_lo(u), kv = unit_hi(u);
+    if (stream) {
+      // partition p starts at the p-th piece boundary met (block offsets from
+      // the unit's start)
+      const int64_t s0 = stream_start[u], j0 = s0 / stream_len;
+      for (int p = 0; p < np; ++p) {
+        const int64_t b = p == 0 ? 0 : (j0 + p) * stream_len - s0;
+        const int64_t e = (j0 + p + 1) * stream_len - s0;
+        ubeg[uoff[u] + p] = (int32_t)std::min<int64_t>(lo + b * kBlock, kv);
+        uend[uoff[u] + p] = (int32_t)std::min<int64_t>(lo + e * kBlock, kv);
+      }
+      continue;
+    }
     const int64_t nblk = (kv - lo + kBlock - 1) / kBlock;
     const int64_t chunk = std::max<int64_t>(1, (nblk + np - 1) / np);
     for (int p = 0; p < np; ++p) {
@@ -527,8 +607,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     std::vector<size_t> idx(v.size());
     std::iota(idx.begin(), idx.end(), 0);
     std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
-    idx = xcd_order(v, idx, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1,
-                    d->num_kv_heads);
+    if (stream)
+      idx = stream_order(v, stream_start, stream_len, stream_pieces, d->num_kv_heads, P.slot_begin);
+    else
+      idx = xcd_order(v, idx, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1,
+                      d->num_kv_heads);
     if (d->work_shuffle_seed)
       for (size_t i = idx.size(); i > 1; --i) std::swap(idx[i - 1], idx[splitmix64(rng) % i]);
     for (size_t i : idx) P.items.push_back(v[i]);
@@ -546,7 +629,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.off_append = align_up(P.off_row_mask + P.row_mask.size() * sizeof(uint64_t), kAlign);
   P.off_rec_index = align_up(P.off_append + P.append_units.size() * sizeof(pmattn_append_unit), kAlign);
   P.off_vrow = align_up(P.off_rec_index + P.rec_index.size() * sizeof(int32_t), kAlign);
-  P.off_qv = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
+  P.off_slot = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
+  P.off_qv = align_up(P.off_slot + P.slot_begin.size() * sizeof(int32_t), kAlign);
   const size_t elem = P.dtype == PMATTN_BF16 ? 2 : 4;
   P.off_part_o = align_up(P.off_qv + P.vrow_src.size() * (size_t)P.hq * P.head_dim * elem, kAlign);
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
@@ -568,6 +652,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     std::memcpy(P.upload_blob.data() + P.off_rec_index, P.rec_index.data(), P.rec_index.size() * sizeof(int32_t));
   if (!P.vrow_src.empty())
     std::memcpy(P.upload_blob.data() + P.off_vrow, P.vrow_src.data(), P.vrow_src.size() * sizeof(int32_t));
+  if (!P.slot_begin.empty())
+    std::memcpy(P.upload_blob.data() + P.off_slot, P.slot_begin.data(), P.slot_begin.size() * sizeof(int32_t));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -642,6 +728,8 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->virtual_row_src = P.vrow_src.data();
   t->num_rec_index = (int32_t)P.rec_index.size();
   t->rec_index = P.rec_index.data();
+  t->num_slots = P.slot_begin.empty() ? 0 : (int32_t)P.slot_begin.size() - 1;
+  t->slot_begin = P.slot_begin.empty() ? nullptr : P.slot_begin.data();
   return PMATTN_OK;
 }
 

@@ -45,6 +45,9 @@ struct Plan {
   std::vector<int32_t> class_rows, class_begin, class_cascade;
   std::vector<pmattn_merge_row> merge_rows;
   int32_t merge_max_parts = 0;  // largest nparts of any merge row
+  // equal-work decode plans: wave w runs tasks [slot_begin[w], slot_begin[w + 1])
+  // of the plan's single class; empty when every task is its own wave
+  std::vector<int32_t> slot_begin;
   int32_t num_records = 0;
   // tree masks, one per row, present only when some sequence is a tree
   std::vector<uint64_t> row_mask;
@@ -57,10 +60,11 @@ struct Plan {
   std::vector<pmattn_append_unit> append_units;
   std::string append_conflict;
   // workspace layout (bytes): [items | merge rows | row masks | append units |
-  // record index | virtual row sources | gathered Q of virtual rows |
-  // partial O | partial lse]; everything before the gathered Q is uploaded
+  // record index | virtual row sources | wave slots | gathered Q of virtual
+  // rows | partial O | partial lse]; everything before the gathered Q is
+  // uploaded
   size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_rec_index = 0,
-         off_vrow = 0, off_qv = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+         off_vrow = 0, off_slot = 0, off_qv = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 

@@ -30,13 +30,14 @@ def check_plan(b, p, num_cus=0):
     grp = b.num_q_heads // b.num_kv_heads
     rs, rp = R.row_tables(b.q_len, b.q_start)
     assert np.array_equal(t["row_seq"], rs) and np.array_equal(t["row_pos"], rp)
-    ns = R.num_splits(b.q_len, b.q_start, b.num_kv_heads, grp, b.num_kv_splits, num_cus)
+    ns = R.num_splits(b.q_len, b.q_start, b.num_kv_heads, grp, b.num_kv_splits, num_cus, b.dtype)
     assert np.array_equal(t["num_splits"], ns)
-    lo, hi = R.split_ranges(b.q_len, b.q_start, ns)
+    bounds = R.seq_bounds(b.q_len, b.q_start, b.num_kv_heads, grp, ns, num_cus, b.dtype, b.num_kv_splits)
+    lo, hi = R.split_ranges(b.q_len, b.q_start, ns, bounds)
     assert np.array_equal(t["split_begin"], lo) and np.array_equal(t["split_end"], hi)
     got = {tuple(int(x) for x in it[:7]) for it in t["items"]}
     assert len(got) == t["items"].shape[0], "duplicate tasks"
-    assert got == R.expected_tasks(b.q_len, b.q_start, b.num_kv_heads, grp, ns)
+    assert got == R.expected_tasks(b.q_len, b.q_start, b.num_kv_heads, grp, ns, bounds)
     R.check_coverage(t["items"], b.q_len, b.q_start, b.num_kv_heads)
     check_records(b, t)
     return t
@@ -114,7 +115,7 @@ def _xcd_of(kv_head, seq, hkv, xcds=8):
     return (kv_head * rep + seq % rep) % xcds
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
+@pytest.mark.parametrize("cfg", [3, 4])
 def test_dispatch_order_is_xcd_aware_and_cost_descending(cfg):
     """Workgroup slot i runs on XCD i % 8; every task of a kv head lands on that
     head's XCD, except where a workgroup is topped up from another XCD at the
@@ -133,6 +134,51 @@ def test_dispatch_order_is_xcd_aware_and_cost_descending(cfg):
         blk = -(-(cls[:, 6] - cls[:, 5]) // 16)
         for x in range(8):
             assert (np.diff(blk[want == x]) <= 0).all()
+
+
+@pytest.mark.parametrize("cfg,num_cus", [(2, 0), (2, 64)])
+def test_equal_work_decode_slots(cfg, num_cus):
+    """Pure decode plans: wave w runs the tasks of slot w, all of one kv head,
+    on that head's XCD (topped-up workgroups aside), each slot one piece of L
+    blocks of the sequences laid end to end (the last piece of a head may be
+    shorter), its tasks in sequence order and back to back."""
+    b = wl.config(cfg, values=False)
+    t = make_plan(b, num_cus=num_cus).tables()
+    assert t["class_rows"].tolist() == [16]
+    sb, it = t["slot_begin"], t["items"]
+    assert sb.size > 1 and sb[0] == 0 and sb[-1] == it.shape[0] and (np.diff(sb) > 0).all()
+    nblk = -(-(np.asarray(b.q_start) + np.asarray(b.q_len)) // 16)
+    start = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    total = int(nblk.sum())
+    per_head = max(1, (num_cus or 256) * 4 // b.num_kv_heads)
+    L = max(16, -(-total // per_head))
+    off_xcd = 0
+    pieces = set()
+    for w in range(sb.size - 1):
+        tk = it[sb[w]:sb[w + 1]]
+        g = set(tk[:, 1].tolist())
+        assert len(g) == 1
+        g = g.pop()
+        off_xcd += (w // 4) % 8 != g % 8
+        a = start[tk[:, 0]] + tk[:, 5] // 16                  # first block, in the concatenation
+        e = start[tk[:, 0]] + -(-tk[:, 6] // 16)
+        assert (a[1:] == e[:-1]).all() and (np.diff(tk[:, 0]) > 0).all()
+        j = a[0] // L
+        assert a[0] == j * L and (e[-1] == (j + 1) * L or e[-1] == total)
+        pieces.add((g, int(j)))
+    assert len(pieces) == sb.size - 1 == b.num_kv_heads * -(-total // L)
+    assert off_xcd <= 8 * 4
+    check_plan(b, make_plan(b, num_cus=num_cus), num_cus=num_cus)
+
+
+def test_equal_work_only_for_pure_auto_split_bf16_decode():
+    # explicit splits (the long-decode workload asks for 16), f32, or a verify row: one task per wave
+    for b in (wl.config(5, values=False), wl.config(1, values=False),
+              wl.custom([dict(q_len=1, seq_len=300), dict(q_len=5, seq_len=90)], hq=8, hkv=2, d=128,
+                        values=False)):
+        assert make_plan(b).tables()["slot_begin"].size == 0
+    b = wl.custom([dict(q_len=1, seq_len=n) for n in (300, 17, 1000)], hq=8, hkv=2, d=128, values=False)
+    assert make_plan(b).tables()["slot_begin"].size > 0
 
 
 def test_dispatch_order_with_few_kv_heads_is_a_permutation():
@@ -307,7 +353,7 @@ def test_append_refuses_shared_target_slots():
 def _check_cascade_plan(b, t, num_kv_splits=0, num_cus=0, mode=1):
     grp = b.num_q_heads // b.num_kv_heads
     rep = R.plan_units(b.q_len, b.q_start, b.block_table, b.num_kv_heads, grp, num_kv_splits, num_cus,
-                       cascade=mode)
+                       cascade=mode, dtype=b.dtype)
     units = rep["units"]
     nb = b.num_seqs
     virt = units[nb:]
