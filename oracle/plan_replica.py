@@ -30,7 +30,7 @@ TASKS_PER_CU = 32
 WG_TASKS_PER_2CU = 3  # 1.5 workgroup tasks per CU
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
-STREAM_WAVES_PER_CU = 4
+STREAM_WAVES_PER_CU = 3
 STREAM_MIN_BLOCKS = 16
 
 
@@ -46,7 +46,7 @@ def stream_bounds(lo, hi, rows, num_kv_heads, num_cus=0):
     """Partition bounds of every unit (key ranges [lo, hi), ``rows`` > 0 for
     units with work) in an equal-work decode plan. The units' blocks are laid
     end to end in unit order; pieces of L blocks, L = max(16, ceil(total /
-    (CUs x 4 / Hkv))), cut them; a unit's partitions are its parts of the
+    (CUs x 3 / Hkv))), cut them; a unit's partitions are its parts of the
     pieces it meets. Returns one list of (begin, end) per unit."""
     nblk = [-(-(int(h) - int(l)) // BLOCK) if r > 0 else 0 for l, h, r in zip(lo, hi, rows)]
     total = sum(nblk)

@@ -114,7 +114,9 @@ constexpr int64_t kWgTasksPer2Cu = 3;
 // Equal-work decode: a plan whose tasks are all 16-row wave tasks (decode
 // rows) with automatic splits gives each of kStreamWavesPerCu waves per CU an
 // equal run of KV blocks of one kv head, never shorter than kStreamMinBlocks.
-constexpr int64_t kStreamWavesPerCu = 4;
+// (Measured on MI355X, 64-sequence decode, % of HBM peak: 2 waves per CU 61,
+// 3: 69.4, 4: 68.6, 6: 62, 8: 66.8; 3 and 4 tie on other context mixes.)
+constexpr int64_t kStreamWavesPerCu = 3;
 constexpr int64_t kStreamMinBlocks = 16;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;

@@ -150,7 +150,7 @@ def test_equal_work_decode_slots(cfg, num_cus):
     nblk = -(-(np.asarray(b.q_start) + np.asarray(b.q_len)) // 16)
     start = np.concatenate([[0], np.cumsum(nblk)[:-1]])
     total = int(nblk.sum())
-    per_head = max(1, (num_cus or 256) * 4 // b.num_kv_heads)
+    per_head = max(1, (num_cus or 256) * 3 // b.num_kv_heads)
     L = max(16, -(-total // per_head))
     off_xcd = 0
     pieces = set()
