@@ -132,8 +132,8 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     AttnArgs ac = a;
     ac.items = items + P.class_begin[c];
     ac.item_count = P.class_begin[c + 1] - P.class_begin[c];
-    if (!P.slot_begin.empty()) {
-      // equal-work decode plan: its single class runs one slot per wave
+    if ((int)c == P.slot_class) {
+      // equal-work decode tasks: one slot per wave
       ac.slot_begin = reinterpret_cast<const int32_t*>(ws + P.off_slot);
       ac.slot_count = (int32_t)P.slot_begin.size() - 1;
     }

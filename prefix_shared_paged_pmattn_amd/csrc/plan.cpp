@@ -67,14 +67,15 @@ std::vector<size_t> xcd_order(const std::vector<pmattn_work_item>& v, const std:
 // g * rep + j % rep), four slots per workgroup, topped up from the XCD with
 // the most slots left. Returns the task order and fills slot_begin.
 std::vector<size_t> stream_order(const std::vector<pmattn_work_item>& v, const std::vector<int64_t>& start,
-                                 int64_t len, int64_t pieces, int hkv, std::vector<int32_t>& slot_begin) {
+                                 const std::vector<int64_t>& lo, int64_t len, int64_t pieces, int hkv,
+                                 std::vector<int32_t>& slot_begin) {
   const int64_t nslot = (int64_t)hkv * pieces;
   std::vector<std::vector<size_t>> slot(nslot);
   for (size_t i = 0; i < v.size(); ++i) {
     const pmattn_work_item& it = v[i];
     // partitions of a stream plan start at piece boundaries or at the unit's
     // first key, so the first block tells the piece
-    const int64_t j = (start[it.seq] + it.kv_begin / kBlock) / len;
+    const int64_t j = (start[it.seq] + (it.kv_begin - lo[it.seq]) / kBlock) / len;
     slot[(int64_t)it.kv_head * pieces + j].push_back(i);
   }
   const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;
@@ -116,6 +117,11 @@ constexpr int64_t kWgTasksPer2Cu = 3;
 // equal run of KV blocks of one kv head, never shorter than kStreamMinBlocks.
 // (Measured on MI355X, 64-sequence decode, % of HBM peak: 2 waves per CU 61,
 // 3: 69.4, 4: 68.6, 6: 62, 8: 66.8; 3 and 4 tie on other context mixes.)
+// Plans with other tasks beside the decode ones keep one task per wave: there
+// the decode waves share the chip with workgroup tasks, and fewer, longer
+// decode waves were slower (mixed batch: 1, 2, 3 waves per CU gave 1.32,
+// 0.92, 0.79 ms against 0.78; shared-prompt cascade 0.173, 0.130, 0.127
+// against 0.125 ms).
 constexpr int64_t kStreamWavesPerCu = 3;
 constexpr int64_t kStreamMinBlocks = 16;
 // ... but never cuts a task below this many block units.
@@ -428,30 +434,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
 
   // ---- KV partitions per unit ------------------------------------------------
   std::vector<int32_t> usplits(U, 0);
-  // Equal-work decode (stream) partitions. Units with rows, in order, laid end
-  // to end: unit u holds blocks [S_u, S_u + n_u) of the concatenation. Cut it
-  // into pieces of L blocks; a unit's partitions are its parts of the pieces
-  // it meets, and piece j of kv head g is the work of one wave.
-  bool stream = d->dtype == PMATTN_BF16 && d->num_kv_splits == 0 && V == 0 && !tiles.empty();
-  for (const Tile& t : tiles) stream = stream && t.cls == 0;
-  std::vector<int64_t> stream_start(U, 0);
-  int64_t stream_len = 0, stream_pieces = 0;
-  if (stream) {
-    int64_t total = 0;
-    for (int u = 0; u < U; ++u) {
-      stream_start[u] = total;
-      if (unit_rows(u) > 0) total += (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
-    }
-    const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
-    const int64_t per_head = std::max<int64_t>(1, cus * kStreamWavesPerCu / d->num_kv_heads);
-    stream_len = std::max(kStreamMinBlocks, (total + per_head - 1) / per_head);
-    stream_pieces = (total + stream_len - 1) / stream_len;
-    for (int u = 0; u < U; ++u) {
-      if (unit_rows(u) == 0) continue;
-      const int64_t n = (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
-      usplits[u] = (int32_t)((stream_start[u] + n - 1) / stream_len - stream_start[u] / stream_len + 1);
-    }
-  } else if (d->num_kv_splits > 0) {
+  if (d->num_kv_splits > 0) {
     for (int u = 0; u < U; ++u) usplits[u] = unit_rows(u) > 0 ? d->num_kv_splits : 0;
   } else {
     // Two resource classes are balanced separately: wave tasks (<= 64 rows,
@@ -481,6 +464,38 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       usplits[u] = (int32_t)std::max<int64_t>(1, p);
     }
   }
+  // Equal-work decode (stream) partitions of the decode units: real sequences
+  // whose rows make one 16-row wave task. Laid end to end in unit order, unit
+  // u holds blocks [S_u, S_u + n_u) of the concatenation; cut it into pieces of
+  // L blocks; a unit's partitions are its parts of the pieces it meets, and
+  // piece j of kv head g is the work of one wave.
+  std::vector<char> sunit(U, 0);
+  bool any_stream = false, any_other = V > 0;
+  for (const Tile& t : tiles) {
+    const bool dec = t.seq < B && t.cls == 0;
+    sunit[t.seq] = dec;
+    any_stream = any_stream || dec;
+    any_other = any_other || !dec;
+  }
+  const bool stream = d->dtype == PMATTN_BF16 && d->num_kv_splits == 0 && any_stream && !any_other;
+  std::vector<int64_t> stream_start(U, 0);
+  int64_t stream_len = 0, stream_pieces = 0;
+  if (stream) {
+    int64_t total = 0;
+    for (int u = 0; u < U; ++u) {
+      stream_start[u] = total;
+      if (sunit[u]) total += (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
+    }
+    const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
+    const int64_t per_head = std::max<int64_t>(1, cus * kStreamWavesPerCu / d->num_kv_heads);
+    stream_len = std::max(kStreamMinBlocks, (total + per_head - 1) / per_head);
+    stream_pieces = (total + stream_len - 1) / stream_len;
+    for (int u = 0; u < U; ++u) {
+      if (!sunit[u]) continue;
+      const int64_t n = (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
+      usplits[u] = (int32_t)((stream_start[u] + n - 1) / stream_len - stream_start[u] / stream_len + 1);
+    }
+  }
   std::vector<int32_t> uoff(U + 1, 0), ubeg, uend;
   for (int u = 0; u < U; ++u) uoff[u + 1] = uoff[u] + usplits[u];
   ubeg.resize(uoff[U]);
@@ -489,7 +504,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     const int np = usplits[u];
     if (!np) continue;
     const int64_t lo = unit_lo(u), kv = unit_hi(u);
-    if (stream) {
+    if (stream && sunit[u]) {
       // partition p starts at the p-th piece boundary met (block offsets from
       // the unit's start)
       const int64_t s0 = stream_start[u], j0 = s0 / stream_len;
@@ -609,9 +624,12 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     std::vector<size_t> idx(v.size());
     std::iota(idx.begin(), idx.end(), 0);
     std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
-    if (stream)
-      idx = stream_order(v, stream_start, stream_len, stream_pieces, d->num_kv_heads, P.slot_begin);
-    else
+    if (stream && c == 0) {
+      std::vector<int64_t> ulo(B);
+      for (int u = 0; u < B; ++u) ulo[u] = unit_lo(u);
+      idx = stream_order(v, stream_start, ulo, stream_len, stream_pieces, d->num_kv_heads, P.slot_begin);
+      P.slot_class = (int32_t)P.class_rows.size();
+    } else
       idx = xcd_order(v, idx, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1,
                       d->num_kv_heads);
     if (d->work_shuffle_seed)

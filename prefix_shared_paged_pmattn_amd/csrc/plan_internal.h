@@ -48,6 +48,7 @@ struct Plan {
   // equal-work decode plans: wave w runs tasks [slot_begin[w], slot_begin[w + 1])
   // of the plan's single class; empty when every task is its own wave
   std::vector<int32_t> slot_begin;
+  int32_t slot_class = -1;  // the class slot_begin belongs to
   int32_t num_records = 0;
   // tree masks, one per row, present only when some sequence is a tree
   std::vector<uint64_t> row_mask;
