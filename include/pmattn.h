@@ -238,8 +238,11 @@ typedef struct pmattn_plan_tables {
 } pmattn_plan_tables;
 
 /* Build a plan on the host. Validates the batch (see pmattn_plan_desc),
- * splits the work into tile tasks, orders them by estimated cost (largest
- * first) and prepares the merge list. Makes no HIP call and touches no GPU.
+ * splits the work into tile tasks (automatic splits: balanced cost quanta;
+ * pure decode batches in bf16: equal KV pieces, one per wave, see
+ * pmattn_plan_tables.slot_begin), orders them by estimated cost (largest
+ * first) with every kv head's tasks on one XCD of the GPU, and prepares the
+ * merge list. Makes no HIP call and touches no GPU.
  * Errors: PMATTN_E_INVALID for null pointers, negative lengths,
  * q_start + q_len > seq_len, a block id outside [0, num_pool_blocks) among the
  * blocks a row can see, bt_stride too small, Hq % Hkv != 0, scale not finite
