@@ -26,6 +26,12 @@ def _batch_cases():
         "decode-g8-d128-split3": (dict(hq=16, hkv=2, d=128), [S(q_len=1, seq_len=n) for n in (2, 47, 300, 777)], 3),
         "decode-g4-d64": (dict(hq=8, hkv=2, d=64), [S(q_len=1, seq_len=n) for n in (5, 64, 65, 129, 400)], 0),
         "verify5-g4": (dict(hq=8, hkv=2, d=128), [S(q_len=5, seq_len=n) for n in (5, 21, 37, 300)], 0),
+        # equal-work decode plans: a long sequence cut into many pieces (a
+        # many-partition merge) beside sequences that share one piece; fewer
+        # kv heads than XCDs; d = 64
+        "decode-equal-work-long-and-short": (dict(hq=8, hkv=2, d=128),
+                                             [S(q_len=1, seq_len=n) for n in (20000, 3, 17, 700, 1)], 0),
+        "decode-equal-work-d64": (dict(hq=16, hkv=4, d=64), [S(q_len=1, seq_len=n) for n in (5000, 40, 333)], 0),
         "prefill-unaligned": (dict(hq=8, hkv=2, d=128), [S(q_len=37, seq_len=42, q_start=5), S(q_len=100, seq_len=100),
                                                          S(q_len=64, seq_len=264, q_start=200)], 0),
         "prefill-d64-split2": (dict(hq=4, hkv=1, d=64), [S(q_len=70, seq_len=90, q_start=20), S(q_len=16, seq_len=16)], 2),
