@@ -287,7 +287,7 @@ def test_empty_plan_launches_nothing():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("P", [5, 100])
+@pytest.mark.parametrize("P", [2, 5, 8, 9, 100])  # group kernel up to 8 partials, wave kernel above
 def test_merge_lse_standalone(d, out_dtype, P):
     import torch
     rng = np.random.Generator(np.random.PCG64(d + P))
