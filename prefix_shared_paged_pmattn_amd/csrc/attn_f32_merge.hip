@@ -102,10 +102,10 @@ constexpr int kGroupBatch = 8;
 // Group variant, for merges of a few partials: a group of 16 lanes merges one
 // output (row, head); lane j owns channels
 // [D/16 j, D/16 (j + 1)), read as 16-byte pieces. Every lane walks the
-// partials itself (no cross-lane reductions), four at a time: the record ids,
-// the four lse values and the four output pieces are independent loads
+// partials itself (no cross-lane reductions), kGroupBatch (8) at a time: the
+// batch's record ids, lse values and output pieces are independent loads
 // issued together, then folded in with an online max (running max m, sums
-// rescaled by exp(m_old - m_new) when it grows). A merge of up to four
+// rescaled by exp(m_old - m_new) when it grows). A merge of up to eight
 // partials costs one memory round trip after its row record.
 template <int D, bool BF16_OUT>
 __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      if (l[u] == kNegInf) continue;  // empty partition: its slot is never read
+      if (l[u] == kNegInf) continue;  // empty partition: its loaded slot (maybe never written) is unused
       const float m_new = fmaxf(m, l[u]);
       const float alpha = m == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * kLog2e);
       const float wt = __builtin_amdgcn_exp2f((l[u] - m_new) * kLog2e);
