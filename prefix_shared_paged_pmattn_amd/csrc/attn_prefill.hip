@@ -17,10 +17,12 @@
 //   registers and every V operand is one 16-byte LDS read of 8 consecutive
 //   keys of one channel (V blocks are channel-major).
 // * Online softmax in fp32 with exp2 (scale*log2e folded in). The O rescale
-//   is lazy: the running reference max moves only when some row's max grows by
-//   more than 2^8, which after the first chunks almost never happens; P stays
-//   below 2^8 and the final O/l is exact either way (online softmax equals
-//   softmax: "Assumptions & free parameters").
+//   is lazy: a row's reference max moves only when the row's max passes it by
+//   more than 2^8 (one compare against a per-row threshold per tile), which
+//   after the first chunks almost never happens; P stays below 2^8 and the
+//   final O/l is exact either way (online softmax equals softmax:
+//   "Assumptions & free parameters"). The half-row max is one
+//   v_permlane32_swap, the 16-score max eight v_maximum3.
 // * Row-wise causal masks ("Editorial extensions"): chunks wholly visible to
 //   every row of the task take an unmasked path (Figure 11, mask-aware
 //   computation); V lanes of keys past the task's end are zeroed when the chunk
@@ -36,7 +38,9 @@
 // * The register staging of the next chunk uses clang vector types: with
 //   HIP's uint4 the copies are memcpys of a union, the staging array stays
 //   in private memory and the backend moves it to LDS, so every chunk's loads
-//   were waited for right after issue (15% of the few-shot time).
+//   were waited for right after issue (15% of the few-shot time). Its loads
+//   are buffer loads with a scalar (block, kv head) base and one 32-bit lane
+//   offset shared by K and V: no 64-bit address arithmetic per chunk.
 #include "attn_kernels.h"
 
 namespace pmattn {
@@ -54,9 +58,6 @@ typedef const int32_t __attribute__((address_space(4)))* cint_p;
 // Tuning knobs (compile-time); the defaults are the measured best.
 #ifndef PMATTN_PF_CHUNK
 #define PMATTN_PF_CHUNK 32
-#endif
-#ifndef PMATTN_PF_TILE_OUTER
-#define PMATTN_PF_TILE_OUTER 1
 #endif
 #ifndef PMATTN_PF_KEEP
 #define PMATTN_PF_KEEP 0
@@ -98,7 +99,7 @@ __device__ __forceinline__ pmattn_work_item load_item(const pmattn_work_item* it
   return it;
 }
 
-// Global -> register staging of one 64-key chunk (4 blocks): thread `tid`
+// Global -> register staging of one chunk (CHUNK / 16 blocks): thread `tid`
 // carries PIECES 16-byte pieces of K and of V; consecutive threads read
 // consecutive 16-byte pieces of a block, so every wave load is 1 KiB
 // contiguous.
@@ -121,20 +122,32 @@ __device__ __forceinline__ int pick(const int (&blk)[N], int b) {
   return r;
 }
 
+// Buffer resource over one (block, kv head) slice of a pool: 16 tokens x D
+// channels of bf16; reads past its end return 0.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* slice) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(slice), (short)0, 32 * D, 0x00020000);
+}
+
 template <int D>
 __device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restrict__ kpool,
                                            const uint16_t* __restrict__ vpool, const int (&blk)[Cfg<D>::NBLK],
                                            int kvh, int hkv, int tid) {
   constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;  // 16-byte pieces per block
+  static_assert(PER_BLOCK % 64 == 0, "a wave's pieces lie in one block");
+  __builtin_assume(tid >= 0 && tid < 256);
 #pragma unroll
   for (int u = 0; u < P; ++u) {
     const int q = tid + 256 * u;
-    const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-    const int64_t base = (int64_t)pick(blk, b) * hkv + kvh;
-    // grouped K block [D/8][16 tokens][8]: channel group r / 16, token r % 16
-    st.k[u] = *reinterpret_cast<const u32x4*>(kpool + base * 16 * D + 8 * r);
-    // V block [D][16 tokens]: channel r / 2, half r % 2
-    st.v[u] = *reinterpret_cast<const u32x4*>(vpool + (base * D + r / 2) * 16 + 8 * (r % 2));
+    // A wave's pieces all lie in one block (a scalar base), and the lane's
+    // byte offset in it, 16 * (q % PER_BLOCK), is the same for K (grouped
+    // [D/8][16][8]: channel group r / 16, token r % 16) and for V ([D][16]:
+    // channel r / 2, half r % 2).
+    const int b = __builtin_amdgcn_readfirstlane(q / PER_BLOCK);
+    const int64_t base = ((int64_t)pick(blk, b) * hkv + kvh) * 16 * D;
+    const uint32_t off = 16u * (uint32_t)(q % PER_BLOCK);
+    st.k[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(block_rsrc<D>(kpool + base), off, 0, 0));
+    st.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(block_rsrc<D>(vpool + base), off, 0, 0));
   }
 }
 
@@ -187,11 +200,29 @@ __device__ __forceinline__ void keep_compute_branch() {
 #endif
 }
 
+// max without the sNaN quieting that fmaxf needs (scores are never
+// signalling NaNs)
+__device__ __forceinline__ float fmax_nq(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// max over lanes l and l ^ 32 (the two halves of a query row's keys)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_nq(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Softmax state of a lane's row: the reference ref2 (in scaled log2 units)
+// subtracted before exp2, and the raw score above which the reference must
+// move (about ref2 / sl2 + kRescaleLog2 / sl2; -inf while the row has seen
+// no visible key, when ref2 is 0).
+struct RowRef {
+  float ref2;
+  float thr;
+};
+
 // One 32-key score tile: S^T = K.Q^T, mask, online softmax with lazy
 // rescale, then O^T += V^T.P^T.
 template <int D, bool TREE>
 __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const bf16x8 (&qop)[D / 16],
-                                             f32x16 (&o)[D / 32], float& m_used, float& l_part,
+                                             f32x16 (&o)[D / 32], RowRef& rr, float& l_part,
                                              bool mask, int lim, float sl2, int i32, int h,
                                              uint64_t rel, int dpos) {
   constexpr int KSTEPS = D / 16, DT = D / 32;
@@ -221,27 +252,33 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
   }
   float mx = s[0];
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const bool grow = mx != kNegInf && (m_used == kNegInf || (mx - m_used) * sl2 > kRescaleLog2);
+  for (int r = 1; r < 16; ++r) mx = fmax_nq(mx, s[r]);
+  mx = max_halves(mx);
+  // the reference moves only for rows whose max passed the threshold (a row
+  // with no visible key so far has threshold -inf: its first one moves it)
+  const bool grow = mx > rr.thr;
   if (__any(grow)) {
     keep_compute_branch<D>();
-    const float m_new = fmaxf(m_used, mx);
-    const float alpha = m_used == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2);
+    const float r2 = mx * sl2;
+    const float alpha = !grow ? 1.f : rr.thr == kNegInf ? 0.f : __builtin_amdgcn_exp2f(rr.ref2 - r2);
     l_part *= alpha;
 #pragma unroll
     for (int t = 0; t < DT; ++t) o[t] *= alpha;
-    m_used = m_new;
+    if (grow) {
+      rr.ref2 = r2;
+      rr.thr = mx + kRescaleLog2 * __builtin_amdgcn_rcpf(sl2);
+    }
   }
-  const float ms = m_used == kNegInf ? 0.f : m_used * sl2;
+  const float ms = rr.ref2;
   f32x8 p0, p1;
-  float ps = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     p0[e] = __builtin_amdgcn_exp2f(s[e] * sl2 - ms);
     p1[e] = __builtin_amdgcn_exp2f(s[8 + e] * sl2 - ms);
-    ps += p0[e] + p1[e];
   }
+  float ps = p0[0] + p1[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) ps += p0[e] + p1[e];
   l_part += ps;
   const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
   const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
@@ -255,78 +292,12 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
 
 template <int D, bool TREE>
 __device__ __forceinline__ void compute_chunk(const uint16_t* lds, const bf16x8 (&qop)[D / 16],
-                                              f32x16 (&o)[D / 32], float& m_used, float& l_part,
+                                              f32x16 (&o)[D / 32], RowRef& rr, float& l_part,
                                               bool mask, int lim, float sl2, int i32, int h,
                                               uint64_t rel, int dpos) {
-#if PMATTN_PF_TILE_OUTER
 #pragma unroll
   for (int kt = 0; kt < Cfg<D>::NTILE; ++kt)
-    compute_tile<D, TREE>(lds, kt, qop, o, m_used, l_part, mask, lim, sl2, i32, h, rel, dpos);
-#else
-  static_assert(!TREE, "token trees take the tile-outer path");
-  constexpr int KSTEPS = D / 16, DT = D / 32, NT = Cfg<D>::NTILE;
-  const uint16_t* kl = lds;
-  const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
-  const int kap = (i32 & ~12) | ((i32 & 4) << 1) | ((i32 & 8) >> 1);
-  f32x16 s[NT];
-#pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    f32x16 acc = {};
-    const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
-#pragma unroll
-    for (int st = 0; st < KSTEPS; ++st)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(kr + 8 * st), qop[st], acc, 0, 0, 0);
-    s[kt] = acc;
-  }
-  if (mask) {
-    keep_compute_branch<D>();
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = key_off(kt, r, h) < lim ? s[kt][r] : kNegInf;
-  }
-  float mx = s[0][0];
-#pragma unroll
-  for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const bool grow = mx != kNegInf && (m_used == kNegInf || (mx - m_used) * sl2 > kRescaleLog2);
-  if (__any(grow)) {
-    keep_compute_branch<D>();
-    const float m_new = fmaxf(m_used, mx);
-    const float alpha = m_used == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m_used - m_new) * sl2);
-    l_part *= alpha;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] *= alpha;
-    m_used = m_new;
-  }
-  const float ms = m_used == kNegInf ? 0.f : m_used * sl2;
-  bf16x8 pb[NT][2];
-  float ps = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    f32x8 p0, p1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p0[e] = __builtin_amdgcn_exp2f(s[kt][e] * sl2 - ms);
-      p1[e] = __builtin_amdgcn_exp2f(s[kt][8 + e] * sl2 - ms);
-      ps += p0[e] + p1[e];
-    }
-    pb[kt][0] = __builtin_convertvector(p0, bf16x8);
-    pb[kt][1] = __builtin_convertvector(p1, bf16x8);
-  }
-  l_part += ps;
-#pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const uint16_t* vr = vl + (32 * t + i32) * Cfg<D>::VROW + 8 * h;
-#pragma unroll
-    for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr + 32 * kt + 16 * kk), pb[kt][kk], o[t], 0, 0, 0);
-  }
-#endif
+    compute_tile<D, TREE>(lds, kt, qop, o, rr, l_part, mask, lim, sl2, i32, h, rel, dpos);
 }
 
 template <int D, bool TREE, int WAVES>
@@ -362,7 +333,8 @@ void attn_prefill_kernel(AttnArgs a) {
   f32x16 o[DT];
 #pragma unroll
   for (int tt = 0; tt < DT; ++tt) o[tt] = (f32x16){};
-  float m_used = kNegInf, l_part = 0.f;
+  RowRef rr = {0.f, kNegInf};
+  float l_part = 0.f;
 
   const cint_p bt_row = (cint_p)(a.block_table + (int64_t)it.seq * a.bt_stride);
   const int kv_end = it.kv_end;
@@ -401,7 +373,7 @@ void attn_prefill_kernel(AttnArgs a) {
     // a chunk every row of the task sees whole needs no mask; in a token tree
     // that excludes the 64 keys before the task's first row
     const bool mask = c0 + CHUNK - 1 > min_pos - (TREE ? 64 : 0) || c0 + CHUNK > kv_end;
-    compute_chunk<D, TREE>(cur, qop, o, m_used, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
+    compute_chunk<D, TREE>(cur, qop, o, rr, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
     if (more) stage_store<D>(lds + ((c + 1) & 1) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
     __syncthreads();
   }
@@ -412,7 +384,7 @@ void attn_prefill_kernel(AttnArgs a) {
   const int64_t row = it.row_begin + t;
   const int qh = kvh * G + (m - t * G);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float lse = l > 0.f ? m_used * a.scale + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+  const float lse = l > 0.f ? (rr.ref2 + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   if (it.part < 0) {
     uint16_t* dst = static_cast<uint16_t*>(a.out) + (row * hq + qh) * D + 4 * h;
