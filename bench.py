@@ -103,6 +103,92 @@ def cpu_baseline(batch, work, min_seconds=10.0):
                        f"exp single-threaded); host os.cpu_count()={os.cpu_count()}")
 
 
+def timed_forward(pm, p, q, kp, vp, bt, out, lse, stream, args, flush):
+    """W untimed then K timed ``pmattn_forward`` steps of plan ``p`` (a cache
+    flush before each). HIP events on the launch stream bracket the tasks pass
+    and the merge pass of every timed step. Returns the per-step tasks, merge
+    and step times (ms) and the host wall time of the K steps (s)."""
+    import ctypes
+
+    import torch
+    ws = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=q.device)
+    p.upload(ws, stream)
+    # Validate every tensor once through the binding, then call the two C-ABI
+    # passes with pre-marshalled arguments so that host overhead stays far
+    # below the GPU time of a step (the stream never waits for the host).
+    pm.forward_tasks(p, q, kp, vp, bt, out, lse, ws, stream)
+    pm.forward_merge(p, out, lse, ws, stream)
+    lib = pm._lib.load()
+    vptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    c_args = (p.handle, vptr(q), vptr(kp), vptr(vp), vptr(bt), vptr(out), vptr(lse), vptr(ws),
+              ws.numel(), ctypes.c_void_p(int(stream.cuda_stream)))
+    m_args = (p.handle, vptr(out), vptr(lse), vptr(ws), ws.numel(),
+              ctypes.c_void_p(int(stream.cuda_stream)))
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        st = lib.pmattn_forward_tasks(*c_args)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= lib.pmattn_forward_merge(*m_args)
+        if ev is not None:
+            ev[2].record(stream)
+        if st:
+            raise RuntimeError(lib.pmattn_last_error().decode())
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush()
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        if not args.no_flush:
+            flush()
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return ([e[0].elapsed_time(e[1]) for e in evs], [e[1].elapsed_time(e[2]) for e in evs],
+            [e[0].elapsed_time(e[2]) for e in evs], wall)
+
+
+def class_breakdown(pm, b, make_plan_for, kp, vp, conv, dev, stream, args, flush):
+    """Each query class of a mixed batch (decode, verify, prefill) planned and
+    timed alone on the same pool, with the same flush and events as the whole
+    batch. Returns {kind: {...}} with the class's time and its rates against
+    both peaks."""
+    import torch
+    import workloads as wl
+    kinds = np.array([wl.seq_kind(int(n)) for n in b.q_len])
+    res = {}
+    for kind in ("prefill", "verify", "decode"):
+        keep = (kinds == kind) & (b.q_len > 0)
+        if not keep.any():
+            continue
+        sb = wl.subset(b, keep, f"{b.name}[{kind}]")
+        w = wl.algorithmic_work(sb)
+        p = make_plan_for(sb)
+        q = conv(sb.q).to(dev)
+        bt = torch.from_numpy(sb.block_table).to(dev)
+        et = torch.bfloat16 if sb.dtype == "bf16" else torch.float32
+        out = torch.empty((sb.num_rows, sb.num_q_heads, sb.head_dim), dtype=et, device=dev)
+        lse = torch.empty((sb.num_rows, sb.num_q_heads), dtype=torch.float32, device=dev)
+        t_task, t_merge, t_step, _ = timed_forward(pm, p, q, kp, vp, bt, out, lse, stream, args, flush)
+        ms = statistics.mean(t_step)
+        gbs = w["bytes"] / (ms * 1e-3) / 1e9
+        tfs = w["flop"] / (ms * 1e-3) / 1e12
+        res[kind] = dict(seqs=int(keep.sum()), rows=sb.num_rows, ms_per_step=ms,
+                         tasks_ms=statistics.mean(t_task), merge_ms=statistics.mean(t_merge),
+                         algorithmic_bytes=w["bytes"], flop=w["flop"], gbs=gbs, tflops=tfs,
+                         hbm_frac=gbs / HBM_PEAK_GBS, mfma_frac=tfs / MFMA_BF16_PEAK_TFS)
+        log(f"[bench] class {kind} alone: {int(keep.sum())} seqs, {sb.num_rows} rows, {ms:.4f} ms/step; "
+            f"{gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% hbm), {tfs:.1f} TFLOP/s "
+            f"({100 * tfs / MFMA_BF16_PEAK_TFS:.1f}% mfma)")
+    return res
+
+
 def bench_radix(args):
     """Host cost of the radix cache manager on a workload's requests. Token ids
     follow the block sharing of the batch: blocks shared between sequences get
@@ -225,6 +311,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--no-class-breakdown", action="store_true",
+                    help="mixed batches: skip timing each query class alone")
     ap.add_argument("--num-kv-splits", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
     ap.add_argument("--work-shuffle-seed", type=int, default=0,
@@ -285,13 +373,16 @@ def main():
     out = torch.empty((b.num_rows, b.num_q_heads, b.head_dim), dtype=et, device=dev)
     lse = torch.empty((b.num_rows, b.num_q_heads), dtype=torch.float32, device=dev)
 
-    def make_plan():
-        return pm.plan(b.q_len, b.seq_len, b.q_start, b.block_table,
-                       num_pool_blocks=b.num_pool_blocks, num_q_heads=b.num_q_heads,
-                       num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
-                       scale=b.scale, num_kv_splits=b.num_kv_splits, num_cus=args.num_cus,
-                       work_shuffle_seed=args.work_shuffle_seed, tree_parent=b.tree_parent,
+    def make_plan_for(x):
+        return pm.plan(x.q_len, x.seq_len, x.q_start, x.block_table,
+                       num_pool_blocks=x.num_pool_blocks, num_q_heads=x.num_q_heads,
+                       num_kv_heads=x.num_kv_heads, head_dim=x.head_dim, dtype=x.dtype,
+                       scale=x.scale, num_kv_splits=x.num_kv_splits, num_cus=args.num_cus,
+                       work_shuffle_seed=args.work_shuffle_seed, tree_parent=x.tree_parent,
                        cascade=args.cascade)
+
+    def make_plan():
+        return make_plan_for(b)
 
     if args.op == "append":
         return bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt)
@@ -303,57 +394,14 @@ def main():
         plan_times.append(time.perf_counter() - t)
     plan_us = statistics.median(plan_times) * 1e6
     tabs = p.tables()
-    ws = torch.empty(p.workspace_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    p.upload(ws, stream)
     scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)       # 1 GiB, read to evict caches
     flush_sink = torch.empty((), dtype=torch.int64, device=dev)
 
     def flush():
         torch.sum(scratch, dim=0, dtype=torch.int64, out=flush_sink)
 
-    # Validate every tensor once through the binding, then call the two C-ABI
-    # passes with pre-marshalled arguments so that host overhead stays far
-    # below the GPU time of a step (the stream never waits for the host).
-    pm.forward_tasks(p, q, kp, vp, bt, out, lse, ws, stream)
-    pm.forward_merge(p, out, lse, ws, stream)
-    import ctypes
-    lib = pm._lib.load()
-    vptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    c_args = (p.handle, vptr(q), vptr(kp), vptr(vp), vptr(bt), vptr(out), vptr(lse), vptr(ws),
-              ws.numel(), ctypes.c_void_p(int(stream.cuda_stream)))
-    m_args = (p.handle, vptr(out), vptr(lse), vptr(ws), ws.numel(),
-              ctypes.c_void_p(int(stream.cuda_stream)))
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        st = lib.pmattn_forward_tasks(*c_args)
-        if ev is not None:
-            ev[1].record(stream)
-        st |= lib.pmattn_forward_merge(*m_args)
-        if ev is not None:
-            ev[2].record(stream)
-        if st:
-            raise RuntimeError(lib.pmattn_last_error().decode())
-
-    for _ in range(args.warmup):
-        if not args.no_flush:
-            flush()
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for k in range(args.steps):
-        if not args.no_flush:
-            flush()
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    t_task = [e[0].elapsed_time(e[1]) for e in evs]    # ms
-    t_merge = [e[1].elapsed_time(e[2]) for e in evs]
-    t_step = [e[0].elapsed_time(e[2]) for e in evs]
+    t_task, t_merge, t_step, wall = timed_forward(pm, p, q, kp, vp, bt, out, lse, stream, args, flush)
     ms_step = statistics.mean(t_step)
     ms_task = statistics.mean(t_task)
     log(f"[bench] plan {plan_us:.1f} us host; items={tabs['items'].shape[0]} "
@@ -394,6 +442,11 @@ def main():
                            algorithmic_bytes=work["bytes"], cache_flush_between_steps=not args.no_flush),
                roofline=roof, plan_host_us=plan_us, tasks_ms=ms_task,
                merge_ms=statistics.mean(t_merge))
+    kinds = {wl.seq_kind(int(n)) for n in b.q_len if n > 0}
+    if len(kinds) > 1 and not args.no_class_breakdown:
+        res["class_breakdown"] = class_breakdown(pm, b, make_plan_for, kp, vp, conv, dev, stream, args, flush)
+        alone = sum(c["ms_per_step"] for c in res["class_breakdown"].values())
+        log(f"[bench] classes alone sum to {alone:.4f} ms/step; together {ms_step:.4f} ms/step")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, work)
         log(f"[bench] cpu baseline {res['cpu_baseline']['value']:.3f} {res['cpu_baseline']['unit']}")

@@ -301,6 +301,7 @@ def check_coverage(items, q_len, q_start, num_kv_heads):
 
 CASCADE_AUTO_MEMBERS = 8
 CASCADE_AUTO_BLOCKS = 64
+CASCADE_AUTO_MIN_SPARED = 0.25   # fraction of the batch's logical keys
 
 
 def cascade_groups(q_len, q_start, block_table, group, mode=1):
@@ -317,7 +318,10 @@ def cascade_groups(q_len, q_start, block_table, group, mode=1):
     first bucket is searched first. A member's own keys start at the end of
     its deepest run. Mode 2 (automatic) makes a group only of runs with at
     least 8 members spanning at least 64 blocks since the nearest group above;
-    a run left out is folded into the ranges of the groups below it.
+    a run left out is folded into the ranges of the groups below it. Mode 2
+    then drops every group unless together they spare at least a quarter of
+    the batch's logical keys, counting (members - 1) x run length per group
+    against the sum of q_start + q_len over sequences with rows.
     """
     n = len(q_len)
     share = [int(q_start[s]) // BLOCK for s in range(n)]
@@ -349,6 +353,11 @@ def cascade_groups(q_len, q_start, block_table, group, mode=1):
                 kid_cover = end
             kids.append((bm, end, kid_cover))
         stack.extend(reversed(kids))
+    if mode == 2 and groups:
+        spared = sum((len(g[3]) - 1) * (g[1] - g[0]) for g in groups)
+        logical = sum(int(q_start[s]) + int(q_len[s]) for s in range(n) if q_len[s] > 0)
+        if spared < CASCADE_AUTO_MIN_SPARED * logical:
+            return [], np.zeros(n, np.int64)
     return groups, own_lo
 
 

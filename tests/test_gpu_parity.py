@@ -154,15 +154,19 @@ def test_full_config3_sampled_rows():
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
-def test_full_config4_sampled_rows():
+@pytest.mark.parametrize("cascade", [2, 1])
+def test_full_config4_sampled_rows(cascade):
+    """The mixed batch at full size: automatic cascade (as bench.py launches
+    it; no groups here) and every shared run grouped (cascade tasks beside
+    prefill, decode and verify tasks)."""
     b = wl.config(4)
     off = b.row_offsets()
     rng = np.random.Generator(np.random.PCG64(44))
     firsts = [int(off[s]) for s in range(16)] + [int(off[s + 1]) - 1 for s in range(16)]
     rows = np.unique(np.concatenate([np.arange(int(off[16]), b.num_rows),      # decode + verify
                                      rng.choice(int(off[16]), 64, replace=False), firsts]))
-    note(f"config 4: {b.num_rows} rows, sampling {rows.size}")
-    out, lse = run_gpu(b)
+    note(f"config 4 (cascade {cascade}): {b.num_rows} rows, sampling {rows.size}")
+    out, lse = run_gpu(b, cascade=cascade)
     compare(b, out, lse, rows=rows)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 

@@ -397,10 +397,22 @@ def test_cascade_plans_match_replica(cfg, mode):
     b = wl.config(cfg, values=False)
     t = make_plan(b, cascade=mode).tables()
     # mode 1 groups every shared run; the automatic mode leaves out the pairs
-    # of the long-decode batch and the tiny batch
-    assert (t["cascade"]["lo"].shape[0] > 0) == (mode == 1 or cfg in (4, 7))
+    # of the long-decode batch and the tiny batch, and the mixed batch's few
+    # groups (they spare 7% of its keys)
+    assert (t["cascade"]["lo"].shape[0] > 0) == (mode == 1 or cfg == 7)
     _check_cascade_plan(b, t, b.num_kv_splits, mode=mode)
 
+
+@pytest.mark.parametrize("own, grouped", [(100, True), (8000, False)])
+def test_cascade_auto_needs_a_quarter_of_the_keys_spared(own, grouped):
+    # ten decode rows on one 64-block shared run: with 100 own tokens each the
+    # group spares 9 x 1024 of 11,240 keys (82%), with 8,000 only 10%
+    seqs = [dict(q_len=1, seq_len=1024 + own, nodes=[("n", 0)]) for _ in range(10)]
+    b = wl.custom(seqs, node_blocks={("n", 0): 64}, hq=8, hkv=2, d=64, values=False)
+    t = make_plan(b, cascade=2).tables()
+    assert (t["cascade"]["lo"].shape[0] > 0) == grouped
+    _check_cascade_plan(b, t, 0, mode=2)
+    assert make_plan(b, cascade=1).tables()["cascade"]["lo"].shape[0] == 1
 
 @pytest.mark.parametrize("seed", range(5))
 def test_cascade_random_batches(seed):

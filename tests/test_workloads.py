@@ -61,3 +61,24 @@ def test_algorithmic_counts_config1():
     w = wl.algorithmic_work(wl.config(1, values=False))
     assert w["unique_kv_tokens"] == 32 + 4 * 16 and w["logical_kv_tokens"] == 4 * 48
     assert w["visible_pairs"] == 4 * 48 and w["flop"] == 4 * 64 * 1 * 192
+
+
+def test_subset_keeps_rows_and_pool():
+    """A class-only sub-batch carries its sequences' rows unchanged, so the
+    oracle gives it exactly the rows the whole batch gives them."""
+    import oracle
+    b = wl.custom([dict(q_len=1, seq_len=40, q_start=39), dict(q_len=5, seq_len=30, q_start=25),
+                   dict(q_len=20, seq_len=50, q_start=30), dict(q_len=1, seq_len=17, q_start=16)],
+                  hq=4, hkv=2, d=8, dtype="bf16", seed=3)
+    kinds = [wl.seq_kind(int(n)) for n in b.q_len]
+    assert kinds == ["decode", "verify", "prefill", "decode"]
+    full_o, full_l = oracle.attend(b)
+    off = b.row_offsets()
+    for kind in ("decode", "verify", "prefill"):
+        keep = np.array([k == kind for k in kinds])
+        sb = wl.subset(b, keep, kind)
+        assert sb.k_pool is b.k_pool and sb.num_pool_blocks == b.num_pool_blocks
+        rows = np.concatenate([np.arange(off[s], off[s + 1]) for s in np.nonzero(keep)[0]])
+        o, lse = oracle.attend(sb)
+        np.testing.assert_array_equal(o, full_o[rows])
+        np.testing.assert_array_equal(lse, full_l[rows])

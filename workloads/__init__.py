@@ -417,6 +417,25 @@ def private_copy(b: Batch) -> Batch:
                      v_pool=np.concatenate(new_v), name=b.name + "+private")
 
 
+def seq_kind(q_len: int) -> str:
+    """Query class of a sequence by its row count: one row is a decode step,
+    up to 16 rows a speculative verify, more a prefill chunk."""
+    return "decode" if q_len == 1 else "verify" if q_len <= 16 else "prefill"
+
+
+def subset(b: Batch, keep: np.ndarray, name: str) -> Batch:
+    """Copy of ``b`` holding only the sequences where ``keep`` is true (their
+    query rows, lengths and block-table rows); the pool is shared unchanged."""
+    keep = np.asarray(keep, dtype=bool)
+    off = b.row_offsets()
+    rows = np.concatenate([np.arange(off[s], off[s + 1]) for s in np.nonzero(keep)[0]] +
+                          [np.zeros(0, dtype=np.int64)])
+    return b.replace(name=name, q_len=b.q_len[keep].copy(), seq_len=b.seq_len[keep].copy(),
+                     q_start=b.q_start[keep].copy(), block_table=b.block_table[keep].copy(),
+                     q=b.q[rows] if b.q is not None else None,
+                     tree_parent=None if b.tree_parent is None else b.tree_parent[rows].copy())
+
+
 def relabel(b: Batch, seed: int) -> Batch:
     """Copy of ``b`` with physical block ids permuted (pool and tables alike)."""
     rng = np.random.Generator(np.random.PCG64(seed))
