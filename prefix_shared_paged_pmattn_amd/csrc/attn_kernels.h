@@ -63,10 +63,10 @@ struct AppendArgs {
 };
 
 // Host launchers (forward.hip).
-hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, hipStream_t st);
-// concurrent: wave tasks of the same plan run beside these workgroups (on a
-// second stream); the kernel then takes 2 waves per SIMD instead of 3.
-hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, bool concurrent, hipStream_t st);
+// concurrent: workgroup tasks of the same plan run beside these waves (on a
+// second stream); 16-row tasks then take the 3-waves-per-SIMD variant.
+hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, hipStream_t st);
+hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
 hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st);

@@ -28,13 +28,13 @@
 //   computation); V lanes of keys past the task's end are zeroed when the chunk
 //   is staged, so pool slots no row can see may hold NaN.
 // * Occupancy is a template parameter: three waves per SIMD (168 VGPRs, 37
-//   KiB of LDS per workgroup) when the workgroup tasks have the chip to
-//   themselves, so that LDS latency and one wave's softmax VALU hide behind
-//   the other waves' MFMA; two when one-wave tasks of the same plan run
-//   beside them, and for token trees (whose masks spill at three). Measured:
-//   few-shot prefill 907 vs 813 TFLOP/s (3 vs 2), mixed batch 0.78 vs 0.84
-//   ms (2 vs 3), tree verify 2 waves 19% faster. 64-key chunks at 2 waves
-//   were 3% slower than 32-key ones.
+//   KiB of LDS per workgroup), so that LDS latency and one wave's softmax
+//   VALU hide behind the other waves' MFMA; two for token trees (whose masks
+//   spill at three). Beside one-wave tasks of the same plan the kernel keeps
+//   three, and those tasks are built to fit the same register share.
+//   Measured: few-shot prefill 907 vs 813 TFLOP/s (3 vs 2), tree verify 2
+//   waves 19% faster. 64-key chunks at 2 waves were 3% slower than 32-key
+//   ones.
 // * The register staging of the next chunk uses clang vector types: with
 //   HIP's uint4 the copies are memcpys of a union, the staging array stays
 //   in private memory and the backend moves it to LDS, so every chunk's loads
@@ -414,18 +414,17 @@ void attn_prefill_kernel(AttnArgs a) {
 
 namespace {
 template <int D>
-void launch_d(const AttnArgs& a, bool concurrent, hipStream_t st) {
+void launch_d(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.item_count), block(256);
   if (a.row_mask) hipLaunchKernelGGL((attn_prefill_kernel<D, true, 2>), grid, block, 0, st, a);
-  else if (concurrent) hipLaunchKernelGGL((attn_prefill_kernel<D, false, 2>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((attn_prefill_kernel<D, false, 3>), grid, block, 0, st, a);
 }
 }  // namespace
 
-hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, bool concurrent, hipStream_t st) {
+hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
-  if (head_dim == 128) launch_d<128>(a, concurrent, st);
-  else launch_d<64>(a, concurrent, st);
+  if (head_dim == 128) launch_d<128>(a, st);
+  else launch_d<64>(a, st);
   return hipGetLastError();
 }
 

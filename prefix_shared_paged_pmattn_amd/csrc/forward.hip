@@ -1,6 +1,7 @@
 // Launcher half of the C ABI: uploads a plan's work list into the caller's
 // workspace and launches the tile-task kernels and the merge on the caller's
 // stream. All device memory is the caller's; nothing here allocates.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <unordered_map>
@@ -18,16 +19,21 @@ constexpr float kLog2e = 1.44269504088896340736f;
 std::mutex g_ws_mu;
 std::unordered_map<const void*, uint64_t> g_ws_owner;
 
-// Per-device auxiliary stream (default priority) and fork/join events: a plan
+// Per-device auxiliary streams (default priority) and fork/join events: a plan
 // that mixes wave tasks (decode/verify, KV-stream bound) and workgroup tasks
-// (prefill, MFMA bound) runs the two kinds concurrently, the wave tasks on the
-// auxiliary stream, joined back into the caller's stream before the merge.
+// (prefill, MFMA bound) runs the two kinds concurrently, the wave-task classes
+// on the auxiliary streams, joined back into the caller's stream before the
+// merge.
 // The record/wait sequence is enqueued under a mutex, so concurrent callers
 // never interleave the shared events (a wait binds to the latest record at
 // enqueue time).
+#ifndef PMATTN_AUX_STREAMS
+#define PMATTN_AUX_STREAMS 2
+#endif
+constexpr int kAux = PMATTN_AUX_STREAMS;
 struct DeviceAux {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipStream_t stream[kAux] = {};
+  hipEvent_t fork = nullptr, join[kAux] = {};
 };
 std::mutex g_aux_mu;
 std::unordered_map<int, DeviceAux> g_aux;
@@ -144,8 +150,8 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
       ac.row_mask = nullptr;
     }
     if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);
-    if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, concurrent, s);
-    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, s);
+    if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
+    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, concurrent, s);
   };
   if (!concurrent) {
     for (size_t c = 0; c < P.class_rows.size(); ++c) {
@@ -159,26 +165,36 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lk(g_aux_mu);
   DeviceAux& aux = g_aux[dev];
-  if (!aux.stream) {
-    if ((e = hipStreamCreateWithFlags(&aux.stream, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&aux.fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&aux.join, hipEventDisableTiming)) != hipSuccess) {
+  if (!aux.fork) {
+    e = hipEventCreateWithFlags(&aux.fork, hipEventDisableTiming);
+    for (int i = 0; i < kAux && e == hipSuccess; ++i)
+      if ((e = hipStreamCreateWithFlags(&aux.stream[i], hipStreamNonBlocking)) == hipSuccess)
+        e = hipEventCreateWithFlags(&aux.join[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
       g_aux.erase(dev);
       return hip_fail(e, "auxiliary stream setup");
     }
   }
-  if ((e = hipEventRecord(aux.fork, st)) != hipSuccess ||
-      (e = hipStreamWaitEvent(aux.stream, aux.fork, 0)) != hipSuccess)
-    return hip_fail(e, "stream fork");
+  // wave-task classes in turn on the auxiliary streams (decode beside verify
+  // beside the workgroup tasks), forking no more streams than there are such
+  // classes: an idle fork and join measured 10 us on a 0.12 ms step
+  int n_wave = 0;
+  for (int32_t rows : P.class_rows) n_wave += rows <= kMaxWaveRows;
+  const int na = std::min(kAux, n_wave);
+  if ((e = hipEventRecord(aux.fork, st)) != hipSuccess) return hip_fail(e, "stream fork");
+  for (int i = 0; i < na; ++i)
+    if ((e = hipStreamWaitEvent(aux.stream[i], aux.fork, 0)) != hipSuccess) return hip_fail(e, "stream fork");
+  int k = 0;
   for (size_t c = 0; c < P.class_rows.size(); ++c)
-    if (P.class_rows[c] <= kMaxWaveRows && (e = launch_class(c, aux.stream)) != hipSuccess)
+    if (P.class_rows[c] <= kMaxWaveRows && (e = launch_class(c, aux.stream[k++ % na])) != hipSuccess)
       return hip_fail(e, "attention kernel launch (wave tasks)");
   for (size_t c = 0; c < P.class_rows.size(); ++c)
     if (P.class_rows[c] > kMaxWaveRows && (e = launch_class(c, st)) != hipSuccess)
       return hip_fail(e, "attention kernel launch (workgroup tasks)");
-  if ((e = hipEventRecord(aux.join, aux.stream)) != hipSuccess ||
-      (e = hipStreamWaitEvent(st, aux.join, 0)) != hipSuccess)
-    return hip_fail(e, "stream join");
+  for (int i = 0; i < na; ++i)
+    if ((e = hipEventRecord(aux.join[i], aux.stream[i])) != hipSuccess ||
+        (e = hipStreamWaitEvent(st, aux.join[i], 0)) != hipSuccess)
+      return hip_fail(e, "stream join");
   return PMATTN_OK;
 }
 
