@@ -115,7 +115,8 @@ class Plan:
                          splits=arr(t.cascade_splits, t.num_cascade)),
             virtual_row_src=arr(t.virtual_row_src, t.num_virtual_rows),
             rec_index=arr(t.rec_index, t.num_rec_index),
-            slot_begin=arr(t.slot_begin, t.num_slots + 1) if t.num_slots else np.zeros(0, np.int32))
+            slot_begin=arr(t.slot_begin, t.num_slots + 1) if t.num_slots else np.zeros(0, np.int32),
+            class_stream=arr(t.class_stream, t.num_classes))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the work list into ``workspace``."""

@@ -80,6 +80,7 @@ class PlanTables(ctypes.Structure):
         ("rec_index", _i32p),
         ("num_slots", ctypes.c_int32),
         ("slot_begin", _i32p),
+        ("class_stream", _i32p),
     ]
 
 

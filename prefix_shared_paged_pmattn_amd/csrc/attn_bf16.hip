@@ -72,7 +72,15 @@ struct Chunk {
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
+// STREAM: no other sequence's task reads these blocks, so the loads carry
+// the non-temporal hint and leave the caches to data that is read again.
+template <bool STREAM, typename T>
+__device__ __forceinline__ T ld_kv(const uint16_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
+template <int D, bool STREAM>
 __device__ __forceinline__ void load_chunk(Chunk<D>& ch, const uint16_t* __restrict__ kpool,
                                            const uint16_t* __restrict__ vpool, int blk0, int blk1,
                                            int kvh, int hkv, int i, int g) {
@@ -82,14 +90,14 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& ch, const uint16_t* __restr
     const int64_t bk = c ? blk1 : blk0;
     const uint16_t* kp = kpool + ((bk * hkv + kvh) * (D / 8) + g) * 128 + 8 * i;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) ch.k[c][s] = ld16(kp + 512 * s);
+    for (int s = 0; s < KS; ++s) ch.k[c][s] = __builtin_bit_cast(bf16x8, ld_kv<STREAM, u32x4>(kp + 512 * s));
   }
   const uint16_t* vp0 = vpool + (((int64_t)blk0 * hkv + kvh) * D + i) * 16 + 4 * g;
   const uint16_t* vp1 = vpool + (((int64_t)blk1 * hkv + kvh) * D + i) * 16 + 4 * g;
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
-    const u32x2 x0 = *reinterpret_cast<const u32x2*>(vp0 + 256 * t);
-    const u32x2 x1 = *reinterpret_cast<const u32x2*>(vp1 + 256 * t);
+    const u32x2 x0 = ld_kv<STREAM, u32x2>(vp0 + 256 * t);
+    const u32x2 x1 = ld_kv<STREAM, u32x2>(vp1 + 256 * t);
     ch.v[t] = __builtin_bit_cast(bf16x8, (u32x4){x0.x, x0.y, x1.x, x1.y});
   }
 }
@@ -248,7 +256,7 @@ struct Depth {
 constexpr int kWavesPerWg = kWaveTasksPerWg;
 
 // One task (item idx) on one wave.
-template <int D, int NT, bool TREE, bool CONC>
+template <int D, int NT, bool TREE, bool CONC, bool STREAM>
 __device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
   constexpr int KS = D / 32, DT = D / 16;
   const pmattn_work_item it = load_item(a.items, idx);
@@ -323,7 +331,7 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
     int c0 = it.kv_begin, b0, b1;
     chunk_ids(c0, b0, b1);
     for (int k = 0; k < nch; ++k) {
-      load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
+      load_chunk<D, STREAM>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
       chunk_ids(c0 + 32, b0, b1);
       zero_tail_v<D>(A, c0, kv_end, g);
       compute_chunk<D, NT, TREE>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g, tr);
@@ -342,9 +350,9 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
     Chunk<D> A, B;
     int c0 = it.kv_begin, b0, b1;
     chunk_ids(c0, b0, b1);
-    load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
+    load_chunk<D, STREAM>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
     chunk_ids(c0 + 32, b0, b1);
-    load_chunk<D>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
+    load_chunk<D, STREAM>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
     // issue_barrier() pins each chunk's loads to the point where they are
     // issued (a compiler memory barrier plus a scheduling barrier), so that the
     // optimizer can neither sink them next to their first use nor hoist the
@@ -354,12 +362,12 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
       chunk_ids(c0 + 64, b0, b1);
       zero_tail_v<D>(A, c0, kv_end, g);
       compute_chunk<D, NT, TREE>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g, tr);
-      load_chunk<D>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
+      load_chunk<D, STREAM>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
       issue_barrier();
       chunk_ids(c0 + 96, b0, b1);
       zero_tail_v<D>(B, c0 + 32, kv_end, g);
       compute_chunk<D, NT, TREE>(B, qop, o, m_run, l_run, lim_base, c0 + 32, sl2, g, tr);
-      load_chunk<D>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
+      load_chunk<D, STREAM>(B, kpool, vpool, b0, b1, kvh, hkv, i, g);
       issue_barrier();
       c0 += 64;
     }
@@ -402,14 +410,14 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
 // plans, 16-row tasks only), its tasks [slot_begin[w], slot_begin[w + 1]) one
 // after another. (The loop stays out of the larger tiles, whose 64-row
 // variant it pushes into spilling.)
-template <int D, int NT, bool TREE, bool CONC>
+template <int D, int NT, bool TREE, bool CONC, bool STREAM>
 __global__ __launch_bounds__(64 * kWavesPerWg) __attribute__((amdgpu_waves_per_eu(WavesPerEu<NT, CONC>::value, 8)))
 void attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWavesPerWg + wave;
   if constexpr (NT != 1) {
-    if (w < a.item_count) run_task<D, NT, TREE, CONC>(a, w, lane);
+    if (w < a.item_count) run_task<D, NT, TREE, CONC, STREAM>(a, w, lane);
     return;
   }
   int first, last;
@@ -423,33 +431,37 @@ void attn_bf16_kernel(AttnArgs a) {
     first = w;
     last = w + 1;
   }
-  for (int idx = first; idx < last; ++idx) run_task<D, NT, TREE, CONC>(a, idx, lane);
+  for (int idx = first; idx < last; ++idx) run_task<D, NT, TREE, CONC, STREAM>(a, idx, lane);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, hipStream_t st) {
+hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, bool stream,
+                            hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
   const int waves = a.slot_begin && class_rows <= 16 ? a.slot_count : a.item_count;
   const dim3 grid((waves + kWavesPerWg - 1) / kWavesPerWg), block(64 * kWavesPerWg);
-#define PMATTN_LAUNCH(D, NT, CONC)                                                            \
-  do {                                                                                       \
-    if (a.row_mask) hipLaunchKernelGGL((attn_bf16_kernel<D, NT, true, CONC>), grid, block, 0, st, a); \
-    else hipLaunchKernelGGL((attn_bf16_kernel<D, NT, false, CONC>), grid, block, 0, st, a);  \
+#define PMATTN_LAUNCH(D, NT, CONC, STREAM)                                                            \
+  do {                                                                                               \
+    if (a.row_mask) hipLaunchKernelGGL((attn_bf16_kernel<D, NT, true, CONC, STREAM>), grid, block, 0, st, a); \
+    else hipLaunchKernelGGL((attn_bf16_kernel<D, NT, false, CONC, STREAM>), grid, block, 0, st, a);  \
   } while (0)
-  if (head_dim == 128) {
-    if (class_rows <= 16) {
-      if (concurrent) PMATTN_LAUNCH(128, 1, true);
-      else PMATTN_LAUNCH(128, 1, false);
-    } else if (class_rows <= 32) PMATTN_LAUNCH(128, 2, false);
-    else PMATTN_LAUNCH(128, 4, false);
-  } else {
-    if (class_rows <= 16) {
-      if (concurrent) PMATTN_LAUNCH(64, 1, true);
-      else PMATTN_LAUNCH(64, 1, false);
-    } else if (class_rows <= 32) PMATTN_LAUNCH(64, 2, false);
-    else PMATTN_LAUNCH(64, 4, false);
-  }
+  // 16- and 32-row tasks stream unshared KV; 64-row tasks always cache it
+#define PMATTN_LAUNCH_D(D)                                             \
+  do {                                                                \
+    if (class_rows <= 16) {                                           \
+      if (concurrent && stream) PMATTN_LAUNCH(D, 1, true, true);      \
+      else if (concurrent) PMATTN_LAUNCH(D, 1, true, false);          \
+      else if (stream) PMATTN_LAUNCH(D, 1, false, true);              \
+      else PMATTN_LAUNCH(D, 1, false, false);                         \
+    } else if (class_rows <= 32) {                                    \
+      if (stream) PMATTN_LAUNCH(D, 2, false, true);                   \
+      else PMATTN_LAUNCH(D, 2, false, false);                         \
+    } else PMATTN_LAUNCH(D, 4, false, false);                         \
+  } while (0)
+  if (head_dim == 128) PMATTN_LAUNCH_D(128);
+  else PMATTN_LAUNCH_D(64);
+#undef PMATTN_LAUNCH_D
 #undef PMATTN_LAUNCH
   return hipGetLastError();
 }

@@ -65,7 +65,9 @@ struct AppendArgs {
 // Host launchers (forward.hip).
 // concurrent: workgroup tasks of the same plan run beside these waves (on a
 // second stream); 16-row tasks then take the 3-waves-per-SIMD variant.
-hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, hipStream_t st);
+// stream: no other sequence reads the class's KV blocks (non-temporal loads).
+hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, bool stream,
+                            hipStream_t st);
 hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);

@@ -151,7 +151,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     }
     if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);
     if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
-    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, concurrent, s);
+    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, concurrent, P.class_stream[c] != 0, s);
   };
   if (!concurrent) {
     for (size_t c = 0; c < P.class_rows.size(); ++c) {

@@ -43,6 +43,9 @@ struct Plan {
   std::vector<int32_t> num_splits, split_offset, split_begin, split_end;
   std::vector<pmattn_work_item> items;
   std::vector<int32_t> class_rows, class_begin, class_cascade;
+  // per class: 1 when no block its tasks read is read by another sequence's
+  // tasks (the kernel then streams K/V with non-temporal loads)
+  std::vector<int32_t> class_stream;
   std::vector<pmattn_merge_row> merge_rows;
   int32_t merge_max_parts = 0;  // largest nparts of any merge row
   // equal-work decode plans: wave w runs tasks [slot_begin[w], slot_begin[w + 1])

@@ -468,3 +468,40 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     assert declared == {n for n, _, _ in _lib.SIGNATURES}
     assert pm.version() == "0.1.0"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_streaming_classes_match_replica(cfg, mode):
+    """The per-class non-temporal flag equals the replica's reading of the
+    exported work list: no block of the class is read for two sequences."""
+    b = wl.config(cfg, values=False)
+    t = make_plan(b, cascade=mode).tables()
+    want = R.streaming_classes(t["items"], t["class_begin"], t["class_cascade"], b.block_table)
+    assert t["class_stream"].tolist() == want.tolist()
+    if cfg == 2:
+        assert want.tolist() == [1]           # private blocks only
+    if cfg == 5 and mode != 1:
+        assert want.tolist() == [0]           # turns shared in pairs (grouped only when forced)
+    if cfg == 7 and mode:
+        # the cascade reads the prompt once; the members' own ranges are private
+        assert [s for s, c in zip(want, t["class_cascade"]) if not c] == [1]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_streaming_classes_random_batches(seed):
+    rng = np.random.Generator(np.random.PCG64(500 + seed))
+    nodes = {("n", k): int(rng.integers(1, 5)) for k in range(4)}
+    seqs = []
+    for _ in range(int(rng.integers(2, 12))):
+        path = [("n", int(k)) for k in sorted(rng.choice(4, size=int(rng.integers(0, 3)), replace=False))]
+        shared = sum(nodes[n] for n in path) * 16
+        ql = int(rng.choice([1, 1, 3, 5, 20, 70]))
+        seqs.append(dict(q_len=ql, seq_len=shared + int(rng.integers(0, 60)) + ql, nodes=path))
+    b = wl.custom(seqs, node_blocks=nodes, hq=8, hkv=2, d=64, values=False)
+    for mode in (0, 1, 2):
+        for splits in (0, 3):
+            bb = b.replace(num_kv_splits=splits)
+            t = make_plan(bb, cascade=mode).tables()
+            want = R.streaming_classes(t["items"], t["class_begin"], t["class_cascade"], bb.block_table)
+            assert t["class_stream"].tolist() == want.tolist()
