@@ -235,12 +235,15 @@ typedef struct pmattn_plan_tables {
    * (one task per wave). */
   int32_t num_slots;
   const int32_t* slot_begin;        /* [num_slots + 1] */
-  /* [num_classes] 1: no KV block a task of the class reads is also read by a
-   * task of another sequence (readers: the item's sequence, or for cascade
-   * classes the virtual sequence of the item's first virtual row). Such a
-   * class streams its K/V with non-temporal loads; shared blocks stay
-   * cacheable for their other readers. */
+  /* [num_classes] 1: every task of the class streams, 0: none, 2: some
+   * (see item_stream). */
   const int32_t* class_stream;
+  /* [num_items] 1: no KV block the task reads is also read by a task of
+   * another sequence (readers: the item's sequence, or for cascade classes
+   * the virtual sequence of the item's first virtual row). Such a task loads
+   * its K/V with the non-temporal hint (one-wave kernel); shared blocks stay
+   * cacheable for their other readers. */
+  const int32_t* item_stream;
 } pmattn_plan_tables;
 
 /* Build a plan on the host. Validates the batch (see pmattn_plan_desc),

@@ -466,13 +466,14 @@ def check_coverage_cascade(items, class_cascade, class_begin, vrow_src, q_len, q
             assert cur.get((row, g), 0) == int(row_pos[row]) + 1, f"row {row} kv head {g} not covered"
 
 
-def streaming_classes(items, class_begin, class_cascade, block_table):
-    """Which task classes may stream their KV with non-temporal loads: those
-    none of whose tasks reads a physical block that a task of another reader
-    also reads. A task's reader is its sequence (item column 0), or, in a
-    cascade class, its virtual sequence, named by its first virtual row
-    (item column 2); a task reads the blocks that hold keys
-    [kv_begin, kv_end) (columns 5 and 6) of its block-table row."""
+def streaming_tasks(items, class_begin, class_cascade, block_table):
+    """Which tasks may stream their KV with non-temporal loads, and so which
+    classes: a task streams when no physical block it reads is also read by a
+    task of another reader. A task's reader is its sequence (item column 0),
+    or, in a cascade class, its virtual sequence, named by its first virtual
+    row (item column 2); a task reads the blocks that hold keys
+    [kv_begin, kv_end) (columns 5 and 6) of its block-table row. Returns
+    (per-task flags, per-class 1 = all stream / 0 = none / 2 = some)."""
     readers = {}
     reads = []
     for c in range(len(class_begin) - 1):
@@ -480,11 +481,12 @@ def streaming_classes(items, class_begin, class_cascade, block_table):
             seq, _, row0, _, _, lo, hi, _ = (int(x) for x in it[:8])
             who = ("virtual", row0) if class_cascade[c] else ("seq", seq)
             blocks = {int(block_table[seq][j]) for j in range(lo // BLOCK, -(-hi // BLOCK))}
-            reads.append((c, blocks))
+            reads.append(blocks)
             for b in blocks:
                 readers.setdefault(b, set()).add(who)
-    out = np.ones(len(class_begin) - 1, np.int32)
-    for c, blocks in reads:
-        if any(len(readers[b]) > 1 for b in blocks):
-            out[c] = 0
-    return out
+    tasks = np.array([int(all(len(readers[b]) == 1 for b in blocks)) for blocks in reads], np.int32)
+    classes = []
+    for c in range(len(class_begin) - 1):
+        part = tasks[class_begin[c]:class_begin[c + 1]]
+        classes.append(1 if part.all() else 0 if not part.any() else 2)
+    return tasks, np.array(classes, np.int32)

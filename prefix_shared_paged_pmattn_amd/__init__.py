@@ -83,7 +83,7 @@ class Plan:
         _check(L.load().pmattn_plan_export(self._h, ctypes.byref(t)))
 
         def arr(ptr, n):
-            return np.ctypeslib.as_array(ptr, shape=(n,)).copy() if n else np.zeros(0, np.int32)
+            return np.ctypeslib.as_array(ptr, shape=(n,)).copy() if n and ptr else np.zeros(0, np.int32)
 
         nsp = int(np.ctypeslib.as_array(t.split_offset, shape=(t.num_seqs + 1,))[-1])
         items = np.zeros((t.num_items, 8), np.int32)
@@ -116,7 +116,8 @@ class Plan:
             virtual_row_src=arr(t.virtual_row_src, t.num_virtual_rows),
             rec_index=arr(t.rec_index, t.num_rec_index),
             slot_begin=arr(t.slot_begin, t.num_slots + 1) if t.num_slots else np.zeros(0, np.int32),
-            class_stream=arr(t.class_stream, t.num_classes))
+            class_stream=arr(t.class_stream, t.num_classes),
+            item_stream=arr(t.item_stream, t.num_items))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the work list into ``workspace``."""

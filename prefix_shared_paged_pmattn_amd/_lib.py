@@ -81,6 +81,7 @@ class PlanTables(ctypes.Structure):
         ("num_slots", ctypes.c_int32),
         ("slot_begin", _i32p),
         ("class_stream", _i32p),
+        ("item_stream", _i32p),
     ]
 
 

@@ -26,6 +26,8 @@ struct AttnArgs {
   float* part_lse;               // [records]
   const int32_t* slot_begin;     // one-wave kernel: wave w runs tasks [slot_begin[w], slot_begin[w+1]);
                                  // null: wave w runs task w
+  const int32_t* item_stream;    // per task of this launch: 1 = non-temporal K/V loads (one-wave
+                                 // kernel, classes whose tasks differ)
   int32_t slot_count;
   int32_t item_count;
   int32_t bt_stride;
@@ -65,8 +67,9 @@ struct AppendArgs {
 // Host launchers (forward.hip).
 // concurrent: workgroup tasks of the same plan run beside these waves (on a
 // second stream); 16-row tasks then take the 3-waves-per-SIMD variant.
-// stream: no other sequence reads the class's KV blocks (non-temporal loads).
-hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, bool stream,
+// stream: 1 no other sequence reads the class's KV blocks (non-temporal
+// loads), 0 some do (cached loads), 2 per task (a.item_stream).
+hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, int stream,
                             hipStream_t st);
 hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);

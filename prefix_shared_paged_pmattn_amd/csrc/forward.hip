@@ -114,6 +114,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.part_o = reinterpret_cast<float*>(ws + P.off_part_o);
   a.part_lse = reinterpret_cast<float*>(ws + P.off_part_lse);
   a.slot_begin = nullptr;
+  a.item_stream = nullptr;
   a.slot_count = 0;
   a.bt_stride = P.bt_stride;
   a.hq = P.hq;
@@ -137,6 +138,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   auto launch_class = [&](size_t c, hipStream_t s) -> hipError_t {
     AttnArgs ac = a;
     ac.items = items + P.class_begin[c];
+    ac.item_stream = reinterpret_cast<const int32_t*>(ws + P.off_istream) + P.class_begin[c];
     ac.item_count = P.class_begin[c + 1] - P.class_begin[c];
     if ((int)c == P.slot_class) {
       // equal-work decode tasks: one slot per wave
@@ -151,7 +153,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     }
     if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);
     if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
-    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, concurrent, P.class_stream[c] != 0, s);
+    return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, concurrent, P.class_stream[c], s);
   };
   if (!concurrent) {
     for (size_t c = 0; c < P.class_rows.size(); ++c) {

@@ -661,15 +661,16 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     P.class_begin.push_back((int32_t)P.items.size());
   }
 
-  // ---- streaming classes: KV no other sequence reads ------------------------
+  // ---- streaming tasks: KV no other sequence reads -----------------------------
   // A block read by the tasks of two sequences (a shared prefix) is worth
-  // keeping in the caches: the second reader often finds it there. A class
+  // keeping in the caches: the second reader often finds it there. A task
   // none of whose blocks is read that way streams its K/V with non-temporal
   // loads. Readers are sequences; a cascade task reads for its virtual
-  // sequence, identified by its first virtual row. (Measured on MI355X: the
-  // 64-sequence decode batch 69% -> 77% of HBM peak with non-temporal K/V;
-  // the long-decode batch, whose blocks are shared in pairs, 69.5% -> 63.4%
-  // had it streamed.)
+  // sequence, identified by its first virtual row. A class is 1 when all its
+  // tasks stream, 0 when none does, 2 when the kernel must look up each
+  // task's flag. (Measured on MI355X: the 64-sequence decode batch 69% -> 77%
+  // of HBM peak with non-temporal K/V; the long-decode batch, whose blocks
+  // are shared in pairs, 69.5% -> 63.4% had all of it streamed.)
   {
     std::vector<int32_t> first_reader(d->num_pool_blocks, -1);
     std::vector<char> multi(d->num_pool_blocks, 0);
@@ -686,11 +687,17 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           else if (first_reader[b] != reader) multi[b] = 1;
         });
       }
+    P.item_stream.assign(P.items.size(), 0);
     for (size_t c = 0; c + 1 < P.class_begin.size(); ++c) {
-      bool alone = true;
-      for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1] && alone; ++i)
+      int32_t n = 0;
+      for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
+        bool alone = true;
         for_blocks(P.items[i], [&](int32_t b) { alone = alone && !multi[b]; });
-      P.class_stream.push_back(alone ? 1 : 0);
+        P.item_stream[i] = alone ? 1 : 0;
+        n += P.item_stream[i];
+      }
+      const int32_t total = P.class_begin[c + 1] - P.class_begin[c];
+      P.class_stream.push_back(n == total ? 1 : n == 0 ? 0 : 2);
     }
   }
 
@@ -704,7 +711,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.off_rec_index = align_up(P.off_append + P.append_units.size() * sizeof(pmattn_append_unit), kAlign);
   P.off_vrow = align_up(P.off_rec_index + P.rec_index.size() * sizeof(int32_t), kAlign);
   P.off_slot = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
-  P.off_qv = align_up(P.off_slot + P.slot_begin.size() * sizeof(int32_t), kAlign);
+  P.off_istream = align_up(P.off_slot + P.slot_begin.size() * sizeof(int32_t), kAlign);
+  P.off_qv = align_up(P.off_istream + P.item_stream.size() * sizeof(int32_t), kAlign);
   const size_t elem = P.dtype == PMATTN_BF16 ? 2 : 4;
   P.off_part_o = align_up(P.off_qv + P.vrow_src.size() * (size_t)P.hq * P.head_dim * elem, kAlign);
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
@@ -728,6 +736,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     std::memcpy(P.upload_blob.data() + P.off_vrow, P.vrow_src.data(), P.vrow_src.size() * sizeof(int32_t));
   if (!P.slot_begin.empty())
     std::memcpy(P.upload_blob.data() + P.off_slot, P.slot_begin.data(), P.slot_begin.size() * sizeof(int32_t));
+  if (!P.item_stream.empty())
+    std::memcpy(P.upload_blob.data() + P.off_istream, P.item_stream.data(), P.item_stream.size() * sizeof(int32_t));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -805,6 +815,7 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->num_slots = P.slot_begin.empty() ? 0 : (int32_t)P.slot_begin.size() - 1;
   t->slot_begin = P.slot_begin.empty() ? nullptr : P.slot_begin.data();
   t->class_stream = P.class_stream.data();
+  t->item_stream = P.item_stream.data();
   return PMATTN_OK;
 }
 

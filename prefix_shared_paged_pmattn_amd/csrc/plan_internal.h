@@ -43,9 +43,10 @@ struct Plan {
   std::vector<int32_t> num_splits, split_offset, split_begin, split_end;
   std::vector<pmattn_work_item> items;
   std::vector<int32_t> class_rows, class_begin, class_cascade;
-  // per class: 1 when no block its tasks read is read by another sequence's
-  // tasks (the kernel then streams K/V with non-temporal loads)
-  std::vector<int32_t> class_stream;
+  // per task: 1 when no block it reads is read by another sequence's tasks
+  // (the kernel then streams its K/V with non-temporal loads); per class: 1
+  // all tasks, 0 none, 2 some
+  std::vector<int32_t> item_stream, class_stream;
   std::vector<pmattn_merge_row> merge_rows;
   int32_t merge_max_parts = 0;  // largest nparts of any merge row
   // equal-work decode plans: wave w runs tasks [slot_begin[w], slot_begin[w + 1])
@@ -64,11 +65,12 @@ struct Plan {
   std::vector<pmattn_append_unit> append_units;
   std::string append_conflict;
   // workspace layout (bytes): [items | merge rows | row masks | append units |
-  // record index | virtual row sources | wave slots | gathered Q of virtual
-  // rows | partial O | partial lse]; everything before the gathered Q is
-  // uploaded
+  // record index | virtual row sources | wave slots | task stream flags |
+  // gathered Q of virtual rows | partial O | partial lse]; everything before
+  // the gathered Q is uploaded
   size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_rec_index = 0,
-         off_vrow = 0, off_slot = 0, off_qv = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
+         off_vrow = 0, off_slot = 0, off_istream = 0, off_qv = 0, off_part_o = 0, off_part_lse = 0,
+         ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 

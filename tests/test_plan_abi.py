@@ -477,12 +477,16 @@ def test_streaming_classes_match_replica(cfg, mode):
     exported work list: no block of the class is read for two sequences."""
     b = wl.config(cfg, values=False)
     t = make_plan(b, cascade=mode).tables()
-    want = R.streaming_classes(t["items"], t["class_begin"], t["class_cascade"], b.block_table)
+    tasks, want = R.streaming_tasks(t["items"], t["class_begin"], t["class_cascade"], b.block_table)
+    assert t["item_stream"].tolist() == tasks.tolist()
     assert t["class_stream"].tolist() == want.tolist()
     if cfg == 2:
         assert want.tolist() == [1]           # private blocks only
     if cfg == 5 and mode != 1:
-        assert want.tolist() == [0]           # turns shared in pairs (grouped only when forced)
+        # turns 1-3 shared in pairs, turn 4 private: partitions 12-15 stream
+        assert want.tolist() == [2]
+        it = t["items"]
+        assert (tasks == (it[:, 5] >= 24576)).all()
     if cfg == 7 and mode:
         # the cascade reads the prompt once; the members' own ranges are private
         assert [s for s, c in zip(want, t["class_cascade"]) if not c] == [1]
@@ -503,5 +507,6 @@ def test_streaming_classes_random_batches(seed):
         for splits in (0, 3):
             bb = b.replace(num_kv_splits=splits)
             t = make_plan(bb, cascade=mode).tables()
-            want = R.streaming_classes(t["items"], t["class_begin"], t["class_cascade"], bb.block_table)
+            tasks, want = R.streaming_tasks(t["items"], t["class_begin"], t["class_cascade"], bb.block_table)
+            assert t["item_stream"].tolist() == tasks.tolist()
             assert t["class_stream"].tolist() == want.tolist()
