@@ -239,10 +239,11 @@ typedef struct pmattn_plan_tables {
    * (see item_stream). */
   const int32_t* class_stream;
   /* [num_items] 1: no KV block the task reads is also read by a task of
-   * another sequence (readers: the item's sequence, or for cascade classes
-   * the virtual sequence of the item's first virtual row). Such a task loads
-   * its K/V with the non-temporal hint (one-wave kernel); shared blocks stay
-   * cacheable for their other readers. */
+   * another row tile (readers: the tile's first row, real or for cascade
+   * classes virtual). A one-wave task so marked loads its K/V with the
+   * non-temporal hint; blocks read again stay cacheable for their other
+   * readers. The workgroup kernel stages K/V through LDS with cacheable
+   * loads whatever the flag. */
   const int32_t* item_stream;
 } pmattn_plan_tables;
 

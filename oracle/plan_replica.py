@@ -469,17 +469,17 @@ def check_coverage_cascade(items, class_cascade, class_begin, vrow_src, q_len, q
 def streaming_tasks(items, class_begin, class_cascade, block_table):
     """Which tasks may stream their KV with non-temporal loads, and so which
     classes: a task streams when no physical block it reads is also read by a
-    task of another reader. A task's reader is its sequence (item column 0),
-    or, in a cascade class, its virtual sequence, named by its first virtual
-    row (item column 2); a task reads the blocks that hold keys
-    [kv_begin, kv_end) (columns 5 and 6) of its block-table row. Returns
-    (per-task flags, per-class 1 = all stream / 0 = none / 2 = some)."""
+    task of another reader. A task's reader is its row tile, named by its
+    first row (item column 2), real or, in a cascade class, virtual; a task
+    reads the blocks that hold keys [kv_begin, kv_end) (columns 5 and 6) of
+    its block-table row (column 0). Returns (per-task flags, per-class 1 =
+    all stream / 0 = none / 2 = some)."""
     readers = {}
     reads = []
     for c in range(len(class_begin) - 1):
         for it in items[class_begin[c]:class_begin[c + 1]]:
             seq, _, row0, _, _, lo, hi, _ = (int(x) for x in it[:8])
-            who = ("virtual", row0) if class_cascade[c] else ("seq", seq)
+            who = ("virtual", row0) if class_cascade[c] else ("real", row0)
             blocks = {int(block_table[seq][j]) for j in range(lo // BLOCK, -(-hi // BLOCK))}
             reads.append(blocks)
             for b in blocks:

@@ -661,14 +661,14 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     P.class_begin.push_back((int32_t)P.items.size());
   }
 
-  // ---- streaming tasks: KV no other sequence reads -----------------------------
-  // A block read by the tasks of two sequences (a shared prefix) is worth
-  // keeping in the caches: the second reader often finds it there. A task
-  // none of whose blocks is read that way streams its K/V with non-temporal
-  // loads. Readers are sequences; a cascade task reads for its virtual
-  // sequence, identified by its first virtual row. A class is 1 when all its
-  // tasks stream, 0 when none does, 2 when the kernel must look up each
-  // task's flag. (Measured on MI355X: the 64-sequence decode batch 69% -> 77%
+  // ---- streaming tasks: KV no other tile reads --------------------------------
+  // A block read by two row tiles (a shared prefix, or the tiles of one long
+  // prefill chunk) is worth keeping in the caches: the second reader often
+  // finds it there. A task none of whose blocks is read that way streams its
+  // K/V with non-temporal loads. Readers are row tiles, named by their first
+  // row (real or virtual); the split and kv-head tasks of one tile read
+  // disjoint bytes. A class is 1 when all its tasks stream, 0 when none does,
+  // 2 when the kernel must look up each task's flag. (Measured on MI355X: the 64-sequence decode batch 69% -> 77%
   // of HBM peak with non-temporal K/V; the long-decode batch, whose blocks
   // are shared in pairs, 69.5% -> 63.4% had all of it streamed.)
   {
@@ -681,7 +681,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     for (size_t c = 0; c + 1 < P.class_begin.size(); ++c)
       for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
         const pmattn_work_item& it = P.items[i];
-        const int32_t reader = P.class_cascade[c] ? B + it.row_begin : it.seq;
+        const int32_t reader = P.class_cascade[c] ? row_off[B] + it.row_begin : it.row_begin;
         for_blocks(it, [&](int32_t b) {
           if (first_reader[b] < 0) first_reader[b] = reader;
           else if (first_reader[b] != reader) multi[b] = 1;
