@@ -382,3 +382,43 @@ def test_cascade_full_config5_and_order():
     compare(b, out, lse)
     o2, l2 = run_gpu(b, dev, cascade=1, work_shuffle_seed=5)
     assert np.array_equal(o2, out) and np.array_equal(l2, lse)
+
+
+def _share_mode_case(kind, d, extra):
+    """Small batches whose one-wave class reads only shared blocks (stream
+    mode 0), or shared and private ones (mode 2), alone, beside a workgroup
+    task (the concurrent instance), or with token trees."""
+    sh = [("n", 0)]
+    if kind == "all-shared-decode":
+        sp = [dict(q_len=1, seq_len=39 + i, nodes=sh) for i in range(4)]
+    elif kind == "some-shared-decode":
+        sp = [dict(q_len=1, seq_len=39 + i, nodes=sh) for i in range(3)] + [dict(q_len=1, seq_len=300 + i) for i in range(3)]
+    elif kind == "all-shared-verify":
+        sp = [dict(q_len=5, seq_len=41 + i, q_start=36 + i, nodes=sh) for i in range(4)]
+    else:
+        sp = ([dict(q_len=5, seq_len=41 + i, q_start=36 + i, nodes=sh) for i in range(3)] +
+              [dict(q_len=5, seq_len=400 + i, q_start=395 + i) for i in range(2)])
+    if extra == "beside-prefill":
+        sp = sp + [dict(q_len=40, seq_len=90, q_start=50)]
+    if extra == "tree":
+        sp = [dict(s, tree=[-1] + [0] * (s["q_len"] - 1)) if s["q_len"] > 1 else s for s in sp]
+        if all(s["q_len"] == 1 for s in sp):
+            sp = sp + [dict(q_len=4, seq_len=60, q_start=56, tree=[-1, 0, 0, 1])]
+    return wl.custom(sp, node_blocks={("n", 0): 2}, hq=8, hkv=2, d=d, seed=5, extra_blocks=2,
+                     name=f"{kind}-d{d}-{extra}")
+
+
+@pytest.mark.parametrize("extra", ["alone", "beside-prefill", "tree"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", ["all-shared-decode", "some-shared-decode", "all-shared-verify", "some-shared-verify"])
+def test_stream_modes(kind, d, extra):
+    """Cached (0) and per-task (2) K/V loads of the one-wave kernel give the
+    oracle's result; the planner picks the intended mode."""
+    b = _share_mode_case(kind, d, extra)
+    t = make_plan(b).tables()
+    wave = [s for r, s in zip(t["class_rows"], t["class_stream"]) if r <= 64]
+    want = 0 if kind.startswith("all") and not (extra == "tree" and kind.endswith("decode")) else 2
+    assert wave == [want], (t["class_rows"], t["class_stream"])
+    note(f"stream mode case {b.name}: classes {t['class_rows'].tolist()} modes {t['class_stream'].tolist()}")
+    out, lse = run_gpu(b)
+    compare(b, out, lse)
