@@ -35,6 +35,14 @@
 // past the task's end are never used: their scores become -inf and their V
 // lanes are zeroed before the PV product, so pool slots no row can see may
 // hold NaN (virtual padding, "Assumptions & free parameters").
+//
+// Instances: head dim D; NT 16-row tiles per task (1 decode, 2 verify, 4);
+// TREE token-tree masks; CONC the launch runs beside workgroup tasks of the
+// same plan (16-row tasks then keep one chunk buffer at 3 waves per SIMD
+// instead of two at 2, so that they pack with the 3-wave workgroup kernel);
+// SMODE how K/V are loaded: 0 cacheable, 1 non-temporal, 2 per the task's
+// flag from the planner (non-temporal when no other row tile reads its
+// blocks, so shared prefix blocks stay in the caches for their other readers).
 #include "attn_kernels.h"
 #include "plan_internal.h"
 

@@ -50,6 +50,12 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
 // lazy rescale threshold, in log2 units of the scaled scores
 constexpr float kRescaleLog2 = 8.0f;
+// LDS operand read-ahead of the QK (K) and PV (V) MFMA runs. Measured on
+// MI355X, few-shot prefill: 962-965 TFLOP/s with the compiler's one-deep
+// schedule, 982 with V two deep, 1,001-1,009 with K four deep as well (3
+// waves/SIMD, no spills); V four deep spilled (851-861).
+constexpr int kKAhead = 4;
+constexpr int kVAhead = 2;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -232,9 +238,20 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
   const int kap = (i32 & ~12) | ((i32 & 4) << 1) | ((i32 & 8) >> 1);
   f32x16 s = {};
   const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
+  // K operands rotate through kKAhead registers, each read that many MFMAs
+  // before its use; the scheduling barriers pin the order (left alone, the
+  // scheduler sinks every read next to its MFMA and waits out the LDS
+  // latency each time)
+  bf16x8 kq[kKAhead];
 #pragma unroll
-  for (int st = 0; st < KSTEPS; ++st)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(kr + 8 * st), qop[st], s, 0, 0, 0);
+  for (int st = 0; st < kKAhead && st < KSTEPS; ++st) kq[st] = lds16(kr + 8 * st);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st) {
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st % kKAhead], qop[st], s, 0, 0, 0);
+    if (st + kKAhead < KSTEPS) kq[st % kKAhead] = lds16(kr + 8 * (st + kKAhead));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (mask) {
     keep_compute_branch<D>();
     // visible iff key < lim (lim = min(pos + 1, kv_end) - c0 for this lane's row)
@@ -282,11 +299,20 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
   l_part += ps;
   const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
   const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
+  // V operands likewise, kVAhead deep: operand j (tile j / 2, keys 16 (j % 2)
+  // onwards) is read kVAhead MFMAs before its use
+  const uint16_t* vb = vl + i32 * Cfg<D>::VROW + 32 * kt + 8 * h;
+  constexpr int NV = 2 * DT;
+  auto vaddr = [&](int j) { return vb + (32 * (j >> 1)) * Cfg<D>::VROW + 16 * (j & 1); };
+  bf16x8 vq[kVAhead];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const uint16_t* vr = vl + (32 * t + i32) * Cfg<D>::VROW + 32 * kt + 8 * h;
-    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr), pb0, o[t], 0, 0, 0);
-    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(vr + 16), pb1, o[t], 0, 0, 0);
+  for (int j = 0; j < kVAhead && j < NV; ++j) vq[j] = lds16(vaddr(j));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    o[j >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[j % kVAhead], (j & 1) ? pb1 : pb0, o[j >> 1], 0, 0, 0);
+    if (j + kVAhead < NV) vq[j % kVAhead] = lds16(vaddr(j + kVAhead));
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
