@@ -672,30 +672,51 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // of HBM peak with non-temporal K/V; the long-decode batch, whose blocks
   // are shared in pairs, 69.5% -> 63.4% had all of it streamed.)
   {
-    std::vector<int32_t> first_reader(d->num_pool_blocks, -1);
-    std::vector<char> multi(d->num_pool_blocks, 0);
+    // Tasks of one tile and partition differ only in their kv head, so each
+    // distinct (reader, key range) is walked once.
+    // per block: -1 unread, its only reader so far (>= 0), or kMulti
+    constexpr int32_t kMulti = -2;
+    std::vector<int32_t> reader_of(d->num_pool_blocks, -1);
     auto for_blocks = [&](const pmattn_work_item& it, auto&& fn) {
       const int32_t* row = d->block_table + (int64_t)it.seq * d->bt_stride;
       for (int32_t j = it.kv_begin / kBlock; j * kBlock < it.kv_end; ++j) fn(row[j]);
     };
+    // distinct ranges per reader as linked lists (a reader has one range per
+    // KV partition of its tile); readers are row indices, real rows first
+    std::vector<int32_t> head(row_off[B] + P.vrow_src.size(), -1), next;
+    std::vector<size_t> reps;        // one task per distinct (reader, range)
+    std::vector<int32_t> item_range(P.items.size());
     for (size_t c = 0; c + 1 < P.class_begin.size(); ++c)
       for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
         const pmattn_work_item& it = P.items[i];
         const int32_t reader = P.class_cascade[c] ? row_off[B] + it.row_begin : it.row_begin;
+        int32_t r = head[reader];
+        while (r >= 0 && (P.items[reps[r]].kv_begin != it.kv_begin || P.items[reps[r]].kv_end != it.kv_end)) r = next[r];
+        if (r >= 0) {
+          item_range[i] = r;
+          continue;
+        }
+        item_range[i] = (int32_t)reps.size();
+        next.push_back(head[reader]);
+        head[reader] = (int32_t)reps.size();
+        reps.push_back(i);
         for_blocks(it, [&](int32_t b) {
-          if (first_reader[b] < 0) first_reader[b] = reader;
-          else if (first_reader[b] != reader) multi[b] = 1;
+          const int32_t rd = reader_of[b];
+          if (rd != reader && rd != kMulti) reader_of[b] = rd == -1 ? reader : kMulti;
         });
       }
+    std::vector<int32_t> rep_stream(reps.size());
+    for (size_t r = 0; r < reps.size(); ++r) {
+      const pmattn_work_item& it = P.items[reps[r]];
+      const int32_t* row = d->block_table + (int64_t)it.seq * d->bt_stride;
+      int32_t j = it.kv_begin / kBlock;
+      while (j * kBlock < it.kv_end && reader_of[row[j]] != kMulti) ++j;
+      rep_stream[r] = j * kBlock >= it.kv_end ? 1 : 0;
+    }
     P.item_stream.assign(P.items.size(), 0);
     for (size_t c = 0; c + 1 < P.class_begin.size(); ++c) {
       int32_t n = 0;
-      for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
-        bool alone = true;
-        for_blocks(P.items[i], [&](int32_t b) { alone = alone && !multi[b]; });
-        P.item_stream[i] = alone ? 1 : 0;
-        n += P.item_stream[i];
-      }
+      for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) n += P.item_stream[i] = rep_stream[item_range[i]];
       const int32_t total = P.class_begin[c + 1] - P.class_begin[c];
       P.class_stream.push_back(n == total ? 1 : n == 0 ? 0 : 2);
     }
