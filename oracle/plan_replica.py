@@ -27,7 +27,8 @@ MAX_WAVE_ROWS = 64
 MAX_TASK_ROWS = 128
 CLASS_ROWS = (16, 32, 64, 128)
 TASKS_PER_CU = 32
-WG_TASKS_PER_2CU = 3  # 1.5 workgroup tasks per CU
+WG_TASKS_PER_2CU = 2       # 1 workgroup task per CU ...
+WG_TASKS_PER_2CU_TREE = 3  # ... 1.5 when the plan holds a token tree
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
 STREAM_WAVES_PER_CU = 3
@@ -178,12 +179,13 @@ def token_tiles(q_len, q_start, group):
     return tiles
 
 
-def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0, dtype="bf16"):
+def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0, dtype="bf16", tree=False):
     """KV partitions per sequence. Explicit: the requested count for every
     sequence with rows. Automatic: a task over n blocks costs n * (2 + rows/16)
     block units. Wave tasks (<= 64 rows) and workgroup tasks (128 rows) are
     balanced separately: each kind's quantum is its total cost over
-    (CUs x 32) wave tasks or (CUs x 1.5) workgroup tasks, at least 48 units; a
+    (CUs x 32) wave tasks or (CUs x 1) workgroup tasks (CUs x 1.5 when
+    ``tree``: some sequence is a token tree), at least 48 units; a
     sequence gets ceil(cost of its largest tile / its kind's quantum)
     partitions, at most 64 and at most its number of blocks."""
     q_len = np.asarray(q_len, np.int64)
@@ -205,8 +207,9 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0, 
         last[s] = max(last[s], c)
         kind[s] = k
     cus = num_cus if num_cus > 0 else 256
+    wg = WG_TASKS_PER_2CU_TREE if tree else WG_TASKS_PER_2CU
     quantum = [max(MIN_QUANTUM, -(-total[k] // t)) for k, t in ((0, cus * TASKS_PER_CU),
-                                                                (1, cus * WG_TASKS_PER_2CU // 2))]
+                                                                (1, cus * wg // 2))]
     for s in range(q_len.shape[0]):
         if q_len[s] == 0:
             continue
@@ -362,7 +365,7 @@ def cascade_groups(q_len, q_start, block_table, group, mode=1):
 
 
 def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0, num_cus=0,
-               cascade=False, dtype="bf16"):
+               cascade=False, dtype="bf16", tree=False):
     """Units of work (real sequences, then cascade groups) with their tiles and
     KV partitions, by the same rules as ``token_tiles`` / ``num_splits`` /
     ``split_ranges`` applied to each unit's own key range [lo, hi).
@@ -417,8 +420,9 @@ def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0
                 u["last"] = max(u["last"], c)
                 u["kind"] = k
         cus = num_cus if num_cus > 0 else 256
+        wg = WG_TASKS_PER_2CU_TREE if tree else WG_TASKS_PER_2CU
         quantum = [max(MIN_QUANTUM, -(-total[0] // (cus * TASKS_PER_CU))),
-                   max(MIN_QUANTUM, -(-total[1] // (cus * WG_TASKS_PER_2CU // 2)))]
+                   max(MIN_QUANTUM, -(-total[1] // (cus * wg // 2)))]
         for u in units:
             nblk = -(-(u["hi"] - u["lo"]) // BLOCK)
             u["splits"] = max(1, min(-(-u["last"] // quantum[u["kind"]]), MAX_AUTO_SPLITS, nblk)) if u["rows"] else 0

@@ -111,7 +111,13 @@ int64_t unit_cost(int cls) { return 2 + kClassRows[cls] / 16; }
 // than 4 on the shared-prompt cascade and 5% on tree verify, 1.5% slower on
 // the mixed batch) ...
 constexpr int64_t kTasksPerCu = 32;
-constexpr int64_t kWgTasksPer2Cu = 3;
+constexpr int64_t kWgTasksPer2Cu = 2;
+// ... and 1.5 per CU when the plan holds token trees: their workgroup kernel
+// runs at 2 waves per SIMD instead of 3, and measured on MI355X the
+// token-tree workload took 0.161-0.163 ms at 1.5 per CU against 0.170-0.172
+// at 1, while the shared-prompt cascade took 0.1035-0.1038 ms at 1 against
+// 0.1084-0.1089 at 1.5 (mixed batch equal).
+constexpr int64_t kWgTasksPer2CuTree = 3;
 // Equal-work decode: a plan whose tasks are all 16-row wave tasks (decode
 // rows) with automatic splits gives each of kStreamWavesPerCu waves per CU an
 // equal run of KV blocks of one kv head, never shorter than kStreamMinBlocks.
@@ -472,7 +478,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       unit_kind[t.seq] = kind;
     }
     const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
-    const int64_t target[2] = {cus * kTasksPerCu, cus * kWgTasksPer2Cu / 2};
+    const int64_t target[2] = {cus * kTasksPerCu, cus * (P.row_mask.empty() ? kWgTasksPer2Cu : kWgTasksPer2CuTree) / 2};
     int64_t quantum[2];
     for (int k = 0; k < 2; ++k)
       quantum[k] = std::max(kMinQuantum, (total[k] + target[k] - 1) / target[k]);

@@ -30,7 +30,8 @@ def check_plan(b, p, num_cus=0):
     grp = b.num_q_heads // b.num_kv_heads
     rs, rp = R.row_tables(b.q_len, b.q_start)
     assert np.array_equal(t["row_seq"], rs) and np.array_equal(t["row_pos"], rp)
-    ns = R.num_splits(b.q_len, b.q_start, b.num_kv_heads, grp, b.num_kv_splits, num_cus, b.dtype)
+    tree = R.row_tree_masks(b.q_len, b.tree_parent) is not None
+    ns = R.num_splits(b.q_len, b.q_start, b.num_kv_heads, grp, b.num_kv_splits, num_cus, b.dtype, tree)
     assert np.array_equal(t["num_splits"], ns)
     bounds = R.seq_bounds(b.q_len, b.q_start, b.num_kv_heads, grp, ns, num_cus, b.dtype, b.num_kv_splits)
     lo, hi = R.split_ranges(b.q_len, b.q_start, ns, bounds)
@@ -76,7 +77,7 @@ def check_records(b, t):
         assert (rows <= cr[c]).all()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7])
 def test_plan_tables_match_replica(cfg):
     b = wl.config(cfg, values=False)
     check_plan(b, make_plan(b))
@@ -353,7 +354,7 @@ def test_append_refuses_shared_target_slots():
 def _check_cascade_plan(b, t, num_kv_splits=0, num_cus=0, mode=1):
     grp = b.num_q_heads // b.num_kv_heads
     rep = R.plan_units(b.q_len, b.q_start, b.block_table, b.num_kv_heads, grp, num_kv_splits, num_cus,
-                       cascade=mode, dtype=b.dtype)
+                       cascade=mode, dtype=b.dtype, tree=R.row_tree_masks(b.q_len, b.tree_parent) is not None)
     units = rep["units"]
     nb = b.num_seqs
     virt = units[nb:]
