@@ -41,6 +41,8 @@
 //   were waited for right after issue (15% of the few-shot time). Its loads
 //   are buffer loads with a scalar (block, kv head) base and one 32-bit lane
 //   offset shared by K and V: no 64-bit address arithmetic per chunk.
+#include <type_traits>
+
 #include "attn_kernels.h"
 
 namespace pmattn {
@@ -388,20 +390,29 @@ void attn_prefill_kernel(AttnArgs a) {
   stage_load<D>(stg, kpool, vpool, blk, kvh, hkv, tid);
   stage_store<D>(lds, stg, c0, kv_end, tid);
   __syncthreads();
-  for (int c = 0; c < nch; ++c, c0 += CHUNK) {
+  // one chunk out of LDS buffer B (0 or 1), staging the next into the other;
+  // the loop runs them in pairs, so every LDS address takes the buffer as an
+  // immediate offset instead of VALU work per chunk (measured on MI355X, one
+  // session: few-shot prefill +1.0-1.3%, token-tree verify +3-5%)
+  auto step = [&](auto buf, int c) {
+    constexpr int B = decltype(buf)::value;
     const bool more = c + 1 < nch;
     if (more) {
       chunk_blocks(c0 + CHUNK, blk);
       stage_load<D>(stg, kpool, vpool, blk, kvh, hkv, tid);
     }
     issue_barrier();
-    const uint16_t* cur = lds + (c & 1) * Cfg<D>::STAGE;
     // a chunk every row of the task sees whole needs no mask; in a token tree
     // that excludes the 64 keys before the task's first row
     const bool mask = c0 + CHUNK - 1 > min_pos - (TREE ? 64 : 0) || c0 + CHUNK > kv_end;
-    compute_chunk<D, TREE>(cur, qop, o, rr, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
-    if (more) stage_store<D>(lds + ((c + 1) & 1) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
+    compute_chunk<D, TREE>(lds + B * Cfg<D>::STAGE, qop, o, rr, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
+    if (more) stage_store<D>(lds + (1 - B) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
     __syncthreads();
+    c0 += CHUNK;
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    if (c + 1 < nch) step(std::integral_constant<int, 1>{}, c + 1);
   }
 
   // epilogue: lane (i32, h) owns channels 32t + 8q + 4h + (0..3) of its row
