@@ -287,7 +287,8 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, int idx, int lane) {
     if (m < M) {
       const int t = m / G;
       pos[n] = it.pos_begin + t;
-      const uint16_t* src = qp + ((int64_t)(it.row_begin + t) * hq + kvh * G + (m - t * G)) * D + 8 * g;
+      const int64_t qr = a.q_row ? a.q_row[it.row_begin + t] : it.row_begin + t;
+      const uint16_t* src = qp + (qr * hq + kvh * G + (m - t * G)) * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < KS; ++s) qop[n][s] = ld16(src + 32 * s);
     } else {

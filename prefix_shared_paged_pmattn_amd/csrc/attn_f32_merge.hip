@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const int kend = min(it.kv_end, it.pos_begin + t + 1);
     const int rpos = it.pos_begin + t;
     const uint64_t rel = a.row_mask ? a.row_mask[row] : ~0ull;  // token tree
-    const float* qrow = qp + (row * hq + qh) * D;
+    const float* qrow = qp + ((a.q_row ? (int64_t)a.q_row[row] : row) * hq + qh) * D;
     float m_run = kNegInf, l_run = 0.f, acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;

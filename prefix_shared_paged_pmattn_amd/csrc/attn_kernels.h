@@ -21,6 +21,8 @@ struct AttnArgs {
   void* out;
   float* lse;                    // may be null
   const pmattn_work_item* items; // this launch's first task
+  const int32_t* q_row;          // null: a task's query row r is row r of q; else row q_row[r]
+                                 // (cascade classes: virtual rows name their member's row)
   const uint64_t* row_mask;      // [R] token-tree masks, or null: every row causal
   float* part_o;                 // [records][d]
   float* part_lse;               // [records]
@@ -76,8 +78,6 @@ hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
 hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st);
 // Copy the query rows src_rows[0..n) of q ([R][row_elems]) into dst ([n][row_elems]).
-hipError_t launch_gather_rows(const void* q, const int32_t* src_rows, int n, int row_bytes, void* dst,
-                              hipStream_t st);
 hipError_t launch_copy_blocks(int head_dim, int dtype, const pmattn_block_copy* copies, int n,
                               void* k_pool, void* v_pool, int hkv, hipStream_t st);
 

@@ -351,7 +351,8 @@ void attn_prefill_kernel(AttnArgs a) {
   const int pos = row_valid ? it.pos_begin + t : -1;
   bf16x8 qop[KSTEPS];
   if (row_valid) {
-    const uint16_t* src = qp + ((int64_t)(it.row_begin + t) * hq + kvh * G + (m - t * G)) * D + (D / 2) * h;
+    const int64_t qr = a.q_row ? a.q_row[it.row_begin + t] : it.row_begin + t;
+    const uint16_t* src = qp + (qr * hq + kvh * G + (m - t * G)) * D + (D / 2) * h;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qop[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + 8 * s));
   } else {

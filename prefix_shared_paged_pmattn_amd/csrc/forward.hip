@@ -114,6 +114,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.part_o = reinterpret_cast<float*>(ws + P.off_part_o);
   a.part_lse = reinterpret_cast<float*>(ws + P.off_part_lse);
   a.slot_begin = nullptr;
+  a.q_row = nullptr;
   a.item_stream = nullptr;
   a.slot_count = 0;
   a.bt_stride = P.bt_stride;
@@ -123,15 +124,6 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   a.scale = P.scale;
   a.scale_log2 = P.scale * kLog2e;
   const pmattn_work_item* items = reinterpret_cast<const pmattn_work_item*>(ws + P.off_items);
-  // cascade: gather the virtual sequences' query rows first (same stream, so
-  // every class launched after it, on either stream, sees them)
-  void* qv = ws + P.off_qv;
-  if (!P.vrow_src.empty()) {
-    const int row_bytes = P.hq * P.head_dim * (P.dtype == PMATTN_BF16 ? 2 : 4);
-    hipError_t e = launch_gather_rows(q, reinterpret_cast<const int32_t*>(ws + P.off_vrow),
-                                      (int)P.vrow_src.size(), row_bytes, qv, st);
-    if (e != hipSuccess) return hip_fail(e, "row gather kernel launch");
-  }
   bool has_wg = false, has_wave = false;
   for (int32_t rows : P.class_rows) (rows > kMaxWaveRows ? has_wg : has_wave) = true;
   const bool concurrent = P.dtype == PMATTN_BF16 && has_wg && has_wave;
@@ -146,9 +138,10 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
       ac.slot_count = (int32_t)P.slot_begin.size() - 1;
     }
     if (P.class_cascade[c]) {
-      // virtual rows: gathered queries; their keys all lie below every
-      // member's first row, so no tree mask applies
-      ac.q = qv;
+      // virtual rows read their member's query row through the uploaded row
+      // table; their keys all lie below every member's first row, so no tree
+      // mask applies
+      ac.q_row = reinterpret_cast<const int32_t*>(ws + P.off_vrow);
       ac.row_mask = nullptr;
     }
     if (P.dtype != PMATTN_BF16) return launch_attn_f32(P.head_dim, ac, s);

@@ -83,25 +83,7 @@ __global__ __launch_bounds__(128) void copy_blocks_kernel(const pmattn_block_cop
   }
 }
 
-// Gather whole query rows (all heads) into the cascade's virtual row buffer:
-// one workgroup per row, 16-byte pieces.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const unsigned char* q, const int32_t* src_rows,
-                                                          int row_bytes, unsigned char* dst) {
-  const int64_t src = ((cint_p)src_rows)[blockIdx.x];
-  const uint4* s = reinterpret_cast<const uint4*>(q + src * row_bytes);
-  uint4* t = reinterpret_cast<uint4*>(dst + (int64_t)blockIdx.x * row_bytes);
-  for (int i = threadIdx.x; i < row_bytes / 16; i += 256) t[i] = s[i];
-}
-
 }  // namespace
-
-hipError_t launch_gather_rows(const void* q, const int32_t* src_rows, int n, int row_bytes, void* dst,
-                              hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, st, static_cast<const unsigned char*>(q),
-                     src_rows, row_bytes, static_cast<unsigned char*>(dst));
-  return hipGetLastError();
-}
 
 hipError_t launch_copy_blocks(int head_dim, int dtype, const pmattn_block_copy* copies, int n,
                               void* k_pool, void* v_pool, int hkv, hipStream_t st) {

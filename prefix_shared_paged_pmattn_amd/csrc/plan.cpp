@@ -739,12 +739,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.off_vrow = align_up(P.off_rec_index + P.rec_index.size() * sizeof(int32_t), kAlign);
   P.off_slot = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
   P.off_istream = align_up(P.off_slot + P.slot_begin.size() * sizeof(int32_t), kAlign);
-  P.off_qv = align_up(P.off_istream + P.item_stream.size() * sizeof(int32_t), kAlign);
-  const size_t elem = P.dtype == PMATTN_BF16 ? 2 : 4;
-  P.off_part_o = align_up(P.off_qv + P.vrow_src.size() * (size_t)P.hq * P.head_dim * elem, kAlign);
+  P.off_upload_end = align_up(P.off_istream + P.item_stream.size() * sizeof(int32_t), kAlign);
+  P.off_part_o = P.off_upload_end;
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
   P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
-  P.upload_blob.assign(P.off_qv, 0);
+  P.upload_blob.assign(P.off_upload_end, 0);
   if (!P.items.empty())
     std::memcpy(P.upload_blob.data() + P.off_items, P.items.data(),
                 P.items.size() * sizeof(pmattn_work_item));

@@ -66,11 +66,10 @@ struct Plan {
   std::string append_conflict;
   // workspace layout (bytes): [items | merge rows | row masks | append units |
   // record index | virtual row sources | wave slots | task stream flags |
-  // gathered Q of virtual rows | partial O | partial lse]; everything before
-  // the gathered Q is uploaded
+  // partial O | partial lse]; everything before the partials is uploaded
   size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_rec_index = 0,
-         off_vrow = 0, off_slot = 0, off_istream = 0, off_qv = 0, off_part_o = 0, off_part_lse = 0,
-         ws_bytes = 0;
+         off_vrow = 0, off_slot = 0, off_istream = 0, off_upload_end = 0, off_part_o = 0,
+         off_part_lse = 0, ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 
