@@ -247,12 +247,17 @@ typedef struct pmattn_plan_tables {
   const int32_t* item_stream;
 } pmattn_plan_tables;
 
-/* Build a plan on the host. Validates the batch (see pmattn_plan_desc),
- * splits the work into tile tasks (automatic splits: balanced cost quanta;
- * pure decode batches in bf16: equal KV pieces, one per wave, see
- * pmattn_plan_tables.slot_begin), orders them by estimated cost (largest
- * first) with every kv head's tasks on one XCD of the GPU, and prepares the
- * merge list. Makes no HIP call and touches no GPU.
+/* Build a plan on the host: the Token-Table / Task-Table step of the
+ * XY-Serve design (XY-Serve review, "Core claim": each step's attention work
+ * is cut into tile-level tasks recorded in tables; "What carries the
+ * argument": tiles are reordered across cores by computational area at run
+ * time). Validates the batch (see pmattn_plan_desc), splits the work into tile
+ * tasks (automatic splits: balanced cost quanta; pure decode batches in bf16:
+ * equal KV pieces, one per wave, see pmattn_plan_tables.slot_begin; the KV
+ * partitions are Flash-Decoding's split-KV, reference list of the same page),
+ * orders them by estimated cost (largest first) with every kv head's tasks on
+ * one XCD of the GPU, and prepares the merge list. Makes no HIP call and
+ * touches no GPU.
  * Errors: PMATTN_E_INVALID for null pointers, negative lengths,
  * q_start + q_len > seq_len, a block id outside [0, num_pool_blocks) among the
  * blocks a row can see, bt_stride too small, Hq % Hkv != 0, scale not finite
@@ -270,25 +275,34 @@ pmattn_status pmattn_plan_workspace_bytes(pmattn_plan_t plan, size_t* bytes);
 
 pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* tables);
 
-/* Copy the plan's work and merge lists into `workspace` (device memory of at
- * least pmattn_plan_workspace_bytes) with an asynchronous host-to-device copy
- * on `stream` (a hipStream_t; NULL = the default stream). pmattn_forward does
- * this by itself whenever the workspace does not hold this plan's lists, so an
- * explicit call is only needed after the caller has written into the
- * workspace memory itself. Errors: PMATTN_E_INVALID, PMATTN_E_WORKSPACE,
- * PMATTN_E_HIP. */
+/* Copy the plan's tables (work list, merge list, row tables) into
+ * `workspace`, device memory of at least pmattn_plan_workspace_bytes, with an
+ * asynchronous host-to-device copy on `stream` (a hipStream_t; NULL = the
+ * default stream). The tables then live in the caller's memory: call this
+ * after pmattn_plan and before the first pmattn_forward, pmattn_forward_tasks
+ * or pmattn_kv_append of the plan on that workspace, and again whenever the
+ * workspace memory has been freed, handed to another plan or written by
+ * anything other than those calls. They never upload by themselves and never
+ * check what the workspace holds (a plan's tables are reused as they are, as a
+ * serving loop runs one plan for every layer of a step). Errors:
+ * PMATTN_E_INVALID, PMATTN_E_WORKSPACE, PMATTN_E_HIP. */
 pmattn_status pmattn_plan_upload(pmattn_plan_t plan, void* workspace, size_t ws_bytes,
                                  void* stream);
 
-/* Run the attention of `plan` on the GPU, asynchronously on `stream`.
- * Device pointers (caller-owned): q [R][Hq][d], k_pool, v_pool (layouts
- * above, at least num_pool_blocks blocks), block_table_dev int32
- * [B][bt_stride] holding the same ids as the host table given to pmattn_plan,
- * out [R][Hq][d] (same element type as q), lse [R][Hq] float32 or NULL,
- * workspace of ws_bytes >= pmattn_plan_workspace_bytes. The kernels read only
- * keys a row can see; pool slots no row can see may hold anything (NaN
- * included) without affecting the result. Errors: PMATTN_E_INVALID (null
- * pointer), PMATTN_E_WORKSPACE, PMATTN_E_HIP (launch failure). */
+/* Run the attention of `plan` on the GPU, asynchronously on `stream`: every
+ * tile task of the work list (matmul-softmax-matmul under each row's own mask,
+ * XY-Serve review, "What carries the argument" and "Editorial extensions"),
+ * then the log-sum-exp merge of split partials (Flash-Decoding, reference list
+ * of the same page). Device pointers (caller-owned): q [R][Hq][d], k_pool,
+ * v_pool (layouts above, at least num_pool_blocks blocks), block_table_dev
+ * int32 [B][bt_stride] holding the same ids as the host table given to
+ * pmattn_plan, out [R][Hq][d] (same element type as q), lse [R][Hq] float32
+ * or NULL, workspace of ws_bytes >= pmattn_plan_workspace_bytes into which
+ * pmattn_plan_upload has copied this plan's tables (the passes also write
+ * partial records into it). The kernels read only keys a row can see; pool
+ * slots no row can see may hold anything (NaN included) without affecting the
+ * result. Errors: PMATTN_E_INVALID (null pointer), PMATTN_E_WORKSPACE,
+ * PMATTN_E_HIP (launch failure). */
 pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_pool,
                              const void* v_pool, const int32_t* block_table_dev, void* out,
                              float* lse, void* workspace, size_t ws_bytes, void* stream);
@@ -300,7 +314,7 @@ pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_po
  * partial (output, lse) records into the workspace. Pass 2,
  * pmattn_forward_merge, merges those records into out/lse (a no-op when the
  * plan split nothing). pass 2 must follow pass 1 on the same stream, with the
- * same workspace. This is the split-KV scheme of "Flash-Decoding for
+ * same workspace (which holds the plan's tables, see pmattn_plan_upload). This is the split-KV scheme of "Flash-Decoding for
  * long-context inference" (XY-Serve pith review, reference list). */
 pmattn_status pmattn_forward_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_table_dev, void* out,
@@ -331,7 +345,8 @@ pmattn_status pmattn_merge_lse(int32_t num_parts, int32_t num_rows, int32_t num_
  * Device pointers (caller-owned): k_new, v_new [R][Hkv][d] of the plan's
  * element type; block_table_dev as for pmattn_forward; k_pool, v_pool are
  * written in place (only the slots of this step's rows); workspace as for
- * pmattn_forward (the work units travel in it). Asynchronous on `stream`.
+ * pmattn_forward (the work units travel in it: pmattn_plan_upload first).
+ * Asynchronous on `stream`.
  * A slot written here must belong to its sequence alone: if another sequence
  * of the plan can see it, or two rows write it, the call fails with
  * PMATTN_E_INVALID (copy such blocks first: copy-on-write). Errors:

@@ -31,9 +31,11 @@
  *   release  the request ends; its references go. Blocks still named by the
  *            tree stay cached until evicted.
  * Copy orders of a batch of admits must run before any K/V of that batch is
- * written: a later admit may evict the tree entry that held a copy's source
- * and hand that block out as a fresh one, which only its new owner's writes
- * (after the copies) may change.
+ * written, and before the admitted sequence's next extend, publish or
+ * release: until then the sequence holds a reference on its copy's source
+ * block, so no admit can hand that block out (as a fresh block or a copy
+ * destination) while the copy may still read it, even when an eviction has
+ * dropped the tree entry that held it.
  * When a block is needed and none is free, whole least-recently-used leaves
  * of the tree are evicted until one is. If nothing evictable remains the call
  * fails with PMATTN_E_CAPACITY and changes nothing.

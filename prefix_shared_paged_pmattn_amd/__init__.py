@@ -120,7 +120,8 @@ class Plan:
             item_stream=arr(t.item_stream, t.num_items))
 
     def upload(self, workspace, stream=None):
-        """``pmattn_plan_upload``: copy the work list into ``workspace``."""
+        """``pmattn_plan_upload``: copy the plan's tables (work list, merge
+        list, row tables) into ``workspace``, asynchronously on ``stream``."""
         _need_dev(workspace, "workspace")
         nbytes = workspace.numel() * workspace.element_size()
         _check(L.load().pmattn_plan_upload(self._h, ctypes.c_void_p(workspace.data_ptr()),
@@ -192,7 +193,7 @@ def _elem_dtype(code):
     return torch.bfloat16 if code == BF16 else torch.float32
 
 
-def _forward_args(p: Plan, q, k_pool, v_pool, block_table, out, lse, workspace, stream):
+def _forward_args(p: Plan, q, k_pool, v_pool, block_table, out, lse, workspace, stream, resident):
     torch = _torch()
     s = p.shape
     et = _elem_dtype(s["dtype"])
@@ -211,22 +212,25 @@ def _forward_args(p: Plan, q, k_pool, v_pool, block_table, out, lse, workspace, 
             raise ValueError(f"{name} has {t.numel()} elements, expected {'' if exact else '>= '}{n}")
         if t.data_ptr() % 16:
             raise ValueError(f"{name} must be 16-byte aligned")
-    return _workspace(p, workspace, q, stream)
+    return _workspace(p, workspace, q, stream, resident)
 
 
-def _workspace(p: Plan, workspace, like, stream):
-    """The caller's workspace (checked), or a fresh one with the plan uploaded:
-    memory just taken from the allocator may have held anything, including an
-    earlier copy of this plan's tables at the same address."""
+def _workspace(p: Plan, workspace, like, stream, resident=False):
+    """The caller's workspace (checked), or a fresh one, with the plan's tables
+    uploaded into it unless ``resident`` says the caller already did so
+    (``p.upload(workspace)``) and nothing has written it since. The library
+    never decides that by itself: memory taken from an allocator may have held
+    anything, including an earlier copy of these tables at the same address."""
     torch = _torch()
-    fresh = workspace is None
-    if fresh:
+    if workspace is None:
+        if resident:
+            raise ValueError("resident=True needs the workspace the plan was uploaded into")
         workspace = torch.empty(max(p.workspace_bytes, 256), dtype=torch.uint8, device=like.device)
     _need_dev(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < p.workspace_bytes:
         raise ValueError(f"workspace has {ws_bytes} bytes, plan needs {p.workspace_bytes}")
-    if fresh:
+    if not resident:
         p.upload(workspace, stream)
     return workspace, ws_bytes
 
@@ -235,12 +239,17 @@ def _vp(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def forward(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=None, stream=None):
+def forward(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=None, stream=None,
+            resident=False):
     """``pmattn_forward``. Tensors: q/out ``[R][Hq][d]``; k_pool
     ``[blocks][Hkv][d/x][16][x]`` (x = 16 bytes / element size); v_pool ``[blocks][Hkv][d][16]`` (element type of
     the plan); block_table int32 ``[B][stride]``; lse float32 ``[R][Hq]`` or
-    None; workspace: a uint8 tensor of at least ``p.workspace_bytes``."""
-    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace, stream)
+    None; workspace: a uint8 tensor of at least ``p.workspace_bytes`` (None:
+    a fresh one). The plan's tables are uploaded into the workspace first,
+    unless ``resident`` (the caller ran ``p.upload(workspace)`` and nothing has
+    written the workspace since)."""
+    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace, stream,
+                                        resident)
     _check(L.load().pmattn_forward(p.handle, _vp(q), _vp(k_pool), _vp(v_pool), _vp(block_table),
                                    _vp(out), _vp(lse), _vp(workspace), ws_bytes,
                                    _stream_ptr(stream, q)))
@@ -248,9 +257,11 @@ def forward(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=No
 
 
 def forward_tasks(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, workspace=None,
-                  stream=None):
-    """``pmattn_forward_tasks``: pass 1 of :func:`forward` (the tile tasks)."""
-    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace, stream)
+                  stream=None, resident=False):
+    """``pmattn_forward_tasks``: pass 1 of :func:`forward` (the tile tasks).
+    Returns the workspace, which :func:`forward_merge` must be given."""
+    workspace, ws_bytes = _forward_args(p, q, k_pool, v_pool, block_table, out, lse, workspace, stream,
+                                        resident)
     _check(L.load().pmattn_forward_tasks(p.handle, _vp(q), _vp(k_pool), _vp(v_pool),
                                          _vp(block_table), _vp(out), _vp(lse), _vp(workspace),
                                          ws_bytes, _stream_ptr(stream, q)))
@@ -277,9 +288,11 @@ def build_batch(kinds, context, pending, *, token_budget: int, reserved: int, ma
     return q[:n].copy()
 
 
-def kv_append(p: Plan, k_new, v_new, block_table, k_pool, v_pool, workspace=None, stream=None):
+def kv_append(p: Plan, k_new, v_new, block_table, k_pool, v_pool, workspace=None, stream=None,
+              resident=False):
     """``pmattn_kv_append``: write this step's K/V rows (``k_new``, ``v_new``
-    ``[R][Hkv][d]``, the plan's element type) into their pool slots, in place."""
+    ``[R][Hkv][d]``, the plan's element type) into their pool slots, in place.
+    ``workspace`` and ``resident`` as for :func:`forward`."""
     torch = _torch()
     s = p.shape
     et = _elem_dtype(s["dtype"])
@@ -298,7 +311,7 @@ def kv_append(p: Plan, k_new, v_new, block_table, k_pool, v_pool, workspace=None
             raise ValueError(f"{name} has {t.numel()} elements, expected {'' if exact else '>= '}{n}")
         if t.data_ptr() % 16:
             raise ValueError(f"{name} must be 16-byte aligned")
-    workspace, ws_bytes = _workspace(p, workspace, k_pool, stream)
+    workspace, ws_bytes = _workspace(p, workspace, k_pool, stream, resident)
     _check(L.load().pmattn_kv_append(p.handle, _vp(k_new), _vp(v_new), _vp(block_table),
                                      _vp(k_pool), _vp(v_pool), _vp(workspace), ws_bytes,
                                      _stream_ptr(stream, k_pool)))
@@ -306,7 +319,9 @@ def kv_append(p: Plan, k_new, v_new, block_table, k_pool, v_pool, workspace=None
 
 
 def forward_merge(p: Plan, out, lse, workspace, stream=None):
-    """``pmattn_forward_merge``: pass 2 of :func:`forward` (merge of split partials)."""
+    """``pmattn_forward_merge``: pass 2 of :func:`forward` (merge of split
+    partials). ``workspace`` must be the one pass 1 (:func:`forward_tasks`)
+    ran on, which holds the plan's tables and the partial records."""
     _need_dev(out, "out")
     _need_dev(workspace, "workspace")
     if lse is not None:

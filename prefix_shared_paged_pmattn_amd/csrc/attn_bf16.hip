@@ -224,38 +224,24 @@ __device__ __forceinline__ pmattn_work_item load_item(const pmattn_work_item* it
   return it;
 }
 
-// Decode-shaped tasks keep two waves per SIMD so that eight waves per CU keep
-// KV loads in flight; the 64-row variant needs the whole register file.
-#ifndef PMATTN_DECODE_DEPTH
-#define PMATTN_DECODE_DEPTH 2
-#endif
-#ifndef PMATTN_DECODE_WAVES
-#define PMATTN_DECODE_WAVES 2
-#endif
-#ifndef PMATTN_VERIFY_DEPTH
-#define PMATTN_VERIFY_DEPTH 1
-#endif
-#ifndef PMATTN_VERIFY_WAVES
-#define PMATTN_VERIFY_WAVES 2
-#endif
-// CONC: the launch shares the chip with workgroup (prefill) tasks of the same
-// plan on another stream.
+// Occupancy and chunk buffers per wave, by tile count NT and whether the
+// launch shares the chip with workgroup tasks of the same plan (CONC).
+// 16-row (decode) tasks double-buffer at 2 waves/SIMD (253 VGPRs): two chunks
+// in flight per wave, eight waves per CU. Beside workgroup tasks they keep one
+// buffer at 3 waves/SIMD (166 VGPRs): three of them, or any mix with the
+// 3-wave workgroup kernel's 168, fill a SIMD's 512 registers, where a
+// 253-register double-buffered wave left a third of them idle (measured on
+// MI355X: shared-prompt cascade 0.116 against 0.124 ms, mixed batch 0.733
+// against 0.752-0.765 ms). 32-row (verify) tasks keep one buffer at 2
+// waves/SIMD (213 VGPRs; their two-buffer variant measured the same); 64-row
+// tasks double-buffer and need the whole register file.
 template <int NT, bool CONC>
 struct WavesPerEu {
-  static constexpr int value = NT == 1 ? (CONC ? 3 : PMATTN_DECODE_WAVES)
-                                       : (NT == 2 && PMATTN_VERIFY_DEPTH == 1 ? PMATTN_VERIFY_WAVES : 1);
+  static constexpr int value = NT == 1 ? (CONC ? 3 : 2) : (NT == 2 ? 2 : 1);
 };
-// Chunks in flight per wave: 1 (occupancy hides latency) or 2 (explicit
-// double buffering). 16-row tasks double-buffer at 2 waves/SIMD; 32-row tasks
-// (speculative verify) keep one buffer so that they too fit 2 waves/SIMD.
-// Beside workgroup tasks, 16-row tasks keep one buffer at 3 waves/SIMD (166
-// VGPRs): three of them, or any mix with the 3-wave workgroup kernel's 168,
-// fill a SIMD's 512 registers, where a 253-register double-buffered wave
-// left a third of them idle. Measured on MI355X: shared-prompt cascade
-// 0.116 against 0.124 ms, mixed batch 0.733 against 0.752-0.765 ms.
 template <int NT, bool CONC>
 struct Depth {
-  static constexpr int value = NT == 1 ? (CONC ? 1 : PMATTN_DECODE_DEPTH) : (NT == 2 ? PMATTN_VERIFY_DEPTH : 2);
+  static constexpr int value = NT == 1 ? (CONC ? 1 : 2) : (NT == 2 ? 1 : 2);
 };
 
 // Tasks are independent; a workgroup holds four of them, one per wave (1- and

@@ -66,7 +66,21 @@ struct AppendArgs {
   int32_t hkv;
 };
 
-// Host launchers (forward.hip).
+// Launcher internals (forward.hip), shared with the allocation-free entry
+// point (noalloc.hip). upload: the plan's tables into ws (async on st).
+// run_tasks / run_merge: the two passes of pmattn_forward over the workspace
+// ws; use_aux lets the wave-task classes of a plan that also holds workgroup
+// tasks run on per-device auxiliary streams.
+struct Plan;
+pmattn_status hip_fail(hipError_t e, const char* what);
+pmattn_status upload(const Plan& P, void* ws, hipStream_t st);
+pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_pool, const void* v_pool,
+                        const int32_t* block_table_dev, void* out, float* lse, void* workspace,
+                        size_t ws_bytes, void* stream, bool use_aux);
+pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+// Kernel launchers.
 // concurrent: workgroup tasks of the same plan run beside these waves (on a
 // second stream); 16-row tasks then take the 3-waves-per-SIMD variant.
 // stream: 1 no other sequence reads the class's KV blocks (non-temporal

@@ -63,17 +63,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const int32_t __attribute__((address_space(4)))* cint_p;
 
-// Tuning knobs (compile-time); the defaults are the measured best.
-#ifndef PMATTN_PF_CHUNK
-#define PMATTN_PF_CHUNK 32
-#endif
-#ifndef PMATTN_PF_KEEP
-#define PMATTN_PF_KEEP 0
-#endif
-
 template <int D>
 struct Cfg {
-  static constexpr int CHUNK = PMATTN_PF_CHUNK;   // keys per iteration (CHUNK/16 blocks)
+  static constexpr int CHUNK = 32;            // keys per iteration (CHUNK/16 blocks)
   static constexpr int NBLK = CHUNK / 16;
   static constexpr int NTILE = CHUNK / 32;        // 32-key score tiles per chunk
   static constexpr int KSTEPS = D / 16;       // QK k-steps of 16 channels
@@ -201,13 +193,6 @@ __device__ __forceinline__ int key_off(int kt, int r, int h) {
   return 32 * kt + 16 * (r >> 3) + 8 * h + 4 * ((r >> 2) & 1) + (r & 3);
 }
 
-template <int D>
-__device__ __forceinline__ void keep_compute_branch() {
-#if PMATTN_PF_KEEP
-  keep_branch();
-#endif
-}
-
 // max without the sNaN quieting that fmaxf needs (scores are never
 // signalling NaNs)
 __device__ __forceinline__ float fmax_nq(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -255,7 +240,6 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
     __builtin_amdgcn_sched_barrier(0);
   }
   if (mask) {
-    keep_compute_branch<D>();
     // visible iff key < lim (lim = min(pos + 1, kv_end) - c0 for this lane's row)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = key_off(kt, r, h) < lim ? s[r] : kNegInf;
@@ -277,7 +261,6 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
   // with no visible key so far has threshold -inf: its first one moves it)
   const bool grow = mx > rr.thr;
   if (__any(grow)) {
-    keep_compute_branch<D>();
     const float r2 = mx * sl2;
     const float alpha = !grow ? 1.f : rr.thr == kNegInf ? 0.f : __builtin_amdgcn_exp2f(rr.ref2 - r2);
     l_part *= alpha;

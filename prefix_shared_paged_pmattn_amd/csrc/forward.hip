@@ -1,6 +1,6 @@
 // Launcher half of the C ABI: uploads a plan's work list into the caller's
 // workspace and launches the tile-task kernels and the merge on the caller's
-// stream. All device memory is the caller's; nothing here allocates.
+// stream. All device memory is the caller's; nothing here allocates it.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
@@ -14,11 +14,6 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// Which plan's lists each workspace currently holds (by plan id; ids are never
-// reused), so that forward() uploads only when the workspace changed hands.
-std::mutex g_ws_mu;
-std::unordered_map<const void*, uint64_t> g_ws_owner;
-
 // Per-device auxiliary streams (default priority) and fork/join events: a plan
 // that mixes wave tasks (decode/verify, KV-stream bound) and workgroup tasks
 // (prefill, MFMA bound) runs the two kinds concurrently, the wave-task classes
@@ -27,16 +22,15 @@ std::unordered_map<const void*, uint64_t> g_ws_owner;
 // The record/wait sequence is enqueued under a mutex, so concurrent callers
 // never interleave the shared events (a wait binds to the latest record at
 // enqueue time).
-#ifndef PMATTN_AUX_STREAMS
-#define PMATTN_AUX_STREAMS 2
-#endif
-constexpr int kAux = PMATTN_AUX_STREAMS;
+constexpr int kAux = 2;
 struct DeviceAux {
   hipStream_t stream[kAux] = {};
   hipEvent_t fork = nullptr, join[kAux] = {};
 };
 std::mutex g_aux_mu;
 std::unordered_map<int, DeviceAux> g_aux;
+
+}  // namespace
 
 pmattn_status hip_fail(hipError_t e, const char* what) {
   return fail(PMATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -48,49 +42,15 @@ pmattn_status upload(const Plan& P, void* ws, hipStream_t st) {
                                   hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
   }
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  g_ws_owner[ws] = P.id;
   return PMATTN_OK;
 }
 
-}  // namespace
-}  // namespace pmattn
-
-using namespace pmattn;
-
-extern "C" {
-
-void pmattn_plan_destroy(pmattn_plan_t plan) {
-  if (!plan) return;
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    for (auto it = g_ws_owner.begin(); it != g_ws_owner.end();)
-      it = (it->second == plan->p.id) ? g_ws_owner.erase(it) : std::next(it);
-  }
-  delete plan;
-}
-
-pmattn_status pmattn_plan_upload(pmattn_plan_t plan, void* workspace, size_t ws_bytes, void* stream) {
-  clear_error();
-  if (!plan || !workspace) return fail(PMATTN_E_INVALID, "NULL plan or workspace");
-  if (ws_bytes < plan->p.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
-  return upload(plan->p, workspace, static_cast<hipStream_t>(stream));
-}
-
-// Upload the plan's tables into `workspace` unless this plan put them there last.
-static pmattn_status ensure_uploaded(const Plan& P, void* workspace, hipStream_t st) {
-  bool need_upload;
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    auto it = g_ws_owner.find(workspace);
-    need_upload = it == g_ws_owner.end() || it->second != P.id;
-  }
-  return need_upload ? upload(P, workspace, st) : PMATTN_OK;
-}
-
-static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
-                               const void* v_pool, const int32_t* block_table_dev, void* out,
-                               float* lse, void* workspace, size_t ws_bytes, void* stream) {
+// use_aux: the wave-task classes of a plan that also holds workgroup tasks may run
+// on the per-device auxiliary streams (created on first use); without it every
+// class runs in turn on the caller's stream.
+pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table_dev, void* out,
+                        float* lse, void* workspace, size_t ws_bytes, void* stream, bool use_aux) {
   if (!plan) return fail(PMATTN_E_INVALID, "plan is NULL");
   const Plan& P = plan->p;
   if (P.items.empty()) return PMATTN_OK;
@@ -98,10 +58,6 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     return fail(PMATTN_E_INVALID, "q, k_pool, v_pool, block_table, out and workspace must be non-NULL");
   if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  {
-    pmattn_status s = ensure_uploaded(P, workspace, st);
-    if (s != PMATTN_OK) return s;
-  }
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   AttnArgs a;
   a.q = q;
@@ -148,7 +104,7 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
     if (P.class_rows[c] > kMaxWaveRows) return launch_attn_prefill(P.head_dim, ac, s);
     return launch_attn_bf16(P.head_dim, P.class_rows[c], ac, concurrent, P.class_stream[c], s);
   };
-  if (!concurrent) {
+  if (!concurrent || !use_aux) {
     for (size_t c = 0; c < P.class_rows.size(); ++c) {
       hipError_t e = launch_class(c, st);
       if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
@@ -193,19 +149,13 @@ static pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_
   return PMATTN_OK;
 }
 
-static pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
-                               size_t ws_bytes, void* stream) {
+pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
+                        size_t ws_bytes, void* stream) {
   if (!plan) return fail(PMATTN_E_INVALID, "plan is NULL");
   const Plan& P = plan->p;
   if (P.merge_rows.empty()) return PMATTN_OK;
   if (!out || !workspace) return fail(PMATTN_E_INVALID, "out and workspace must be non-NULL");
   if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
-  {
-    std::lock_guard<std::mutex> lk(g_ws_mu);
-    auto it = g_ws_owner.find(workspace);
-    if (it == g_ws_owner.end() || it->second != P.id)
-      return fail(PMATTN_E_INVALID, "workspace does not hold this plan's lists: run the tasks pass first");
-  }
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   MergeArgs m;
   m.part_o = reinterpret_cast<const float*>(ws + P.off_part_o);
@@ -224,11 +174,26 @@ static pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* 
   return PMATTN_OK;
 }
 
+}  // namespace pmattn
+
+using namespace pmattn;
+
+extern "C" {
+
+void pmattn_plan_destroy(pmattn_plan_t plan) { delete plan; }
+
+pmattn_status pmattn_plan_upload(pmattn_plan_t plan, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!plan || !workspace) return fail(PMATTN_E_INVALID, "NULL plan or workspace");
+  if (ws_bytes < plan->p.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
+  return upload(plan->p, workspace, static_cast<hipStream_t>(stream));
+}
+
 pmattn_status pmattn_forward_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
                                    const void* v_pool, const int32_t* block_table_dev, void* out,
                                    float* lse, void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
-  return run_tasks(plan, q, k_pool, v_pool, block_table_dev, out, lse, workspace, ws_bytes, stream);
+  return run_tasks(plan, q, k_pool, v_pool, block_table_dev, out, lse, workspace, ws_bytes, stream, true);
 }
 
 pmattn_status pmattn_forward_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
@@ -249,8 +214,6 @@ pmattn_status pmattn_kv_append(pmattn_plan_t plan, const void* k_new, const void
     return fail(PMATTN_E_INVALID, "k_new, v_new, block_table, k_pool, v_pool and workspace must be non-NULL");
   if (ws_bytes < P.ws_bytes) return fail(PMATTN_E_WORKSPACE, "workspace too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  pmattn_status s = ensure_uploaded(P, workspace, st);
-  if (s != PMATTN_OK) return s;
   AppendArgs a;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -286,7 +249,7 @@ pmattn_status pmattn_forward(pmattn_plan_t plan, const void* q, const void* k_po
                              float* lse, void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
   pmattn_status s = run_tasks(plan, q, k_pool, v_pool, block_table_dev, out, lse, workspace,
-                              ws_bytes, stream);
+                              ws_bytes, stream, true);
   if (s != PMATTN_OK) return s;
   return run_merge(plan, out, lse, workspace, ws_bytes, stream);
 }

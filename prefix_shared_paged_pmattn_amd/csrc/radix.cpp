@@ -42,6 +42,12 @@ struct Node {
 struct Seq {
   std::vector<int32_t> tokens;
   std::vector<int32_t> blocks;
+  // source block of the copy-on-write order admit gave out (-1: none). The
+  // sequence holds a reference on it until its next extend, publish or
+  // release, by which time the copy has run: otherwise an eviction during the
+  // admit could free it, and a later admit of the same batch could receive it
+  // as a fresh block (or copy destination) while the copy still reads it.
+  int32_t cow_src = -1;
 };
 
 struct Match {
@@ -74,6 +80,10 @@ using Cache = pmattn_radix_s;
 void ref(Cache& c, int32_t b) { ++c.refs[b]; }
 void unref(Cache& c, int32_t b) {
   if (--c.refs[b] == 0) c.free_list.push_back(b);
+}
+void drop_cow_src(Cache& c, Seq& s) {
+  if (s.cow_src >= 0) unref(c, s.cow_src);
+  s.cow_src = -1;
 }
 
 bool is_leaf(const Node* n) { return n->parent && n->children.empty(); }
@@ -229,8 +239,8 @@ pmattn_status pmattn_radix_admit(pmattn_radix_t c, const int32_t* tokens, int32_
       if (src >= 0) unref(*c, src);
       return fail(PMATTN_E_CAPACITY, "block pool exhausted");
     }
-    if (src >= 0) unref(*c, src);  // the copy order keeps no reference
     Seq s;
+    s.cow_src = src;  // the reference taken above stays with the sequence
     s.tokens.assign(tokens, tokens + n);
     s.blocks = shared;
     s.blocks.insert(s.blocks.end(), fresh.begin(), fresh.end());
@@ -260,6 +270,7 @@ pmattn_status pmattn_radix_extend(pmattn_radix_t c, int32_t seq_id, const int32_
   auto it = c->seqs.find(seq_id);
   if (it == c->seqs.end()) return fail(PMATTN_E_INVALID, "unknown seq_id");
   Seq& s = it->second;
+  drop_cow_src(*c, s);
   const int32_t total = (int32_t)s.tokens.size() + n;
   const int32_t nb = (total + kB - 1) / kB;
   if (capacity < nb) return fail(PMATTN_E_INVALID, "block_table capacity too small");
@@ -281,7 +292,8 @@ pmattn_status pmattn_radix_publish(pmattn_radix_t c, int32_t seq_id) {
   if (!c) return fail(PMATTN_E_INVALID, "NULL cache");
   auto it = c->seqs.find(seq_id);
   if (it == c->seqs.end()) return fail(PMATTN_E_INVALID, "unknown seq_id");
-  const Seq& s = it->second;
+  Seq& s = it->second;
+  drop_cow_src(*c, s);
   const int32_t n = (int32_t)s.tokens.size();
   try {
     Match m = match(*c, s.tokens.data(), n);
@@ -320,6 +332,7 @@ pmattn_status pmattn_radix_release(pmattn_radix_t c, int32_t seq_id) {
   if (!c) return fail(PMATTN_E_INVALID, "NULL cache");
   auto it = c->seqs.find(seq_id);
   if (it == c->seqs.end()) return fail(PMATTN_E_INVALID, "unknown seq_id");
+  drop_cow_src(*c, it->second);
   for (int32_t b : it->second.blocks) unref(*c, b);
   c->seqs.erase(it);
   return PMATTN_OK;

@@ -8,7 +8,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 from . import _lib as L
-from . import _check, _dtype_code, _need_dev, _stream_ptr, _torch
+from . import _check, _dtype_code, _need_dev, _torch
 
 BLOCK = 16
 
@@ -81,17 +81,40 @@ class RadixCache:
 
 def copy_blocks(copies: List[Tuple[int, int, int]], k_pool, v_pool, num_kv_heads: int, head_dim: int,
                 dtype="bf16", stream=None):
-    """``pmattn_copy_blocks``: run copy-on-write orders (src, dst, slots) on the GPU."""
+    """``pmattn_copy_blocks``: run copy-on-write orders (src, dst, slots) on the GPU.
+
+    Every order is checked on the host first: src and dst name blocks of the
+    pools (whose element type must be ``dtype``), slots lies in 0..16, src !=
+    dst and no dst repeats, so a bad order raises instead of writing outside
+    the pools. The order array is copied to the device on ``stream``, the
+    stream the kernel reads it on."""
     torch = _torch()
     _need_dev(k_pool, "k_pool")
     _need_dev(v_pool, "v_pool")
+    code = _dtype_code(dtype)
+    et = torch.bfloat16 if code == L.BF16 else torch.float32
+    if k_pool.dtype != et or v_pool.dtype != et:
+        raise ValueError(f"k_pool and v_pool must have dtype {et}")
+    if int(head_dim) not in (64, 128) or int(num_kv_heads) < 1:
+        raise ValueError("head_dim must be 64 or 128 and num_kv_heads >= 1")
+    per_block = int(num_kv_heads) * BLOCK * int(head_dim)
+    if k_pool.numel() != v_pool.numel() or k_pool.numel() % per_block:
+        raise ValueError("k_pool and v_pool must hold the same whole number of blocks")
+    nblocks = k_pool.numel() // per_block
     if not copies:
         return
-    arr = torch.tensor(np.asarray(copies, np.int32).reshape(-1, 3), device=k_pool.device)
-    if len({c[1] for c in copies}) != len(copies) or any(c[0] == c[1] for c in copies):
+    a = np.asarray(copies, np.int64).reshape(-1, 3)
+    if (a[:, :2] < 0).any() or (a[:, :2] >= nblocks).any():
+        raise ValueError(f"copy orders must name blocks in [0, {nblocks})")
+    if (a[:, 2] < 0).any() or (a[:, 2] > BLOCK).any():
+        raise ValueError("copy orders must copy 0..16 slots")
+    if len(set(a[:, 1].tolist())) != a.shape[0] or (a[:, 0] == a[:, 1]).any():
         raise ValueError("copy orders need distinct destinations and src != dst")
-    _check(L.load().pmattn_copy_blocks(ctypes.c_void_p(arr.data_ptr()), len(copies),
+    st = stream if stream is not None else torch.cuda.current_stream(k_pool.device)
+    with torch.cuda.stream(st):
+        arr = torch.tensor(a.astype(np.int32), device=k_pool.device)
+    _check(L.load().pmattn_copy_blocks(ctypes.c_void_p(arr.data_ptr()), int(a.shape[0]),
                                        ctypes.c_void_p(k_pool.data_ptr()), ctypes.c_void_p(v_pool.data_ptr()),
-                                       int(num_kv_heads), int(head_dim), _dtype_code(dtype),
-                                       _stream_ptr(stream, k_pool)))
+                                       int(num_kv_heads), int(head_dim), code,
+                                       ctypes.c_void_p(int(st.cuda_stream))))
     return arr

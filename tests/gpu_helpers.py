@@ -2,6 +2,7 @@
 library through its C ABI, and compare with the fp64 oracle."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -69,3 +70,37 @@ def compare(b, out, lse, rows=None, ref=None):
     assert stats["mean_abs"] <= tol["mean_abs"], stats
     assert stats["lse_max"] <= tol["lse"], stats
     return stats
+
+
+_FULL_REF = {}
+
+
+def oracle_all_rows(b, key=None, workers=None):
+    """``oracle.attend`` over every row of ``b``, one sequence per task on a
+    thread pool (numpy and BLAS release the GIL; BLAS runs one thread per
+    worker). Same function, same arithmetic per row as a single call; the
+    result is cached under ``key`` for tests that compare several GPU runs of
+    one workload."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    if key is not None and key in _FULL_REF:
+        return _FULL_REF[key]
+    off = b.row_offsets()
+    seqs = [s for s in range(len(b.q_len)) if b.q_len[s] > 0]
+    out = np.empty((b.num_rows, b.num_q_heads, b.head_dim), np.float64)
+    lse = np.empty((b.num_rows, b.num_q_heads), np.float64)
+
+    def one(s):
+        rows = np.arange(int(off[s]), int(off[s + 1]))
+        o, l = oracle.attend(b, rows=rows)
+        out[rows] = o
+        lse[rows] = l
+
+    workers = workers or max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, seqs))
+    if key is not None:
+        _FULL_REF[key] = (out, lse)
+    return out, lse

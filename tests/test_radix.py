@@ -162,3 +162,45 @@ def test_invalid_arguments():
     import ctypes
     assert lib.pmattn_radix_admit(c._h, None, 3, None, None, None, 0, None, None) == _lib.E_INVALID
     assert lib.pmattn_radix_publish(c._h, 77) == _lib.E_INVALID
+
+
+def test_copy_source_stays_pinned_when_its_leaf_is_evicted():
+    """A full pool: the admit that gets a copy-on-write order must evict the
+    very leaf holding the copy's source. The new sequence keeps a reference on
+    that block until its next extend/publish/release, so a second admit of the
+    same batch can receive it neither as a fresh block nor as its copy
+    destination (one copy launch would then read and write it at once)."""
+    c = RadixCache(5)
+    s1, _, bt1, _ = c.admit(range(40))             # 3 blocks: [0,16) [16,32) [32,40)
+    c.publish(s1)
+    c.release(s1)                                  # cached in the tree only; 2 blocks free
+    assert c.stats()["free_blocks"] == 2
+    # match 20 tokens: block 0 shared, block 1 copied (4 slots); 3 fresh blocks
+    # needed beside the shared one, so the tree's leaf is evicted
+    s2, cl, bt2, cp = c.admit(list(range(20)) + [99] * 44)
+    assert cl == 20 and cp is not None and cp[0] == bt1[1] and cp[2] == 4
+    assert c.stats()["evicted_nodes"] >= 1
+    src = cp[0]
+    assert src not in bt2.tolist() and c.block_refs(src) == 1   # held for the copy
+    # the pool is now full: a second admit cannot take the source block
+    with pytest.raises(pm.PmattnError) as e:
+        c.admit([7] * 16)
+    assert e.value.status == _lib.E_CAPACITY
+    c.publish(s2)                                  # the copy has run by now
+    assert c.block_refs(src) == 0
+    s3, _, bt3, cp3 = c.admit([7] * 16)
+    assert cp3 is None and bt3.tolist() == [src]
+
+
+def test_copy_source_released_by_extend_and_release():
+    for finish in ("extend", "release"):
+        c = RadixCache(16)
+        s1, _, bt1, _ = c.admit(range(40))
+        c.publish(s1)
+        s2, _, _, cp = c.admit(list(range(20)) + [5])
+        refs_before = c.block_refs(cp[0])
+        if finish == "extend":
+            c.extend(s2, [6], 22)
+        else:
+            c.release(s2)
+        assert c.block_refs(cp[0]) == refs_before - 1
