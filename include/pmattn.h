@@ -322,6 +322,23 @@ pmattn_status pmattn_forward_tasks(pmattn_plan_t plan, const void* q, const void
 pmattn_status pmattn_forward_merge(pmattn_plan_t plan, void* out, float* lse, void* workspace,
                                    size_t ws_bytes, void* stream);
 
+/* pmattn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments as pmattn_forward minus the workspace, same kernels and the
+ * same result: the plan's tables and partial records go into a static device
+ * array of the library (64 MiB, held by every GPU the library runs on until
+ * the process ends), which each call first fills with this plan's tables on
+ * `stream`. Calls no hipMalloc, hipFree or other allocating routine, and runs
+ * every task class on `stream`. Every call on one GPU shares that array and
+ * leaves its contents to the next: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be serialized by the caller,
+ * e.g. all on one stream. Errors: PMATTN_E_WORKSPACE when the plan needs more
+ * than the array holds (pmattn_plan_workspace_bytes > 64 MiB), otherwise as
+ * pmattn_forward. */
+pmattn_status pmattn_forward_noalloc(pmattn_plan_t plan, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table_dev, void* out,
+                                     float* lse, void* stream);
+
 /* Merge P partial attention results over disjoint key sets into the full
  * result (the Flash-Decoding merge): with L = ln sum_p exp(part_lse[p]),
  * out = sum_p exp(part_lse[p] - L) * part_o[p], lse = L. Partitions with

@@ -20,8 +20,8 @@ import numpy as np
 
 from . import _lib as L
 
-__all__ = ["Plan", "PmattnError", "plan", "forward", "forward_tasks", "forward_merge", "merge_lse", "kv_append", "build_batch",
-           "version", "BF16", "F32"]
+__all__ = ["Plan", "PmattnError", "plan", "forward", "forward_tasks", "forward_merge", "forward_noalloc",
+           "merge_lse", "kv_append", "build_batch", "version", "BF16", "F32"]
 
 BF16, F32 = L.BF16, L.F32
 
@@ -266,6 +266,33 @@ def forward_tasks(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, worksp
                                          _vp(block_table), _vp(out), _vp(lse), _vp(workspace),
                                          ws_bytes, _stream_ptr(stream, q)))
     return workspace
+
+
+def forward_noalloc(p: Plan, q, k_pool, v_pool, block_table, out, lse=None, stream=None):
+    """``pmattn_forward_noalloc``: :func:`forward` without a workspace (the
+    library's static device scratch holds the tables and partials; calls on
+    one GPU must not overlap). Tensors as for :func:`forward`."""
+    torch = _torch()
+    s = p.shape
+    et = _elem_dtype(s["dtype"])
+    r, hq, hkv, d = s["num_rows"], s["hq"], s["hkv"], s["d"]
+    pool_elems = s["num_pool_blocks"] * hkv * 16 * d
+    checks = [(q, "q", et, r * hq * d, True), (out, "out", et, r * hq * d, True),
+              (k_pool, "k_pool", et, pool_elems, False), (v_pool, "v_pool", et, pool_elems, False),
+              (block_table, "block_table", torch.int32, s["num_seqs"] * s["bt_stride"], True)]
+    if lse is not None:
+        checks.append((lse, "lse", torch.float32, r * hq, True))
+    for t, name, dt, n, exact in checks:
+        _need_dev(t, name)
+        if t.dtype != dt:
+            raise ValueError(f"{name} must have dtype {dt}, got {t.dtype}")
+        if (t.numel() != n) if exact else (t.numel() < n):
+            raise ValueError(f"{name} has {t.numel()} elements, expected {'' if exact else '>= '}{n}")
+        if t.data_ptr() % 16:
+            raise ValueError(f"{name} must be 16-byte aligned")
+    _check(L.load().pmattn_forward_noalloc(p.handle, _vp(q), _vp(k_pool), _vp(v_pool), _vp(block_table),
+                                           _vp(out), _vp(lse), _stream_ptr(stream, q)))
+    return out, lse
 
 
 PREFILL, DECODE, VERIFY = 0, 1, 2
