@@ -1,11 +1,16 @@
 """Benchmark of libpmattn on one MI355X.
 
-Default workload: decode over a paged GQA KV pool, one Llama-3-8B-shaped layer
-(64 sequences, context lengths uniform in [512, 4096], 32 query / 8 kv heads,
-head_dim 128, bf16, 16-token blocks, random non-contiguous block tables).
-``--config N`` selects one of the six synthetic workloads instead
-(1 tiny fp32, 2 decode, 3 few-shot shared prefix, 4 mixed chunk, 5 long decode,
-6 token-tree verify).
+Default workload: the mixed chunked batch the metric is quoted on (paged mixed
+attention): 16 prefill chunks of 512 tokens at unaligned starts, 96 decode
+rows and 32 sequences verifying 5 linear drafts, prefixes shared through a
+branching radix tree; 32 query / 8 kv heads, head_dim 128, bf16, 16-token
+blocks, random non-contiguous block tables. The same JSON line also carries
+the decode (64 sequences), few-shot prefill (256 x 128 on one shared 2048
+prefix) and long-context decode (8 x 32k) workloads, each timed the same way
+(``configs``), so that both halves of the metric (decode GB/s, prefill
+TFLOP/s) are measured by every run. ``--config N`` makes workload N the main
+line instead (1 tiny fp32, 2 decode, 3 few-shot, 4 mixed, 5 long decode, 6
+token-tree verify, 7 shared-prompt decode).
 
 One step = one ``pmattn_forward`` of the whole batch (tile tasks + merge) with
 inputs resident in HBM; the plan is built once per batch on the host (as a
@@ -42,12 +47,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """First 16 hex digits of the sha256 over the decode kernel's source and the
-    planner's (the planner decides the split partials the kernel writes)."""
+# Workload -> (committed rocprofv3 counter summary, sources of the dominant
+# kernel and of the planner that shapes its work)
+_TASK_KERNEL = {
+    2: ("attn_bf16_decode_64seq.md", ("attn_bf16.hip", "task_wave.h", "task_common.h", "plan.cpp")),
+    4: ("attn_mixed_chunk_144seq.md", ("attn_mixed.hip", "task_wave.h", "task_wg.h", "task_common.h",
+                                       "plan.cpp")),
+}
+
+
+def kernel_source_hash(files):
+    """First 16 hex digits of the sha256 over the given sources (csrc/)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "plan.cpp"):
+    for f in files:
         with open(os.path.join(ROOT, "prefix_shared_paged_pmattn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -56,51 +69,82 @@ def kernel_source_hash():
 def measured_traffic(config_idx):
     """HBM bytes per launch of the tasks kernel from the committed rocprofv3
     counter summary (FETCH_SIZE and WRITE_SIZE, calibrated by a 1 GiB copy),
-    or None when there is none for this workload or the kernel source has
+    or None when there is none for this workload or the kernel's sources have
     changed since the counters were taken."""
-    import hashlib
-    prof = {2: "attn_bf16_decode_64seq.md"}.get(config_idx)
+    prof = _TASK_KERNEL.get(config_idx)
     if prof is None:
         return None
-    path = os.path.join(ROOT, "profiles", prof)
     try:
-        text = open(path).read()
-        sha = kernel_source_hash()
+        text = open(os.path.join(ROOT, "profiles", prof[0])).read()
+        sha = kernel_source_hash(prof[1])
     except OSError:
         return None
     fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes", "kernel_source")))
-    if fields.get("kernel_source_sha256_16") != sha:
+    if fields.get("kernel_source_sha256_16") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(batch, work, min_seconds=10.0):
-    """Time the fp64 oracle on the same batch (whole batch, repeated until
-    ``min_seconds`` of CPU work); returns a dict in the metric's unit."""
-    import oracle
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    runs = []
-    t_end = time.perf_counter() + min_seconds
-    while True:
+        return 1
+
+
+def cpu_baseline(batch, work, seconds=15.0):
+    """The fp64 oracle on a bounded sample of the same batch: whole sequences
+    in a fixed seeded order, each through ``oracle.attend`` on its rows, until
+    ``seconds`` of CPU time; the rate is the sample's own algorithmic bytes
+    (or FLOP) over that time, in the metric's unit."""
+    import oracle
+    import workloads as wl
+    threads = _blas_threads()
+    off = batch.row_offsets()
+    seqs = [s for s in np.random.Generator(np.random.PCG64(7)).permutation(batch.num_seqs) if batch.q_len[s] > 0]
+    done = np.zeros(batch.num_seqs, bool)
+    t = 0.0
+    for s in seqs:
         t0 = time.perf_counter()
-        oracle.attend(batch)
-        runs.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end and len(runs) >= 2:
+        oracle.attend(batch, rows=np.arange(int(off[s]), int(off[s + 1])))
+        t += time.perf_counter() - t0
+        done[s] = True
+        if t >= seconds:
             break
-    t = statistics.median(runs)
-    bound = "hbm" if work["flop"] / work["bytes"] < 100 else "mfma"
+    sw = wl.algorithmic_work(wl.subset(batch, done, batch.name + "[sample]"))
+    bound = "hbm" if work["flop"] / work["bytes"] < 315 else "mfma"
     if bound == "hbm":
-        val, unit = work["bytes"] / t / 1e9, "GB/s"
+        val, unit = sw["bytes"] / t / 1e9, "GB/s"
     else:
-        val, unit = work["flop"] / t / 1e12, "TFLOP/s"
+        val, unit = sw["flop"] / t / 1e12, "TFLOP/s"
+    kinds = {}
+    for s in np.nonzero(done)[0]:
+        k = wl.seq_kind(int(batch.q_len[s]))
+        kinds[k] = kinds.get(k, 0) + 1
     return dict(value=val, unit=unit, cores=int(threads), kind="oracle",
-                sample=f"whole batch ({batch.num_seqs} sequences, {batch.num_rows} rows), "
-                       f"{len(runs)} runs of {t:.2f} s median, numpy fp64 (BLAS threads={threads}; "
-                       f"exp single-threaded); host os.cpu_count()={os.cpu_count()}")
+                sample=f"{int(done.sum())} of {batch.num_seqs} sequences ({', '.join(f'{v} {k}' for k, v in sorted(kinds.items()))}; "
+                       f"{sw['bytes']} algorithmic bytes, {sw['flop']:.4g} FLOP) in {t:.1f} s, one oracle.attend "
+                       f"call per sequence, numpy fp64 (BLAS threads={threads}; exp single-threaded); "
+                       f"host os.cpu_count()={os.cpu_count()}")
+
+
+def per_core_oracle():
+    """The oracle on the whole tiny fp32 batch and the whole 64-sequence
+    decode batch with BLAS limited to one thread (one core)."""
+    import oracle
+    import workloads as wl
+    from threadpoolctl import threadpool_limits
+    res = {}
+    with threadpool_limits(1):
+        for idx, key in ((1, "tiny"), (2, "decode")):
+            b = wl.config(idx)
+            w = wl.algorithmic_work(b)
+            t0 = time.perf_counter()
+            oracle.attend(b)
+            t = time.perf_counter() - t0
+            res[key] = dict(workload=b.name, seconds=t, gbs=w["bytes"] / t / 1e9, threads=1)
+    return res
 
 
 def timed_forward(pm, p, q, kp, vp, bt, out, lse, stream, args, flush):
@@ -306,13 +350,15 @@ def bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--no-class-breakdown", action="store_true",
                     help="mixed batches: skip timing each query class alone")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the main workload (skip the other workloads' lines)")
     ap.add_argument("--num-kv-splits", type=int, default=None)
     ap.add_argument("--num-cus", type=int, default=0, help="compute units the plan balances for")
     ap.add_argument("--work-shuffle-seed", type=int, default=0,
@@ -350,28 +396,34 @@ def main():
         print(json.dumps(dict(copy_bytes=1 << 30, dispatches=3)), flush=True)
         return
 
-    t0 = time.perf_counter()
-    b = wl.config(args.config)
-    if args.num_kv_splits is not None:
-        b = b.replace(num_kv_splits=args.num_kv_splits)
-    work = wl.algorithmic_work(b)
-    log(f"[bench] generated {b.name} in {time.perf_counter() - t0:.1f}s: rows={b.num_rows} "
-        f"blocks={b.num_pool_blocks} unique_kv_tokens={work['unique_kv_tokens']} flop={work['flop']:.4g} "
-        f"bytes={work['bytes']:.4g}")
-
     dev = torch.device("cuda:0")
-    if b.dtype == "bf16":
-        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)  # noqa: E731
-        et = torch.bfloat16
-    else:
-        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
-        et = torch.float32
-    q = conv(b.q).to(dev)
-    kp = conv(b.k_pool).to(dev)
-    vp = conv(b.v_pool).to(dev)
-    bt = torch.from_numpy(b.block_table).to(dev)
-    out = torch.empty((b.num_rows, b.num_q_heads, b.head_dim), dtype=et, device=dev)
-    lse = torch.empty((b.num_rows, b.num_q_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)       # 1 GiB, read to evict caches
+    flush_sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def flush():
+        torch.sum(scratch, dim=0, dtype=torch.int64, out=flush_sink)
+
+    def load(idx):
+        t0 = time.perf_counter()
+        b = wl.config(idx)
+        if args.num_kv_splits is not None and idx == args.config:
+            b = b.replace(num_kv_splits=args.num_kv_splits)
+        work = wl.algorithmic_work(b)
+        log(f"[bench] generated {b.name} in {time.perf_counter() - t0:.1f}s: rows={b.num_rows} "
+            f"blocks={b.num_pool_blocks} unique_kv_tokens={work['unique_kv_tokens']} flop={work['flop']:.4g} "
+            f"bytes={work['bytes']:.4g}")
+        if b.dtype == "bf16":
+            conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)  # noqa: E731
+            et = torch.bfloat16
+        else:
+            conv = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+            et = torch.float32
+        t = dict(q=conv(b.q).to(dev), kp=conv(b.k_pool).to(dev), vp=conv(b.v_pool).to(dev),
+                 bt=torch.from_numpy(b.block_table).to(dev),
+                 out=torch.empty((b.num_rows, b.num_q_heads, b.head_dim), dtype=et, device=dev),
+                 lse=torch.empty((b.num_rows, b.num_q_heads), dtype=torch.float32, device=dev))
+        return b, work, conv, t
 
     def make_plan_for(x):
         return pm.plan(x.q_len, x.seq_len, x.q_start, x.block_table,
@@ -381,58 +433,61 @@ def main():
                        work_shuffle_seed=args.work_shuffle_seed, tree_parent=x.tree_parent,
                        cascade=args.cascade)
 
-    def make_plan():
-        return make_plan_for(b)
-
     if args.op == "append":
-        return bench_append(args, b, pm, make_plan, dev, conv, kp, vp, bt)
+        b, work, conv, t = load(args.config)
+        return bench_append(args, b, pm, lambda: make_plan_for(b), dev, conv, t["kp"], t["vp"], t["bt"])
 
-    plan_times = []
-    for _ in range(20):
-        t = time.perf_counter()
-        p = make_plan()
-        plan_times.append(time.perf_counter() - t)
-    plan_us = statistics.median(plan_times) * 1e6
-    tabs = p.tables()
-    stream = torch.cuda.current_stream(dev)
-    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)       # 1 GiB, read to evict caches
-    flush_sink = torch.empty((), dtype=torch.int64, device=dev)
+    def run(idx, b, work, t):
+        """Plan (host time: median of 20) and time K steps; the workload's
+        summary with its rate against its own bound."""
+        plan_times = []
+        for _ in range(20):
+            t0 = time.perf_counter()
+            p = make_plan_for(b)
+            plan_times.append(time.perf_counter() - t0)
+        tabs = p.tables()
+        t_task, t_merge, t_step, wall = timed_forward(pm, p, t["q"], t["kp"], t["vp"], t["bt"], t["out"],
+                                                      t["lse"], stream, args, flush)
+        ms_step, ms_task = statistics.mean(t_step), statistics.mean(t_task)
+        log(f"[bench] {b.name}: plan {statistics.median(plan_times) * 1e6:.1f} us host; items={tabs['items'].shape[0]} "
+            f"classes={tabs['class_rows'].tolist()} one kernel={bool(tabs['mixed_kernel'])} "
+            f"merge_rows={tabs['merge_rows'].shape[0]} ws={p.workspace_bytes} B")
+        log(f"[bench] {b.name}: step ms mean {ms_step:.4f} median {statistics.median(t_step):.4f} "
+            f"p10 {np.percentile(t_step, 10):.4f} p90 {np.percentile(t_step, 90):.4f}; "
+            f"tasks {ms_task:.4f} merge {statistics.mean(t_merge):.4f}; wall incl. flush "
+            f"{wall / args.steps * 1e3:.4f} ms/step")
+        t_bytes = work["bytes"] / HBM_PEAK_GBS / 1e9 * 1e3        # ms at the HBM roofline
+        peak_f = MFMA_BF16_PEAK_TFS if b.dtype == "bf16" else FP32_PEAK_TFS
+        t_flop = work["flop"] / peak_f / 1e12 * 1e3               # ms at the MFMA (or fp32) roofline
+        bound = "mfma" if t_flop > t_bytes else "hbm"
+        if bound == "mfma":
+            value, unit = work["flop"] / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+            achieved = work["flop"] / (ms_task * 1e-3) / 1e12
+            peak = peak_f
+        else:
+            value, unit = work["bytes"] / (ms_step * 1e-3) / 1e9, "GB/s"
+            achieved = work["bytes"] / (ms_task * 1e-3) / 1e9
+            peak = HBM_PEAK_GBS
+        plain = (args.num_kv_splits is None and not args.num_cus and not args.work_shuffle_seed
+                 and args.cascade == 2)
+        roof = dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
+                    traffic=measured_traffic(idx) if plain else None)
+        res = dict(workload=b.name, ms_per_step=ms_step, tasks_ms=ms_task, merge_ms=statistics.mean(t_merge),
+                   value=value, unit=unit, roofline=roof, frac_step=value / peak,
+                   gbs=work["bytes"] / (ms_step * 1e-3) / 1e9, tflops=work["flop"] / (ms_step * 1e-3) / 1e12,
+                   # both resources can be busy at once: the bound is the slower of the two
+                   max_bound=dict(hbm_ms=t_bytes, mfma_ms=t_flop, frac_step=max(t_bytes, t_flop) / ms_step,
+                                  frac_kernel=max(t_bytes, t_flop) / ms_task),
+                   plan_host_us=statistics.median(plan_times) * 1e6, one_kernel=bool(tabs["mixed_kernel"]),
+                   algorithmic_bytes=work["bytes"], flop=work["flop"])
+        log(f"[bench] {b.name}: {value:.1f} {unit} per step; tasks pass {achieved:.1f} {unit} = "
+            f"{100 * roof['frac']:.1f}% of {bound} peak; max-bound {100 * res['max_bound']['frac_step']:.1f}% of step")
+        return p, res
 
-    def flush():
-        torch.sum(scratch, dim=0, dtype=torch.int64, out=flush_sink)
-
-    t_task, t_merge, t_step, wall = timed_forward(pm, p, q, kp, vp, bt, out, lse, stream, args, flush)
-    ms_step = statistics.mean(t_step)
-    ms_task = statistics.mean(t_task)
-    log(f"[bench] plan {plan_us:.1f} us host; items={tabs['items'].shape[0]} "
-        f"classes={tabs['class_rows'].tolist()} merge_rows={tabs['merge_rows'].shape[0]} "
-        f"ws={p.workspace_bytes} B")
-    log(f"[bench] step ms mean {ms_step:.4f} median {statistics.median(t_step):.4f} "
-        f"p10 {np.percentile(t_step, 10):.4f} p90 {np.percentile(t_step, 90):.4f}; "
-        f"tasks {ms_task:.4f} merge {statistics.mean(t_merge):.4f}; wall incl. flush "
-        f"{wall / args.steps * 1e3:.4f} ms/step")
-
-    flop_bound = work["flop"] / work["bytes"] > 315   # above the MI355X ridge point
-    if flop_bound:
-        value = work["flop"] / (ms_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        achieved = work["flop"] / (ms_task * 1e-3) / 1e12
-        peak = MFMA_BF16_PEAK_TFS if b.dtype == "bf16" else FP32_PEAK_TFS
-        roof = dict(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak,
-                    traffic=None)
-    else:
-        value = work["bytes"] / (ms_step * 1e-3) / 1e9
-        unit = "GB/s"
-        achieved = work["bytes"] / (ms_task * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS,
-                    traffic=None if args.num_kv_splits is not None or args.num_cus or args.work_shuffle_seed or args.cascade != 2
-                    else measured_traffic(args.config))
-    log(f"[bench] value {value:.1f} {unit}; dominant kernel (tasks pass) {achieved:.1f} {roof['unit']} "
-        f"= {100 * roof['frac']:.1f}% of {roof['bound']} peak")
-
-    res = dict(metric=METRIC, value=value, unit=unit, n_gpus=1, steps=args.steps,
-               warmup=args.warmup, ms_per_step=ms_step, higher_is_better=True, scaling="weak",
+    b, work, conv, t = load(args.config)
+    p, main_res = run(args.config, b, work, t)
+    res = dict(metric=METRIC, value=main_res["value"], unit=main_res["unit"], n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=main_res["ms_per_step"], higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype=b.dtype, data="synthetic",
                config=dict(workload=b.name, num_seqs=b.num_seqs, query_rows=b.num_rows,
                            q_heads=b.num_q_heads, kv_heads=b.num_kv_heads, head_dim=b.head_dim,
@@ -440,16 +495,33 @@ def main():
                            unique_kv_bytes=work["kv_bytes_unique"],
                            logical_kv_bytes=work["kv_bytes_logical"], flop=work["flop"],
                            algorithmic_bytes=work["bytes"], cache_flush_between_steps=not args.no_flush),
-               roofline=roof, plan_host_us=plan_us, tasks_ms=ms_task,
-               merge_ms=statistics.mean(t_merge))
+               roofline=main_res["roofline"],
+               **{k: main_res[k] for k in ("tasks_ms", "merge_ms", "plan_host_us", "one_kernel", "gbs", "tflops",
+                                           "max_bound")})
     kinds = {wl.seq_kind(int(n)) for n in b.q_len if n > 0}
     if len(kinds) > 1 and not args.no_class_breakdown:
-        res["class_breakdown"] = class_breakdown(pm, b, make_plan_for, kp, vp, conv, dev, stream, args, flush)
+        res["class_breakdown"] = class_breakdown(pm, b, make_plan_for, t["kp"], t["vp"], conv, dev, stream, args,
+                                                 flush)
         alone = sum(c["ms_per_step"] for c in res["class_breakdown"].values())
-        log(f"[bench] classes alone sum to {alone:.4f} ms/step; together {ms_step:.4f} ms/step")
+        log(f"[bench] classes alone sum to {alone:.4f} ms/step; together {main_res['ms_per_step']:.4f} ms/step")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, work)
-        log(f"[bench] cpu baseline {res['cpu_baseline']['value']:.3f} {res['cpu_baseline']['unit']}")
+        log(f"[bench] cpu baseline {res['cpu_baseline']['value']:.3f} {res['cpu_baseline']['unit']} "
+            f"({res['cpu_baseline']['sample']})")
+        res["cpu_baseline"]["per_core"] = per_core_oracle()
+        log(f"[bench] oracle at one thread: {res['cpu_baseline']['per_core']}")
+    del t, p
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        res["configs"] = {}
+        for idx in (2, 3, 5):
+            if idx == args.config:
+                continue
+            bi, wi, _, ti = load(idx)
+            _, ri = run(idx, bi, wi, ti)
+            res["configs"][str(idx)] = ri
+            del ti
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

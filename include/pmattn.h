@@ -245,6 +245,17 @@ typedef struct pmattn_plan_tables {
    * readers. The workgroup kernel stages K/V through LDS with cacheable
    * loads whatever the flag. */
   const int32_t* item_stream;
+  /* 1: pmattn_forward runs the whole batch as one kernel (bf16 plans without
+   * token trees that hold both 16-row tasks and larger ones). Workgroup i of
+   * that launch runs mix_table[i]: 4 * item + 2 * c (one task on the whole
+   * workgroup; c = 1 for items of cascade classes) or 4 * b + 1 (bundle b: wave
+   * w runs mix_bundles[4 * b + w] = item * 2 + c, or nothing for -1). Every
+   * item appears exactly once. */
+  int32_t mixed_kernel;
+  int32_t num_mix_entries;
+  const int32_t* mix_table;         /* [num_mix_entries] */
+  int32_t num_mix_bundles;
+  const int32_t* mix_bundles;       /* [4 * num_mix_bundles] */
 } pmattn_plan_tables;
 
 /* Build a plan on the host: the Token-Table / Task-Table step of the

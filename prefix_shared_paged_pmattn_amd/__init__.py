@@ -117,7 +117,10 @@ class Plan:
             rec_index=arr(t.rec_index, t.num_rec_index),
             slot_begin=arr(t.slot_begin, t.num_slots + 1) if t.num_slots else np.zeros(0, np.int32),
             class_stream=arr(t.class_stream, t.num_classes),
-            item_stream=arr(t.item_stream, t.num_items))
+            item_stream=arr(t.item_stream, t.num_items),
+            mixed_kernel=int(t.mixed_kernel),
+            mix_table=arr(t.mix_table, t.num_mix_entries),
+            mix_bundles=arr(t.mix_bundles, 4 * t.num_mix_bundles))
 
     def upload(self, workspace, stream=None):
         """``pmattn_plan_upload``: copy the plan's tables (work list, merge

@@ -82,6 +82,11 @@ class PlanTables(ctypes.Structure):
         ("slot_begin", _i32p),
         ("class_stream", _i32p),
         ("item_stream", _i32p),
+        ("mixed_kernel", ctypes.c_int32),
+        ("num_mix_entries", ctypes.c_int32),
+        ("mix_table", _i32p),
+        ("num_mix_bundles", ctypes.c_int32),
+        ("mix_bundles", _i32p),
     ]
 
 

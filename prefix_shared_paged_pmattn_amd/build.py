@@ -20,8 +20,8 @@ LIB = os.path.join(PKG, "libpmattn.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["attn_bf16.hip", "attn_prefill.hip", "attn_f32_merge.hip", "kv_append.hip", "forward.hip",
-               "noalloc.hip"]
+HIP_SOURCES = ["attn_bf16.hip", "attn_prefill.hip", "attn_mixed.hip", "attn_f32_merge.hip", "kv_append.hip",
+               "forward.hip", "noalloc.hip"]
 CXX_SOURCES = ["plan.cpp", "radix.cpp", "batch.cpp"]
 
 HIP_FLAGS = [

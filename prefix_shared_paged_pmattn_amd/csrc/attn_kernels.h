@@ -40,6 +40,17 @@ struct AttnArgs {
   float scale_log2;              // scale * log2(e)
 };
 
+// The mixed-batch kernel (attn_mixed.hip): workgroup i runs table[i], a
+// workgroup task (4 * item + 2 * cascade) or a bundle of four wave tasks
+// (4 * bundle + 1; bundles[4 * bundle + wave] = item * 2 + cascade, or -1).
+struct MixedArgs {
+  AttnArgs a;                    // a.items: the whole work list; a.q_row: the virtual
+                                 // row table (cascade entries); a.item_stream per item
+  const int32_t* table;
+  const int32_t* bundles;
+  int32_t entries;
+};
+
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
@@ -88,6 +99,7 @@ pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* workspa
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, int stream,
                             hipStream_t st);
 hipError_t launch_attn_prefill(int head_dim, const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_mixed(int head_dim, const MixedArgs& m, hipStream_t st);
 hipError_t launch_attn_f32(int head_dim, const AttnArgs& a, hipStream_t st);
 hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStream_t st);
 hipError_t launch_kv_append(int head_dim, int dtype, const AppendArgs& a, hipStream_t st);

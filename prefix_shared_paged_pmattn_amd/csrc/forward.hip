@@ -80,6 +80,21 @@ pmattn_status run_tasks(pmattn_plan_t plan, const void* q, const void* k_pool,
   a.scale = P.scale;
   a.scale_log2 = P.scale * kLog2e;
   const pmattn_work_item* items = reinterpret_cast<const pmattn_work_item*>(ws + P.off_items);
+  if (P.mixed) {
+    // one kernel for the whole mixed batch, on the caller's stream
+    MixedArgs m;
+    m.a = a;
+    m.a.items = items;
+    m.a.item_stream = reinterpret_cast<const int32_t*>(ws + P.off_istream);
+    m.a.q_row = P.vrow_src.empty() ? nullptr : reinterpret_cast<const int32_t*>(ws + P.off_vrow);
+    m.a.item_count = (int32_t)P.items.size();
+    m.table = reinterpret_cast<const int32_t*>(ws + P.off_mix_table);
+    m.bundles = reinterpret_cast<const int32_t*>(ws + P.off_mix_bundles);
+    m.entries = (int32_t)P.mix_table.size();
+    hipError_t e = launch_attn_mixed(P.head_dim, m, st);
+    if (e != hipSuccess) return hip_fail(e, "mixed-batch kernel launch");
+    return PMATTN_OK;
+  }
   bool has_wg = false, has_wave = false;
   for (int32_t rows : P.class_rows) (rows > kMaxWaveRows ? has_wg : has_wave) = true;
   const bool concurrent = P.dtype == PMATTN_BF16 && has_wg && has_wave;

@@ -133,6 +133,15 @@ constexpr int64_t kStreamMinBlocks = 16;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;
 constexpr int kMaxAutoSplits = 64;
+// Mixed-batch kernel: estimated duration per KV block (1/100 us) of a tile
+// of more than 64 rows, of a smaller workgroup task and of a 16-row wave task,
+// measured per table entry on MI355X (mixed-chunk workload, one session:
+// 0.72, 0.98 and 1.45 us).
+constexpr int64_t kMixTileBlockCost = 72;
+constexpr int64_t kMixSmallTaskBlockCost = 98;
+constexpr int64_t kMixWaveBlockCost = 145;
+// Shader engines per XCD, which receive an XCD's workgroups in turn.
+constexpr int kSeRoundRobin = 4;
 // Automatic cascade: a shared run becomes a group only with this many members
 // and this many blocks (measured on the pages' workloads).
 constexpr int kCascadeAutoMembers = 8;
@@ -728,6 +737,113 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     }
   }
 
+  // ---- mixed-batch kernel table ----------------------------------------------
+  // One kernel serves a bf16 batch that mixes 16-row wave tasks (decode rows)
+  // with larger tasks (prefill chunks, verify drafts), without token trees
+  // (XY-Serve review, "Core claim": one meta-kernel runs every stage's tile
+  // tasks from one table, ordered by cost across cores). Each workgroup runs
+  // one table entry: a workgroup task (K/V staged once in LDS for its four
+  // waves) or a bundle of four wave tasks (one per wave, each streaming its
+  // own K/V). Per XCD (kv head g on XCD g, as in xcd_order, so that readers
+  // of a block meet in one L2), both kinds are taken largest first and
+  // interleaved in proportion to their estimated cost, so that every CU holds
+  // some of each while they run (decode streams HBM beside MFMA-bound prefill
+  // tiles; POD-Attention, XY-Serve review reference list) and both kinds end
+  // together. Bundles hold four wave tasks of neighbouring cost.
+  {
+    bool has_wave = false, has_wg = false;
+    for (int32_t rows : P.class_rows) (rows <= kClassRows[0] ? has_wave : has_wg) = true;
+    P.mixed = d->dtype == PMATTN_BF16 && P.row_mask.empty() && has_wave && has_wg;
+    if (P.mixed) {
+      const int rep = d->num_kv_heads >= kXcds ? 1 : (kXcds + d->num_kv_heads - 1) / d->num_kv_heads;
+      struct Entry {
+        int64_t cost;
+        int32_t e;
+      };
+      std::vector<Entry> parts[2][kXcds];  // [0] workgroup tasks, [1] wave tasks
+      for (size_t c = 0; c + 1 < P.class_begin.size(); ++c) {
+        const int kind = P.class_rows[c] <= kClassRows[0] ? 1 : 0;
+        for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
+          const pmattn_work_item& it = P.items[i];
+          const int x = (d->num_kv_heads >= kXcds ? it.kv_head : it.kv_head * rep + it.seq % rep) % kXcds;
+          const int64_t nblk = (it.kv_end - it.kv_begin + kBlock - 1) / kBlock;
+          // estimated duration (1/100 us) in this kernel: per KV block, a
+          // tile of more than 64 rows 72 (MFMA bound), a smaller workgroup
+          // task 98 (one chunk in flight per workgroup), a 16-row wave task
+          // 145 (one chunk in flight per wave; a bundle lasts as long as its
+          // longest task). Measured per entry on MI355X, mixed-chunk workload.
+          const int64_t cost = nblk * (kind ? kMixWaveBlockCost
+                                            : P.class_rows[c] > kMaxWaveRows ? kMixTileBlockCost
+                                                                             : kMixSmallTaskBlockCost);
+          parts[kind][x].push_back(Entry{cost, i * 2 + P.class_cascade[c]});
+        }
+      }
+      std::vector<std::vector<int32_t>> lists(kXcds);
+      for (int x = 0; x < kXcds; ++x) {
+        for (int k = 0; k < 2; ++k) {
+          auto& v = parts[k][x];
+          std::stable_sort(v.begin(), v.end(), [](const Entry& a, const Entry& b) { return a.cost > b.cost; });
+          if (d->work_shuffle_seed)
+            for (size_t i = v.size(); i > 1; --i) std::swap(v[i - 1], v[splitmix64(rng) % i]);
+        }
+        // table entries of this XCD in three streams: tiles of more than 64
+        // rows, smaller workgroup tasks, and bundles of four wave tasks
+        std::vector<Entry> streams[3];
+        for (const Entry& en : parts[0][x]) {
+          const int32_t item = en.e >> 1;
+          const bool big = (int64_t)P.items[item].n_tok * G > kMaxWaveRows;
+          streams[big ? 0 : 1].push_back(Entry{en.cost, 4 * item + 2 * (en.e & 1)});
+        }
+        const auto& wv = parts[1][x];
+        for (size_t i = 0; i < wv.size(); i += kWaveTasksPerWg) {
+          const int32_t b = (int32_t)(P.mix_bundles.size() / kWaveTasksPerWg);
+          for (size_t k = i; k < i + kWaveTasksPerWg; ++k) P.mix_bundles.push_back(k < wv.size() ? wv[k].e : -1);
+          streams[2].push_back(Entry{wv[i].cost, 4 * b + 1});  // the bundle's longest task
+        }
+        // Interleave in proportion to estimated duration (next comes the
+        // stream that has used the smallest share of its own total), in
+        // groups of kSeRoundRobin entries of one stream and neighbouring cost.
+        // Within an XCD the hardware deals workgroups to its shader engines
+        // round-robin and in order (measured on MI355X: entry k of an XCD
+        // always lands on engine k % 4 of a fixed per-XCD order), so a group
+        // puts one entry of the same kind on every engine: the engines free
+        // their slots at the same pace (one full engine blocks dispatch to
+        // the others) and each engine's CUs see every kind in turn.
+        int64_t tot[3] = {0, 0, 0}, used[3] = {0, 0, 0};
+        size_t h[3] = {0, 0, 0};
+        for (int k = 0; k < 3; ++k)
+          for (const Entry& en : streams[k]) tot[k] += en.cost;
+        for (;;) {
+          int k = -1;
+          for (int j = 0; j < 3; ++j) {
+            if (h[j] == streams[j].size()) continue;
+            if (k < 0 || (__int128)used[j] * tot[k] < (__int128)used[k] * tot[j]) k = j;
+          }
+          if (k < 0) break;
+          for (int g = 0; g < kSeRoundRobin && h[k] < streams[k].size(); ++g) {
+            const Entry& en = streams[k][h[k]++];
+            used[k] += en.cost;
+            lists[x].push_back(en.e);
+          }
+        }
+      }
+      // workgroup i runs on XCD i % kXcds; an XCD whose list ran out is
+      // topped up from the one with the most entries left
+      size_t total = 0;
+      for (const auto& l : lists) total += l.size();
+      std::vector<size_t> head(kXcds, 0);
+      for (size_t slot = 0; P.mix_table.size() < total; ++slot) {
+        int x = (int)(slot % kXcds);
+        if (head[x] == lists[x].size()) {
+          size_t best = 0;
+          for (int y = 0; y < kXcds; ++y)
+            if (lists[y].size() - head[y] > best) best = lists[y].size() - head[y], x = y;
+        }
+        P.mix_table.push_back(lists[x][head[x]++]);
+      }
+    }
+  }
+
   for (const pmattn_merge_row& mr : P.merge_rows) P.merge_max_parts = std::max(P.merge_max_parts, mr.nparts);
 
   // ---- workspace layout and the upload image --------------------------------
@@ -739,7 +855,9 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.off_vrow = align_up(P.off_rec_index + P.rec_index.size() * sizeof(int32_t), kAlign);
   P.off_slot = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
   P.off_istream = align_up(P.off_slot + P.slot_begin.size() * sizeof(int32_t), kAlign);
-  P.off_upload_end = align_up(P.off_istream + P.item_stream.size() * sizeof(int32_t), kAlign);
+  P.off_mix_table = align_up(P.off_istream + P.item_stream.size() * sizeof(int32_t), kAlign);
+  P.off_mix_bundles = align_up(P.off_mix_table + P.mix_table.size() * sizeof(int32_t), kAlign);
+  P.off_upload_end = align_up(P.off_mix_bundles + P.mix_bundles.size() * sizeof(int32_t), kAlign);
   P.off_part_o = P.off_upload_end;
   P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
   P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
@@ -764,6 +882,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     std::memcpy(P.upload_blob.data() + P.off_slot, P.slot_begin.data(), P.slot_begin.size() * sizeof(int32_t));
   if (!P.item_stream.empty())
     std::memcpy(P.upload_blob.data() + P.off_istream, P.item_stream.data(), P.item_stream.size() * sizeof(int32_t));
+  if (!P.mix_table.empty())
+    std::memcpy(P.upload_blob.data() + P.off_mix_table, P.mix_table.data(), P.mix_table.size() * sizeof(int32_t));
+  if (!P.mix_bundles.empty())
+    std::memcpy(P.upload_blob.data() + P.off_mix_bundles, P.mix_bundles.data(),
+                P.mix_bundles.size() * sizeof(int32_t));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -842,6 +965,11 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->slot_begin = P.slot_begin.empty() ? nullptr : P.slot_begin.data();
   t->class_stream = P.class_stream.data();
   t->item_stream = P.item_stream.data();
+  t->mixed_kernel = P.mixed ? 1 : 0;
+  t->num_mix_entries = (int32_t)P.mix_table.size();
+  t->mix_table = P.mix_table.data();
+  t->num_mix_bundles = (int32_t)(P.mix_bundles.size() / kWaveTasksPerWg);
+  t->mix_bundles = P.mix_bundles.data();
   return PMATTN_OK;
 }
 

@@ -54,6 +54,13 @@ struct Plan {
   std::vector<int32_t> slot_begin;
   int32_t slot_class = -1;  // the class slot_begin belongs to
   int32_t num_records = 0;
+  // Mixed-batch kernel (bf16 plans without token trees holding both 16-row
+  // wave tasks and larger tasks): one workgroup per table entry, either one
+  // workgroup task (entry 4 * item + 2 * cascade) or a bundle of four wave
+  // tasks, one per wave (entry 4 * bundle + 1; bundle slots item * 2 +
+  // cascade, or -1 for none).
+  bool mixed = false;
+  std::vector<int32_t> mix_table, mix_bundles;
   // tree masks, one per row, present only when some sequence is a tree
   std::vector<uint64_t> row_mask;
   // cascade (shared-prefix) virtual sequences, their rows, and the record
@@ -66,10 +73,11 @@ struct Plan {
   std::string append_conflict;
   // workspace layout (bytes): [items | merge rows | row masks | append units |
   // record index | virtual row sources | wave slots | task stream flags |
-  // partial O | partial lse]; everything before the partials is uploaded
+  // mixed table | mixed bundles | partial O | partial lse]; everything before
+  // the partials is uploaded
   size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_rec_index = 0,
-         off_vrow = 0, off_slot = 0, off_istream = 0, off_upload_end = 0, off_part_o = 0,
-         off_part_lse = 0, ws_bytes = 0;
+         off_vrow = 0, off_slot = 0, off_istream = 0, off_mix_table = 0, off_mix_bundles = 0,
+         off_upload_end = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
   std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
 };
 

@@ -511,3 +511,69 @@ def test_streaming_classes_random_batches(seed):
             tasks, want = R.streaming_tasks(t["items"], t["class_begin"], t["class_cascade"], bb.block_table)
             assert t["item_stream"].tolist() == tasks.tolist()
             assert t["class_stream"].tolist() == want.tolist()
+
+
+def _check_mixed_table(t):
+    """The mixed-batch table runs every item exactly once: workgroup entries
+    name items of classes above 16 rows, bundle slots items of 16-row classes,
+    and each entry's cascade bit matches its item's class."""
+    n = t["items"].shape[0]
+    cls_of = np.zeros(n, np.int64)
+    casc_of = np.zeros(n, np.int64)
+    for c in range(len(t["class_rows"])):
+        cls_of[t["class_begin"][c]:t["class_begin"][c + 1]] = t["class_rows"][c]
+        casc_of[t["class_begin"][c]:t["class_begin"][c + 1]] = t["class_cascade"][c]
+    seen = np.zeros(n, np.int64)
+    bundles = t["mix_bundles"].reshape(-1, 4)
+    used_bundles = np.zeros(bundles.shape[0], np.int64)
+    for e in t["mix_table"]:
+        if e & 1:
+            used_bundles[e >> 2] += 1
+            for s in bundles[e >> 2]:
+                if s < 0:
+                    continue
+                seen[s >> 1] += 1
+                assert cls_of[s >> 1] == 16 and casc_of[s >> 1] == (s & 1)
+        else:
+            i = e >> 2
+            seen[i] += 1
+            assert cls_of[i] > 16 and casc_of[i] == ((e >> 1) & 1)
+    assert (seen == 1).all() and (used_bundles == 1).all()
+
+
+@pytest.mark.parametrize("cfg,cascade", [(4, 0), (4, 1), (4, 2), (7, 1), (7, 2)])
+def test_mixed_table_covers_every_item_once(cfg, cascade):
+    """Configs 4 (prefill, verify and decode rows) and 7 (decode rows whose
+    shared prompt the cascade turns into workgroup tasks)."""
+    b = wl.config(cfg, values=False)
+    t = make_plan(b, cascade=cascade).tables()
+    assert t["mixed_kernel"] == 1
+    _check_mixed_table(t)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mixed_table_random_batches(seed):
+    rng = np.random.Generator(np.random.PCG64(400 + seed))
+    specs = []
+    for _ in range(int(rng.integers(2, 9))):
+        n = int(rng.integers(1, 900))
+        ql = int(rng.choice([1, 1, 3, 5, 40, 150]))
+        ql = min(ql, n)
+        specs.append(dict(q_len=ql, seq_len=n, q_start=n - ql))
+    specs.append(dict(q_len=1, seq_len=int(rng.integers(1, 500))))
+    specs.append(dict(q_len=70, seq_len=300, q_start=230))
+    b = wl.custom(specs, hq=8, hkv=int(rng.choice([1, 2, 8])), d=128, seed=seed, values=False,
+                  num_kv_splits=int(rng.choice([0, 0, 3])))
+    t = make_plan(b, cascade=int(rng.integers(0, 3)), work_shuffle_seed=int(rng.integers(0, 3))).tables()
+    assert t["mixed_kernel"] == 1
+    _check_mixed_table(t)
+    for dt, tree in (("f32", None), ("bf16", "tree")):
+        bb = b.replace(dtype=dt) if dt == "f32" else b
+        kw = {}
+        if tree:
+            # stars of at most 64 rows, chains beyond (still a tree plan)
+            kw["tree_parent"] = np.concatenate([[-1] + [0] * (q - 1) if q <= 64 else list(range(-1, q - 1))
+                                                for q in b.q_len]).astype(np.int32)
+        tt = make_plan(bb, **kw).tables()
+        if dt == "f32" or tt["row_tree_mask"] is not None:   # fp32, or a real token tree
+            assert tt["mixed_kernel"] == 0
