@@ -5,10 +5,11 @@
 // masks serves the three kinds of rows).
 //
 // Workgroup i (4 waves) runs entry i of the plan's mixed table:
-// * a workgroup task (more than 16 rows: prefill tiles, verify drafts): the
-//   four waves share each K/V chunk through LDS (task_wg.h);
-// * or a bundle of four 16-row wave tasks (decode): each wave streams its own
-//   task's K/V into registers (task_wave.h).
+// * a workgroup task (more than 32 rows: prefill tiles): the four waves share
+//   each K/V chunk through LDS (task_wg.h);
+// * or a bundle of four wave tasks of up to 32 rows (decode rows, verify
+//   drafts): each wave streams its own task's K/V into registers
+//   (task_wave.h; 32-row tasks in 16-key chunks to fit the registers).
 // Both bodies fit the same budget, 168 registers and 37 KiB of LDS, so three
 // workgroups of either kind share a CU. The planner interleaves the two kinds
 // in cost proportion within each XCD's share of the table; the dispatcher
@@ -41,8 +42,16 @@ void attn_mixed_kernel(MixedArgs m) {
   const int idx = e >> 1, lane = threadIdx.x & 63;
   const pmattn_work_item it = load_item(a.items, idx);
   const int32_t* qr = (e & 1) ? a.q_row : nullptr;
-  if (((cint_p)a.item_stream)[idx]) run_task<D, 1, false, true, true>(a, it, qr, lane);
-  else run_task<D, 1, false, true, false>(a, it, qr, lane);
+  const bool stream = ((cint_p)a.item_stream)[idx];
+  if (it.n_tok * a.group <= 16) {
+    if (stream) run_task<D, 1, false, true, true>(a, it, qr, lane);
+    else run_task<D, 1, false, true, false>(a, it, qr, lane);
+  } else {
+    // 17..32 rows (verify drafts): two 16-row tiles against 16-key chunks,
+    // which keeps the wave within the kernel's 168 registers
+    if (stream) run_task<D, 2, false, true, true, 1>(a, it, qr, lane);
+    else run_task<D, 2, false, true, false, 1>(a, it, qr, lane);
+  }
 }
 
 }  // namespace

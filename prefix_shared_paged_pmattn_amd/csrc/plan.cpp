@@ -136,10 +136,13 @@ constexpr int kMaxAutoSplits = 64;
 // Mixed-batch kernel: estimated duration per KV block (1/100 us) of a tile
 // of more than 64 rows, of a smaller workgroup task and of a 16-row wave task,
 // measured per table entry on MI355X (mixed-chunk workload, one session:
-// 0.72, 0.98 and 1.45 us).
+// 0.72, 0.98 and 1.45 us)
 constexpr int64_t kMixTileBlockCost = 72;
 constexpr int64_t kMixSmallTaskBlockCost = 98;
 constexpr int64_t kMixWaveBlockCost = 145;
+// ... and of a 17..32-row wave task (16-key chunks: twice the round trips
+// per key of a 16-row task; measured 3.36 us)
+constexpr int64_t kMixWave32BlockCost = 336;
 // Shader engines per XCD, which receive an XCD's workgroups in turn.
 constexpr int kSeRoundRobin = 4;
 // Automatic cascade: a shared run becomes a group only with this many members
@@ -754,51 +757,49 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     bool has_wave = false, has_wg = false;
     for (int32_t rows : P.class_rows) (rows <= kClassRows[0] ? has_wave : has_wg) = true;
     P.mixed = d->dtype == PMATTN_BF16 && P.row_mask.empty() && has_wave && has_wg;
+    // (a plan of 16- and 32-row tasks only is mixed too: its 32-row tasks run
+    // as wave tasks beside the 16-row ones)
     if (P.mixed) {
       const int rep = d->num_kv_heads >= kXcds ? 1 : (kXcds + d->num_kv_heads - 1) / d->num_kv_heads;
       struct Entry {
         int64_t cost;
         int32_t e;
       };
-      std::vector<Entry> parts[2][kXcds];  // [0] workgroup tasks, [1] wave tasks
+      // streams: [0] workgroup tiles of more than 64 rows, [1] other workgroup
+      // tasks, [2] 16-row wave tasks, [3] 17..32-row wave tasks
+      std::vector<Entry> parts[4][kXcds];
       for (size_t c = 0; c + 1 < P.class_begin.size(); ++c) {
-        const int kind = P.class_rows[c] <= kClassRows[0] ? 1 : 0;
+        const int rows = P.class_rows[c];
+        const int k = rows <= kClassRows[0] ? 2 : rows <= kClassRows[1] ? 3 : rows > kMaxWaveRows ? 0 : 1;
         for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
           const pmattn_work_item& it = P.items[i];
           const int x = (d->num_kv_heads >= kXcds ? it.kv_head : it.kv_head * rep + it.seq % rep) % kXcds;
           const int64_t nblk = (it.kv_end - it.kv_begin + kBlock - 1) / kBlock;
-          // estimated duration (1/100 us) in this kernel: per KV block, a
-          // tile of more than 64 rows 72 (MFMA bound), a smaller workgroup
-          // task 98 (one chunk in flight per workgroup), a 16-row wave task
-          // 145 (one chunk in flight per wave; a bundle lasts as long as its
-          // longest task). Measured per entry on MI355X, mixed-chunk workload.
-          const int64_t cost = nblk * (kind ? kMixWaveBlockCost
-                                            : P.class_rows[c] > kMaxWaveRows ? kMixTileBlockCost
-                                                                             : kMixSmallTaskBlockCost);
-          parts[kind][x].push_back(Entry{cost, i * 2 + P.class_cascade[c]});
+          // estimated duration (1/100 us) in this kernel, per KV block: see
+          // kMix*BlockCost (a bundle lasts as long as its longest task)
+          static constexpr int64_t per_block[4] = {kMixTileBlockCost, kMixSmallTaskBlockCost, kMixWaveBlockCost,
+                                                   kMixWave32BlockCost};
+          parts[k][x].push_back(Entry{nblk * per_block[k], i * 2 + P.class_cascade[c]});
         }
       }
       std::vector<std::vector<int32_t>> lists(kXcds);
       for (int x = 0; x < kXcds; ++x) {
-        for (int k = 0; k < 2; ++k) {
+        std::vector<Entry> streams[4];
+        for (int k = 0; k < 4; ++k) {
           auto& v = parts[k][x];
           std::stable_sort(v.begin(), v.end(), [](const Entry& a, const Entry& b) { return a.cost > b.cost; });
           if (d->work_shuffle_seed)
             for (size_t i = v.size(); i > 1; --i) std::swap(v[i - 1], v[splitmix64(rng) % i]);
-        }
-        // table entries of this XCD in three streams: tiles of more than 64
-        // rows, smaller workgroup tasks, and bundles of four wave tasks
-        std::vector<Entry> streams[3];
-        for (const Entry& en : parts[0][x]) {
-          const int32_t item = en.e >> 1;
-          const bool big = (int64_t)P.items[item].n_tok * G > kMaxWaveRows;
-          streams[big ? 0 : 1].push_back(Entry{en.cost, 4 * item + 2 * (en.e & 1)});
-        }
-        const auto& wv = parts[1][x];
-        for (size_t i = 0; i < wv.size(); i += kWaveTasksPerWg) {
-          const int32_t b = (int32_t)(P.mix_bundles.size() / kWaveTasksPerWg);
-          for (size_t k = i; k < i + kWaveTasksPerWg; ++k) P.mix_bundles.push_back(k < wv.size() ? wv[k].e : -1);
-          streams[2].push_back(Entry{wv[i].cost, 4 * b + 1});  // the bundle's longest task
+          if (k < 2) {
+            for (const Entry& en : v) streams[k].push_back(Entry{en.cost, 4 * (en.e >> 1) + 2 * (en.e & 1)});
+            continue;
+          }
+          // bundles of four wave tasks of neighbouring cost
+          for (size_t i = 0; i < v.size(); i += kWaveTasksPerWg) {
+            const int32_t b = (int32_t)(P.mix_bundles.size() / kWaveTasksPerWg);
+            for (size_t j = i; j < i + kWaveTasksPerWg; ++j) P.mix_bundles.push_back(j < v.size() ? v[j].e : -1);
+            streams[k].push_back(Entry{v[i].cost, 4 * b + 1});  // the bundle's longest task
+          }
         }
         // Interleave in proportion to estimated duration (next comes the
         // stream that has used the smallest share of its own total), in
@@ -809,13 +810,13 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
         // puts one entry of the same kind on every engine: the engines free
         // their slots at the same pace (one full engine blocks dispatch to
         // the others) and each engine's CUs see every kind in turn.
-        int64_t tot[3] = {0, 0, 0}, used[3] = {0, 0, 0};
-        size_t h[3] = {0, 0, 0};
-        for (int k = 0; k < 3; ++k)
+        int64_t tot[4] = {0, 0, 0, 0}, used[4] = {0, 0, 0, 0};
+        size_t h[4] = {0, 0, 0, 0};
+        for (int k = 0; k < 4; ++k)
           for (const Entry& en : streams[k]) tot[k] += en.cost;
         for (;;) {
           int k = -1;
-          for (int j = 0; j < 3; ++j) {
+          for (int j = 0; j < 4; ++j) {
             if (h[j] == streams[j].size()) continue;
             if (k < 0 || (__int128)used[j] * tot[k] < (__int128)used[k] * tot[j]) k = j;
           }

@@ -48,17 +48,24 @@
 // blocks, so shared prefix blocks stay in the caches for their other readers).
 #pragma once
 
+#include <type_traits>
+
 #include "task_common.h"
 
 namespace pmattn {
 namespace {
 
-template <int D>
+// A chunk is NB blocks: 32 keys (NB = 2), or 16 (NB = 1: half the registers
+// in flight, for tasks whose other state fills the register budget).
+template <int D, int NB = 2>
 struct Chunk {
   static constexpr int KS = D / 32;   // QK k-steps of 32 channels
   static constexpr int DT = D / 16;   // 16-channel output tiles
-  bf16x8 k[2][KS];
-  bf16x8 v[DT];
+  bf16x8 k[NB][KS];
+  // V operand of output tile t: slots 4g..4g+3 of both blocks (NB = 2), or
+  // of the one block (NB = 1; the operand's upper half, the absent block, is
+  // zero)
+  typename std::conditional<NB == 2, bf16x8, u32x2>::type v[DT];
 };
 
 // Issue the loads of the 32-key chunk made of physical blocks blk0, blk1.
@@ -78,26 +85,38 @@ __device__ __forceinline__ T ld_kv(const uint16_t* p) {
   else return *reinterpret_cast<const T*>(p);
 }
 
-template <int D, bool STREAM>
-__device__ __forceinline__ void load_chunk(Chunk<D>& ch, const uint16_t* __restrict__ kpool,
+template <int D, bool STREAM, int NB>
+__device__ __forceinline__ void load_chunk(Chunk<D, NB>& ch, const uint16_t* __restrict__ kpool,
                                            const uint16_t* __restrict__ vpool, int blk0, int blk1,
                                            int kvh, int hkv, int i, int g) {
-  constexpr int KS = Chunk<D>::KS, DT = Chunk<D>::DT;
+  constexpr int KS = Chunk<D, NB>::KS, DT = Chunk<D, NB>::DT;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < NB; ++c) {
     const int64_t bk = c ? blk1 : blk0;
     const uint16_t* kp = kpool + ((bk * hkv + kvh) * (D / 8) + g) * 128 + 8 * i;
 #pragma unroll
     for (int s = 0; s < KS; ++s) ch.k[c][s] = __builtin_bit_cast(bf16x8, ld_kv<STREAM, u32x4>(kp + 512 * s));
   }
   const uint16_t* vp0 = vpool + (((int64_t)blk0 * hkv + kvh) * D + i) * 16 + 4 * g;
-  const uint16_t* vp1 = vpool + (((int64_t)blk1 * hkv + kvh) * D + i) * 16 + 4 * g;
+  if constexpr (NB == 1) {
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    const u32x2 x0 = ld_kv<STREAM, u32x2>(vp0 + 256 * t);
-    const u32x2 x1 = ld_kv<STREAM, u32x2>(vp1 + 256 * t);
-    ch.v[t] = __builtin_bit_cast(bf16x8, (u32x4){x0.x, x0.y, x1.x, x1.y});
+    for (int t = 0; t < DT; ++t) ch.v[t] = ld_kv<STREAM, u32x2>(vp0 + 256 * t);
+  } else {
+    const uint16_t* vp1 = vpool + (((int64_t)blk1 * hkv + kvh) * D + i) * 16 + 4 * g;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      const u32x2 x0 = ld_kv<STREAM, u32x2>(vp0 + 256 * t);
+      const u32x2 x1 = ld_kv<STREAM, u32x2>(vp1 + 256 * t);
+      ch.v[t] = __builtin_bit_cast(bf16x8, (u32x4){x0.x, x0.y, x1.x, x1.y});
+    }
   }
+}
+
+// The V operand of output tile t as the MFMA takes it.
+template <int D, int NB>
+__device__ __forceinline__ bf16x8 v_operand(const Chunk<D, NB>& ch, int t) {
+  if constexpr (NB == 1) return __builtin_bit_cast(bf16x8, (u32x4){ch.v[t].x, ch.v[t].y, 0u, 0u});
+  else return ch.v[t];
 }
 
 // Zero the V lanes of keys at or past the task's end (only the last, partial
@@ -107,21 +126,26 @@ __device__ __forceinline__ void load_chunk(Chunk<D>& ch, const uint16_t* __restr
 // Element e of a lane's V operand is key c0 + 4g + slot_off(e).
 __device__ __forceinline__ constexpr int slot_off(int e) { return 16 * (e >> 2) + (e & 3); }
 
-template <int D>
-__device__ __forceinline__ void zero_tail_v(Chunk<D>& ch, int c0, int kv_end, int g) {
+template <int D, int NB>
+__device__ __forceinline__ void zero_tail_v(Chunk<D, NB>& ch, int c0, int kv_end, int g) {
   const int nv = kv_end - (c0 + 4 * g);
   uint32_t keep[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w)
     keep[w] = (slot_off(2 * w + 1) < nv ? 0xFFFF0000u : 0u) | (slot_off(2 * w) < nv ? 0x0000FFFFu : 0u);
 #pragma unroll
-  for (int t = 0; t < Chunk<D>::DT; ++t) {
-    uint4 u = __builtin_bit_cast(uint4, ch.v[t]);
-    u.x &= keep[0];
-    u.y &= keep[1];
-    u.z &= keep[2];
-    u.w &= keep[3];
-    ch.v[t] = __builtin_bit_cast(bf16x8, u);
+  for (int t = 0; t < Chunk<D, NB>::DT; ++t) {
+    if constexpr (NB == 1) {
+      ch.v[t].x &= keep[0];
+      ch.v[t].y &= keep[1];
+    } else {
+      uint4 u = __builtin_bit_cast(uint4, ch.v[t]);
+      u.x &= keep[0];
+      u.y &= keep[1];
+      u.z &= keep[2];
+      u.w &= keep[3];
+      ch.v[t] = __builtin_bit_cast(bf16x8, u);
+    }
   }
 }
 
@@ -138,31 +162,31 @@ struct TreeRows {
   int tree_from;
 };
 
-template <int D, int NT, bool TREE>
-__device__ __forceinline__ void wave_chunk(const Chunk<D>& ch, const bf16x8 (&qop)[NT][D / 32],
+template <int D, int NT, bool TREE, int NB>
+__device__ __forceinline__ void wave_chunk(const Chunk<D, NB>& ch, const bf16x8 (&qop)[NT][D / 32],
                                               f32x4 (&o)[NT][D / 16], float (&m_run)[NT],
                                               float (&l_run)[NT], const int (&lim_base)[NT], int c0,
                                               float sl2, int g, const TreeRows<NT>& tr) {
-  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int KS = D / 32, DT = D / 16, NS = 4 * NB;  // scores per lane
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[0][s], qop[n][s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[1][s], qop[n][s], s1, 0, 0, 0);
+      if constexpr (NB == 2) s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.k[1][s], qop[n][s], s1, 0, 0, 0);
     }
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     // score j holds key c0 + 4g + slot_off(j) (tile j/4, accumulator row
     // 4g + j%4); visible iff key < min(pos + 1, kv_end)
     const int lim = lim_base[n] - c0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sv[j] = (slot_off(j) < lim) ? sv[j] : kNegInf;
+    for (int j = 0; j < NS; ++j) sv[j] = (slot_off(j) < lim) ? sv[j] : kNegInf;
     if constexpr (TREE) {
       if (c0 > tr.tree_from) {
         const int db = tr.dbase[n] - c0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NS; ++j) {
           const int dd = db - slot_off(j);  // how far before the row's position
           const bool hide = (unsigned)dd < 64u && !((tr.rel[n] >> dd) & 1ull);
           sv[j] = hide ? kNegInf : sv[j];
@@ -171,17 +195,17 @@ __device__ __forceinline__ void wave_chunk(const Chunk<D>& ch, const bf16x8 (&qo
     }
     float mx = sv[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+    for (int j = 1; j < NS; ++j) mx = fmaxf(mx, sv[j]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run[n], mx);
     const float ms = (m_new == kNegInf) ? 0.f : m_new * sl2;
     const float alpha = __builtin_amdgcn_exp2f(m_run[n] * sl2 - ms);
     m_run[n] = m_new;
-    f32x8 p;
+    f32x8 p = {};
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NS; ++j) {
       p[j] = __builtin_amdgcn_exp2f(sv[j] * sl2 - ms);
       psum += p[j];
     }
@@ -190,7 +214,7 @@ __device__ __forceinline__ void wave_chunk(const Chunk<D>& ch, const bf16x8 (&qo
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       o[n][t] *= alpha;
-      o[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ch.v[t], pb, o[n][t], 0, 0, 0);
+      o[n][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_operand(ch, t), pb, o[n][t], 0, 0, 0);
     }
   }
 }
@@ -217,9 +241,10 @@ struct Depth {
 
 // One task on one wave. q_row: null, or the table naming each of the task's
 // rows' query row (virtual rows of cascade tasks).
-template <int D, int NT, bool TREE, bool CONC, bool STREAM>
+template <int D, int NT, bool TREE, bool CONC, bool STREAM, int NB = 2>
 __device__ __forceinline__ void run_task(const AttnArgs& a, const pmattn_work_item& it, const int32_t* q_row,
                                          int lane) {
+  static_assert(NB == 2 || Depth<NT, CONC>::value == 1, "16-key chunks run one buffer deep");
   constexpr int KS = D / 32, DT = D / 16;
   const int i = lane & 15, g = lane >> 4;
   const int G = a.group, hq = a.hq, hkv = a.hkv, kvh = it.kv_head;
@@ -266,7 +291,7 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, const pmattn_work_it
   auto chunk_ids = [&](int c, int& b0, int& b1) {
     const int bi = c >> 4;
     b0 = bt_row[min(bi, last_blk)];
-    b1 = bt_row[min(bi + 1, last_blk)];
+    b1 = NB == 2 ? bt_row[min(bi + 1, last_blk)] : b0;
   };
 
   const float sl2 = a.scale_log2;
@@ -288,16 +313,17 @@ __device__ __forceinline__ void run_task(const AttnArgs& a, const pmattn_work_it
   }
   if constexpr (Depth<NT, CONC>::value == 1) {
     // One buffer per wave; latency is hidden by the other waves on the SIMD.
-    const int nch = (kv_end - it.kv_begin + 31) >> 5;
-    Chunk<D> A;
+    constexpr int CK = 16 * NB;  // keys per chunk
+    const int nch = (kv_end - it.kv_begin + CK - 1) / CK;
+    Chunk<D, NB> A;
     int c0 = it.kv_begin, b0, b1;
     chunk_ids(c0, b0, b1);
     for (int k = 0; k < nch; ++k) {
       load_chunk<D, STREAM>(A, kpool, vpool, b0, b1, kvh, hkv, i, g);
-      chunk_ids(c0 + 32, b0, b1);
+      chunk_ids(c0 + CK, b0, b1);
       zero_tail_v<D>(A, c0, kv_end, g);
       wave_chunk<D, NT, TREE>(A, qop, o, m_run, l_run, lim_base, c0, sl2, g, tr);
-      c0 += 32;
+      c0 += CK;
     }
   } else {
     // Software pipeline over pairs of 32-key chunks with two register buffers:

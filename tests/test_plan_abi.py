@@ -515,8 +515,9 @@ def test_streaming_classes_random_batches(seed):
 
 def _check_mixed_table(t):
     """The mixed-batch table runs every item exactly once: workgroup entries
-    name items of classes above 16 rows, bundle slots items of 16-row classes,
-    and each entry's cascade bit matches its item's class."""
+    name items of classes above 32 rows, bundle slots items of 16- and 32-row
+    classes (a bundle holds one of the two), and each entry's cascade bit
+    matches its item's class."""
     n = t["items"].shape[0]
     cls_of = np.zeros(n, np.int64)
     casc_of = np.zeros(n, np.int64)
@@ -529,15 +530,18 @@ def _check_mixed_table(t):
     for e in t["mix_table"]:
         if e & 1:
             used_bundles[e >> 2] += 1
+            kinds = set()
             for s in bundles[e >> 2]:
                 if s < 0:
                     continue
                 seen[s >> 1] += 1
-                assert cls_of[s >> 1] == 16 and casc_of[s >> 1] == (s & 1)
+                kinds.add(int(cls_of[s >> 1]))
+                assert cls_of[s >> 1] <= 32 and casc_of[s >> 1] == (s & 1)
+            assert len(kinds) == 1
         else:
             i = e >> 2
             seen[i] += 1
-            assert cls_of[i] > 16 and casc_of[i] == ((e >> 1) & 1)
+            assert cls_of[i] > 32 and casc_of[i] == ((e >> 1) & 1)
     assert (seen == 1).all() and (used_bundles == 1).all()
 
 
