@@ -145,23 +145,23 @@ def plan(q_len, seq_len, q_start, block_table, *, num_pool_blocks: int, num_q_he
     b = int(ql.shape[0])
     if sl.shape != (b,) or qs.shape != (b,) or bt.shape[0] != b:
         raise ValueError("q_len, seq_len, q_start and block_table disagree on num_seqs")
-    i32p = lambda a: a.ctypes.data_as(L._i32p)  # noqa: E731
+    rows = int(ql.sum())
     tp = None
     if tree_parent is not None:
         tp = _i32(tree_parent)
-        if tp.shape != (int(ql.sum()),):
+        if tp.shape != (rows,):
             raise ValueError("tree_parent needs one entry per query row")
-    d = L.PlanDesc(num_seqs=b, q_len=i32p(ql), seq_len=i32p(sl), q_start=i32p(qs),
-                   block_table=i32p(bt), bt_stride=int(bt.shape[1]),
+    d = L.PlanDesc(num_seqs=b, q_len=ql.ctypes.data, seq_len=sl.ctypes.data, q_start=qs.ctypes.data,
+                   block_table=bt.ctypes.data, bt_stride=int(bt.shape[1]),
                    num_pool_blocks=int(num_pool_blocks), block_size=16,
                    num_q_heads=int(num_q_heads), num_kv_heads=int(num_kv_heads),
                    head_dim=int(head_dim), dtype=_dtype_code(dtype), scale=float(scale),
                    num_kv_splits=int(num_kv_splits), num_cus=int(num_cus),
                    work_shuffle_seed=int(work_shuffle_seed),
-                   tree_parent=i32p(tp) if tp is not None else None, cascade=int(cascade))
+                   tree_parent=tp.ctypes.data if tp is not None else None, cascade=int(cascade))
     h = ctypes.c_void_p()
     _check(L.load().pmattn_plan(ctypes.byref(d), ctypes.byref(h)))
-    shape = dict(num_seqs=b, num_rows=int(ql.sum()), bt_stride=int(bt.shape[1]),
+    shape = dict(num_seqs=b, num_rows=rows, bt_stride=int(bt.shape[1]),
                  num_pool_blocks=int(num_pool_blocks), hq=int(num_q_heads), hkv=int(num_kv_heads),
                  d=int(head_dim), dtype=_dtype_code(dtype))
     return Plan(h, shape)

@@ -14,12 +14,13 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 
 
 class PlanDesc(ctypes.Structure):
+    # host int32 arrays, passed as addresses (const int32_t* in the C header)
     _fields_ = [
         ("num_seqs", ctypes.c_int32),
-        ("q_len", _i32p),
-        ("seq_len", _i32p),
-        ("q_start", _i32p),
-        ("block_table", _i32p),
+        ("q_len", ctypes.c_void_p),
+        ("seq_len", ctypes.c_void_p),
+        ("q_start", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
         ("bt_stride", ctypes.c_int32),
         ("num_pool_blocks", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
@@ -31,7 +32,7 @@ class PlanDesc(ctypes.Structure):
         ("num_kv_splits", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("work_shuffle_seed", ctypes.c_uint64),
-        ("tree_parent", _i32p),
+        ("tree_parent", ctypes.c_void_p),
         ("cascade", ctypes.c_int32),
     ]
 

@@ -37,9 +37,8 @@ pmattn_status hip_fail(hipError_t e, const char* what) {
 }
 
 pmattn_status upload(const Plan& P, void* ws, hipStream_t st) {
-  if (!P.upload_blob.empty()) {
-    hipError_t e = hipMemcpyAsync(ws, P.upload_blob.data(), P.upload_blob.size(),
-                                  hipMemcpyHostToDevice, st);
+  if (P.off_upload_end > 0) {
+    hipError_t e = hipMemcpyAsync(ws, P.blob.get(), P.off_upload_end, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
   }
   return PMATTN_OK;

@@ -11,8 +11,14 @@
 // merged by log-sum-exp afterwards.
 //
 // Pure host code: no HIP call, so every rule here is testable on a CPU.
+//
+// The planner runs once per batch on the host, so it is written to stay in
+// the tens of microseconds for batches of ten thousand tasks: every ordering
+// is a counting sort over small integer keys, the block table is walked once
+// per row, the tables are written straight into the upload image, and the
+// working buffers belong to the calling thread and are reused by its next
+// plan (for the per-block marks, 16 bytes per pool block).
 #include <algorithm>
-#include <map>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -26,80 +32,6 @@ namespace pmattn {
 namespace {
 thread_local std::string g_last_error;
 std::atomic<uint64_t> g_next_plan_id{1};
-
-// XCD-aware dispatch order. K/V of (block, kv head) is read only by tasks of
-// that kv head, so all tasks of one kv head go to one XCD (kv heads spread
-// over several XCDs when there are fewer than kXcds, by sequence): every task
-// that reads a shared block finds it in the same L2. Each XCD keeps its tasks
-// in the given (cost-descending) order; workgroup slot i, which the hardware
-// gives to XCD i % kXcds, takes the next `per_wg` tasks of that XCD, topped up
-// from the XCD with the most tasks left once that one runs out (so that every
-// slot but the last holds exactly per_wg tasks).
-std::vector<size_t> xcd_order(const std::vector<pmattn_work_item>& v, const std::vector<size_t>& order,
-                              int per_wg, int hkv) {
-  const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;  // XCDs per kv head
-  std::vector<std::vector<size_t>> q(kXcds);
-  for (size_t i : order) {
-    const pmattn_work_item& it = v[i];
-    const int x = (hkv >= kXcds ? it.kv_head : it.kv_head * rep + it.seq % rep) % kXcds;
-    q[x].push_back(i);
-  }
-  std::vector<size_t> head(kXcds, 0), out;
-  out.reserve(order.size());
-  for (size_t slot = 0; out.size() < order.size(); ++slot) {
-    int x = (int)(slot % kXcds);
-    for (int k = 0; k < per_wg && out.size() < order.size(); ++k) {
-      if (head[x] == q[x].size()) {
-        size_t best = 0;
-        for (int y = 0; y < kXcds; ++y)
-          if (q[y].size() - head[y] > best) best = q[y].size() - head[y], x = y;
-      }
-      out.push_back(q[x][head[x]++]);
-    }
-  }
-  return out;
-}
-
-// Dispatch order of an equal-work decode plan. Slot (g, j) is the run of tasks
-// of kv head g inside piece j, in unit order (each unit's partition p lies in
-// piece start_u / len + p). Slots go to XCDs like tasks in xcd_order (kv head
-// g on XCD g; with fewer than kXcds heads, piece j of head g on XCD
-// g * rep + j % rep), four slots per workgroup, topped up from the XCD with
-// the most slots left. Returns the task order and fills slot_begin.
-std::vector<size_t> stream_order(const std::vector<pmattn_work_item>& v, const std::vector<int64_t>& start,
-                                 const std::vector<int64_t>& lo, int64_t len, int64_t pieces, int hkv,
-                                 std::vector<int32_t>& slot_begin) {
-  const int64_t nslot = (int64_t)hkv * pieces;
-  std::vector<std::vector<size_t>> slot(nslot);
-  for (size_t i = 0; i < v.size(); ++i) {
-    const pmattn_work_item& it = v[i];
-    // partitions of a stream plan start at piece boundaries or at the unit's
-    // first key, so the first block tells the piece
-    const int64_t j = (start[it.seq] + (it.kv_begin - lo[it.seq]) / kBlock) / len;
-    slot[(int64_t)it.kv_head * pieces + j].push_back(i);
-  }
-  const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;
-  std::vector<std::vector<int64_t>> q(kXcds);
-  for (int g = 0; g < hkv; ++g)
-    for (int64_t j = 0; j < pieces; ++j)
-      q[(hkv >= kXcds ? g : g * rep + (int)(j % rep)) % kXcds].push_back((int64_t)g * pieces + j);
-  std::vector<size_t> head(kXcds, 0), out;
-  out.reserve(v.size());
-  slot_begin.assign(1, 0);
-  for (int64_t taken = 0, wg = 0; taken < nslot; ++wg) {
-    int x = (int)(wg % kXcds);
-    for (int k = 0; k < kWaveTasksPerWg && taken < nslot; ++k, ++taken) {
-      if (head[x] == q[x].size()) {
-        size_t best = 0;
-        for (int y = 0; y < kXcds; ++y)
-          if (q[y].size() - head[y] > best) best = q[y].size() - head[y], x = y;
-      }
-      for (size_t i : slot[q[x][head[x]++]]) out.push_back(i);
-      slot_begin.push_back((int32_t)out.size());
-    }
-  }
-  return out;
-}
 
 // Cost model for ordering and automatic splitting, in "block units": a task
 // over n KV blocks costs n * (2 + rows/16). The constant 2 stands for the
@@ -158,6 +90,7 @@ constexpr int kCascadeAutoBlocks = 64;
 // decode batch spares 92%.
 constexpr int64_t kCascadeAutoSaveDiv = 4;
 
+
 int class_of_rows(int rows) {
   for (int c = 0; c < kNumClasses; ++c)
     if (rows <= kClassRows[c]) return c;
@@ -171,11 +104,151 @@ uint64_t splitmix64(uint64_t& s) {
   return z ^ (z >> 31);
 }
 
+// Shuffles idx[0, n) in place (the work_shuffle_seed option).
+template <typename T>
+void shuffle(T* idx, size_t n, uint64_t& rng) {
+  for (size_t i = n; i > 1; --i) std::swap(idx[i - 1], idx[splitmix64(rng) % i]);
+}
+
+// XCD of a task. K/V of (block, kv head) is read only by tasks of that kv
+// head, so all tasks of one kv head go to one XCD (kv heads spread over
+// several XCDs when there are fewer than kXcds, by sequence): every task that
+// reads a shared block finds it in the same L2.
+inline int xcd_of(int kv_head, int seq, int hkv) {
+  const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;  // XCDs per kv head
+  return (hkv >= kXcds ? kv_head : kv_head * rep + seq % rep) % kXcds;
+}
+
+// Stable counting sort: out[0, n) = the indices 0..n-1 ordered by key
+// ascending (keys in [0, nkeys)), equal keys in index order.
+void counting_order(const uint32_t* key, uint32_t n, size_t nkeys, std::vector<uint32_t>& cnt, uint32_t* out) {
+  cnt.assign(nkeys + 1, 0);
+  for (uint32_t i = 0; i < n; ++i) ++cnt[key[i] + 1];
+  for (size_t k = 0; k < nkeys; ++k) cnt[k + 1] += cnt[k];
+  for (uint32_t i = 0; i < n; ++i) out[cnt[key[i]]++] = i;
+}
+
+// Deals the entries of kXcds queues (queue x: entries [beg[x], end[x]) of a
+// common array) to workgroup slots: slot i, which the hardware gives to XCD
+// i % kXcds, takes the next `per_wg` entries of that XCD's queue, topped up
+// from the queue with the most entries left once that one runs out (so that
+// every slot but the last holds exactly per_wg entries). emit(e) receives
+// each entry's index in the common array, in dispatch order.
+template <typename Emit>
+void deal(const size_t* beg, const size_t* end, int per_wg, Emit&& emit) {
+  size_t head[kXcds], total = 0, done = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    head[x] = beg[x];
+    total += end[x] - beg[x];
+  }
+  for (size_t slot = 0; done < total; ++slot) {
+    int x = (int)(slot % kXcds);
+    for (int k = 0; k < per_wg && done < total; ++k, ++done) {
+      if (head[x] == end[x]) {
+        size_t best = 0;
+        for (int y = 0; y < kXcds; ++y)
+          if (end[y] - head[y] > best) best = end[y] - head[y], x = y;
+      }
+      emit(head[x]++);
+    }
+  }
+}
+
 struct Tile {
   int32_t seq;  // unit: a real sequence (< B) or a virtual cascade sequence
   int32_t tok_begin, n_tok, cls;
   int32_t kv_end;  // one past the tile's last visible key
+  int32_t range0;  // its first KV range (ranges [range0, range0 + k))
+  int32_t k;       // its non-empty KV partitions
+  int64_t rec0;    // its first partial record (kv head g: rec0 + g * k * rows), or -1
+  int32_t row, row0, pos0;  // its block-table row, first query row (real or virtual), first position
 };
+
+// One KV partition of one tile, clipped to the tile's keys: the tasks of the
+// tile's kv heads over these keys.
+struct Range {
+  int32_t tile, lo, hi, nblk;  // nblk: blocks' worth of keys, ceil((hi - lo) / 16)
+};
+
+// A task of a class before ordering: a range, a kv head and its XCD.
+struct Cand {
+  uint32_t range;
+  uint16_t g, x;
+};
+
+// Per pool block, valid while gen is the current plan's: the one row tile
+// reading it (or kMulti) and the range it reads it through, and the one
+// sequence that sees it (or kMulti).
+constexpr int32_t kMulti = -2;
+struct Mark {
+  uint32_t gen;
+  int32_t reader, seq, range;
+};
+
+// A range's first block (start) or one past its last, along its table row.
+struct Event {
+  int32_t pos;
+  uint32_t range;
+  int32_t start;
+  bool operator<(const Event& o) const { return pos != o.pos ? pos < o.pos : start < o.start; }
+};
+
+struct Target {
+  int32_t blk, seq;
+  uint32_t slots;  // bit o: slot o is written
+};
+
+struct VSeq {
+  int32_t lo, hi, table_seq, row_begin, rows;
+};
+
+// A mixed-table stream entry: its estimated duration and table code.
+struct MixEntry {
+  int64_t cost;
+  int32_t e;
+};
+
+struct Listed {
+  int64_t rec_base;
+  int32_t parts, trows, row0, g;
+  bool virt;
+};
+
+// Working buffers of one planning thread, reused by its next plan.
+struct Scratch {
+  std::vector<int32_t> row_off, own_lo, usplits, uoff, ubeg, uend, member_slot, vrow, cands;
+  std::vector<int64_t> stream_start;
+  std::vector<char> member, sunit;
+  std::vector<VSeq> vseqs;
+  std::vector<std::vector<int32_t>> members;
+  std::vector<Tile> tiles;
+  std::vector<Range> ranges;
+  std::vector<Target> targets;
+  std::vector<pmattn_append_unit> units;
+  std::vector<uint64_t> row_mask, anc;
+  std::vector<Listed> listed;
+  std::vector<uint32_t> key, order, cnt, row_list, tile_first, tile_list;
+  std::vector<Cand> cand;
+  std::vector<int32_t> qitem;
+  std::vector<char> rstream;
+  std::vector<int32_t> rec_start, rec_fill, slot_first;
+  std::vector<uint64_t> pairs;
+  std::vector<int32_t> mix_cat, mix_code;
+  std::vector<MixEntry> mix_streams[4];
+  std::vector<uint32_t> slot_key, slot_order;
+  std::vector<int64_t> last_cost;
+  std::vector<int32_t> unit_kind;
+  std::vector<Event> events;
+  std::vector<uint32_t> active;
+  std::vector<Mark> marks;
+  std::vector<uint32_t> tstamp;  // per pool block: the last plan that appends to it
+  uint32_t gen = 0;
+};
+thread_local Scratch g_scratch;
+// The calling thread's buffers, as a plain pointer: taken once per plan, so
+// that the compiler does not recompute the thread-local address at every use.
+__attribute__((noinline)) Scratch* thread_scratch() { return &g_scratch; }
+
 }  // namespace
 
 pmattn_status fail(pmattn_status st, const std::string& msg) {
@@ -183,6 +256,38 @@ pmattn_status fail(pmattn_status st, const std::string& msg) {
   return st;
 }
 void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+// The exact copy-on-write check: two rows writing one pool slot, or a written
+// slot that another sequence can see. Run only when the per-block marks of
+// the plan's row walk cannot rule a conflict out (a block written by one
+// sequence and seen, or also written, by another).
+std::string exact_append_check(const pmattn_plan_desc* d, std::vector<Target>& targets) {
+  std::sort(targets.begin(), targets.end(), [](const Target& a, const Target& b) { return a.blk < b.blk; });
+  for (size_t i = 1; i < targets.size(); ++i)
+    if (targets[i].blk == targets[i - 1].blk && (targets[i].slots & targets[i - 1].slots))
+      return "two query rows write the same pool slot (block " + std::to_string(targets[i].blk) + ")";
+  for (int s = 0; s < d->num_seqs && !targets.empty(); ++s) {
+    if (d->q_len[s] == 0) continue;
+    const int64_t kv = (int64_t)d->q_start[s] + d->q_len[s];
+    const int32_t* bt = d->block_table + (int64_t)s * d->bt_stride;
+    const int64_t nb = (kv + kBlock - 1) / kBlock;
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t blk = bt[j];
+      const uint32_t seen = j + 1 < nb ? 0xFFFFu : (1u << (kv - j * kBlock)) - 1u;
+      auto it = std::lower_bound(targets.begin(), targets.end(), blk,
+                                 [](const Target& a, int32_t b) { return a.blk < b; });
+      for (; it != targets.end() && it->blk == blk; ++it)
+        if (it->seq != s && (it->slots & seen))
+          return "sequence " + std::to_string(s) + " can see pool slots that sequence " + std::to_string(it->seq) +
+                 " appends to (block " + std::to_string(blk) + "): copy the block first";
+    }
+  }
+  return std::string();
+}
+
+}  // namespace
 
 static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   if (!d) return fail(PMATTN_E_INVALID, "desc is NULL");
@@ -219,8 +324,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.head_dim = d->head_dim;
   P.dtype = d->dtype;
   P.scale = d->scale;
+  const int hkv = d->num_kv_heads;
+  Scratch& S = *thread_scratch();
+  auto bt_row = [&](int s) { return d->block_table + (int64_t)s * d->bt_stride; };
 
-  // ---- validate sequences, row tables -------------------------------------
+  // ---- validate sequences ---------------------------------------------------
   int64_t rows = 0;
   for (int s = 0; s < B; ++s) {
     const int64_t ql = d->q_len[s], sl = d->seq_len[s], qs = d->q_start[s];
@@ -233,125 +341,84 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     if (need_blocks > d->bt_stride)
       return fail(PMATTN_E_INVALID, "bt_stride < ceil(seq_len/16) at sequence " + std::to_string(s));
     const int64_t vis_blocks = (qs + ql + kBlock - 1) / kBlock;
-    const int32_t* row = d->block_table + (int64_t)s * d->bt_stride;
-    for (int64_t j = 0; j < vis_blocks; ++j)
-      if (row[j] < 0 || row[j] >= d->num_pool_blocks)
-        return fail(PMATTN_E_INVALID, "block id out of [0, num_pool_blocks) at sequence " +
-                                          std::to_string(s) + " block " + std::to_string(j));
+    const int32_t* row = bt_row(s);
+    int32_t bad = 0;  // (a branch-free pass the compiler vectorizes)
+    for (int64_t j = 0; j < vis_blocks; ++j) bad |= (row[j] < 0) | (row[j] >= d->num_pool_blocks);
+    if (bad)
+      for (int64_t j = 0; j < vis_blocks; ++j)
+        if (row[j] < 0 || row[j] >= d->num_pool_blocks)
+          return fail(PMATTN_E_INVALID, "block id out of [0, num_pool_blocks) at sequence " +
+                                            std::to_string(s) + " block " + std::to_string(j));
     rows += ql;
   }
   if (rows > INT32_MAX / std::max(1, d->num_q_heads))
     return fail(PMATTN_E_INVALID, "too many query rows");
   P.num_rows = (int32_t)rows;
-  P.row_seq.resize(rows);
-  P.row_pos.resize(rows);
-  {
-    int64_t r = 0;
-    for (int s = 0; s < B; ++s)
-      for (int t = 0; t < d->q_len[s]; ++t, ++r) {
-        P.row_seq[r] = s;
-        P.row_pos[r] = d->q_start[s] + t;
-      }
-  }
+  std::vector<int32_t>& row_off = S.row_off;
+  row_off.assign(B + 1, 0);
+  for (int s = 0; s < B; ++s) row_off[s + 1] = row_off[s] + d->q_len[s];
+  P.seq_row_off.assign(row_off.begin(), row_off.end());
+  P.seq_q_start.assign(d->q_start, d->q_start + B);
 
   // ---- speculative token trees: per-row visibility of the 64 keys before it --
   // Bit k of a row's mask stands for the key k positions back. Ancestors (and
   // the row itself) set their bits; keys below q_start are context and always
   // visible, so every bit past the row's own index is set too. Chains (parent
   // r - 1) give all ones, the causal rule.
+  bool tree = false;
+  S.row_mask.clear();
   if (d->tree_parent && rows > 0) {
-    bool any_tree = false;
-    int64_t r0 = 0;
     for (int s = 0; s < B; ++s) {
       const int ql = d->q_len[s];
+      const int32_t* par = d->tree_parent + row_off[s];
       bool chain = true;
       for (int r = 0; r < ql; ++r) {
-        const int32_t par = d->tree_parent[r0 + r];
-        if (par < -1 || par >= r)
+        if (par[r] < -1 || par[r] >= r)
           return fail(PMATTN_E_INVALID, "tree_parent must lie in [-1, row) at sequence " +
                                             std::to_string(s) + " row " + std::to_string(r));
-        chain = chain && par == r - 1;
+        chain = chain && par[r] == r - 1;
       }
       if (!chain && ql > kMaxTreeRows)
         return fail(PMATTN_E_UNSUPPORTED, "a token tree holds at most 64 rows (sequence " +
                                               std::to_string(s) + ")");
-      any_tree = any_tree || !chain;
-      r0 += ql;
+      tree = tree || !chain;
     }
-    if (any_tree) {
-      P.row_mask.assign(rows, ~0ull);
-      std::vector<uint64_t> anc;  // bit a: row a of the sequence is an ancestor-or-self
-      r0 = 0;
+    if (tree) {
+      S.row_mask.assign(rows, ~0ull);
+      std::vector<uint64_t>& anc = S.anc;  // bit a: row a of the sequence is an ancestor-or-self
       for (int s = 0; s < B; ++s) {
         const int ql = d->q_len[s];
+        const int32_t* par = d->tree_parent + row_off[s];
         bool chain = true;
-        for (int r = 0; r < ql; ++r) chain = chain && d->tree_parent[r0 + r] == r - 1;
-        if (!chain) {
-          anc.assign(ql, 0);
-          for (int r = 0; r < ql; ++r) {
-            const int32_t par = d->tree_parent[r0 + r];
-            anc[r] = (par < 0 ? 0ull : anc[par]) | (1ull << r);
-            uint64_t m = r < 63 ? ~0ull << (r + 1) : 0ull;
-            for (int a = 0; a <= r; ++a)
-              if (anc[r] >> a & 1ull) m |= 1ull << (r - a);
-            P.row_mask[r0 + r] = m;
-          }
+        for (int r = 0; r < ql; ++r) chain = chain && par[r] == r - 1;
+        if (chain) continue;
+        anc.assign(ql, 0);
+        for (int r = 0; r < ql; ++r) {
+          anc[r] = (par[r] < 0 ? 0ull : anc[par[r]]) | (1ull << r);
+          uint64_t m = r < 63 ? ~0ull << (r + 1) : 0ull;
+          for (int a = 0; a <= r; ++a)
+            if (anc[r] >> a & 1ull) m |= 1ull << (r - a);
+          S.row_mask[row_off[s] + r] = m;
         }
-        r0 += ql;
       }
     }
   }
 
-  // ---- KV append units and their copy-on-write check ------------------------
+  // ---- KV append units ------------------------------------------------------
   // A unit is the run of a sequence's new tokens that falls into one block.
-  // Every slot written must be visible to its own sequence alone.
-  {
-    struct Target {
-      int32_t blk, seq;
-      uint32_t slots;  // bit o: slot o is written
-    };
-    std::vector<Target> targets;
-    int64_t r0 = 0;
-    for (int s = 0; s < B; ++s) {
-      const int ql = d->q_len[s], qs = d->q_start[s];
-      const int32_t* bt = d->block_table + (int64_t)s * d->bt_stride;
-      for (int t = 0; t < ql;) {
-        const int pos = qs + t, j = pos / kBlock, o = pos % kBlock;
-        const int n = std::min(ql - t, kBlock - o);
-        P.append_units.push_back(pmattn_append_unit{s, (int32_t)(r0 + t), n, j, o});
-        targets.push_back(Target{bt[j], s, ((1u << n) - 1u) << o});
-        t += n;
-      }
-      r0 += ql;
-    }
-    std::sort(targets.begin(), targets.end(),
-              [](const Target& a, const Target& b) { return a.blk < b.blk; });
-    std::vector<uint64_t> filter(1024, 0);  // 65536-bit filter on the low id bits
-    for (const Target& x : targets) filter[(x.blk & 0xFFFF) >> 6] |= 1ull << (x.blk & 63);
-    for (size_t i = 1; i < targets.size() && P.append_conflict.empty(); ++i)
-      if (targets[i].blk == targets[i - 1].blk && (targets[i].slots & targets[i - 1].slots))
-        P.append_conflict = "two query rows write the same pool slot (block " +
-                            std::to_string(targets[i].blk) + ")";
-    for (int s = 0; s < B && P.append_conflict.empty() && !targets.empty(); ++s) {
-      const int64_t kv = (int64_t)d->q_start[s] + d->q_len[s];
-      if (d->q_len[s] == 0) continue;
-      const int32_t* bt = d->block_table + (int64_t)s * d->bt_stride;
-      const int64_t nb = (kv + kBlock - 1) / kBlock;
-      for (int64_t j = 0; j < nb; ++j) {
-        const int32_t blk = bt[j];
-        if (!(filter[(blk & 0xFFFF) >> 6] >> (blk & 63) & 1ull)) continue;
-        const uint32_t seen = j + 1 < nb ? 0xFFFFu : (1u << (kv - j * kBlock)) - 1u;
-        auto it = std::lower_bound(targets.begin(), targets.end(), blk,
-                                   [](const Target& a, int32_t b) { return a.blk < b; });
-        for (; it != targets.end() && it->blk == blk; ++it)
-          if (it->seq != s && (it->slots & seen)) {
-            P.append_conflict = "sequence " + std::to_string(s) + " can see pool slots that sequence " +
-                                std::to_string(it->seq) + " appends to (block " +
-                                std::to_string(blk) + "): copy the block first";
-            break;
-          }
-        if (!P.append_conflict.empty()) break;
-      }
+  // Every slot written must be visible to its own sequence alone: checked
+  // after the row walk below.
+  S.units.clear();
+  S.targets.clear();
+  for (int s = 0; s < B; ++s) {
+    const int ql = d->q_len[s], qs = d->q_start[s];
+    const int32_t* bt = bt_row(s);
+    for (int t = 0; t < ql;) {
+      const int pos = qs + t, j = pos / kBlock, o = pos % kBlock;
+      const int n = std::min(ql - t, kBlock - o);
+      S.units.push_back(pmattn_append_unit{s, row_off[s] + t, n, j, o});
+      S.targets.push_back(Target{bt[j], s, ((1u << n) - 1u) << o});
+      t += n;
     }
   }
 
@@ -362,18 +429,20 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // query row, becomes a virtual sequence: its rows are all members' rows, its
   // keys the run. The members then attend only to the keys after their
   // deepest run, and the log-sum-exp merge joins the parts.
-  std::vector<int32_t> row_off(B + 1, 0);
-  for (int s = 0; s < B; ++s) row_off[s + 1] = row_off[s] + d->q_len[s];
-  std::vector<int32_t> own_lo(B, 0);  // first key of each sequence's own range
-  std::vector<char> member(B, 0);
-  struct VSeq {
-    int32_t lo, hi, table_seq, row_begin, rows;
-  };
-  std::vector<VSeq> vseqs;
+  std::vector<int32_t>& own_lo = S.own_lo;  // first key of each sequence's own range
+  std::vector<char>& member = S.member;
+  std::vector<VSeq>& vseqs = S.vseqs;
+  std::vector<int32_t>& vrow = S.vrow;  // source row of each virtual row
+  own_lo.assign(B, 0);
+  member.assign(B, 0);
+  vseqs.clear();
+  vrow.clear();
+  size_t nvm = 0;  // member lists in use (S.members[0, nvm))
   if (d->cascade) {
     auto bt = [&](int s, int j) { return d->block_table[(int64_t)s * d->bt_stride + j]; };
     auto shareable = [&](int s) { return d->q_start[s] / kBlock; };  // blocks before the first row
-    std::vector<int32_t> cands;
+    std::vector<int32_t>& cands = S.cands;
+    cands.clear();
     for (int s = 0; s < B; ++s)
       if (d->q_len[s] > 0 && (int64_t)d->q_len[s] * G <= kMaxWaveRows && shareable(s) >= 1) cands.push_back(s);
     // automatic mode: only runs that enough sequences share over enough
@@ -387,58 +456,73 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       int32_t depth, cover_lo;
     };
     std::vector<Node> stack;
-    stack.push_back(Node{cands, 0, 0});
-    std::vector<std::vector<int32_t>> members;
+    if (cands.size() >= 2) stack.push_back(Node{cands, 0, 0});
     while (!stack.empty()) {
       Node node = std::move(stack.back());
       stack.pop_back();
       const int32_t depth = node.depth;
-      std::map<int32_t, std::vector<int32_t>> buckets;
-      for (int32_t m : node.mem)
-        if (shareable(m) > depth) buckets[bt(m, depth)].push_back(m);
+      // buckets: members by their block at `depth`, in ascending block id,
+      // each bucket in node order
+      std::vector<uint64_t>& pairs = S.pairs;
+      pairs.clear();
+      for (size_t i = 0; i < node.mem.size(); ++i)
+        if (shareable(node.mem[i]) > depth) pairs.push_back((uint64_t)(uint32_t)bt(node.mem[i], depth) << 32 | i);
+      std::sort(pairs.begin(), pairs.end());
       std::vector<Node> kids;
-      for (auto& kv : buckets) {
-        const std::vector<int32_t>& bm = kv.second;
-        if (bm.size() < 2) continue;
-        int32_t L = depth + 1;
-        for (;;) {
-          bool same = true;
-          for (int32_t m : bm) same = same && shareable(m) > L && bt(m, L) == bt(bm[0], L);
-          if (!same) break;
-          ++L;
+      for (size_t a = 0, e; a < pairs.size(); a = e) {
+        for (e = a + 1; e < pairs.size() && pairs[e] >> 32 == pairs[a] >> 32;) ++e;
+        if (e - a < 2) continue;
+        std::vector<int32_t> bm(e - a);
+        for (size_t i = a; i < e; ++i) bm[i - a] = node.mem[(uint32_t)pairs[i]];
+        // the run all members share from here: up to the first block that
+        // some member lacks or holds differently
+        int32_t L = INT32_MAX;
+        for (int32_t m : bm) L = std::min(L, shareable(m));
+        const int32_t* first = bt_row(bm[0]);
+        for (size_t i = 1; i < bm.size(); ++i) {
+          const int32_t* row = bt_row(bm[i]);
+          int32_t j = depth + 1;
+          while (j < L && row[j] == first[j]) ++j;
+          L = j;
         }
         int32_t cover = node.cover_lo;
         if ((int)bm.size() >= min_members && L - node.cover_lo >= min_blocks) {
           vseqs.push_back(VSeq{node.cover_lo * kBlock, L * kBlock, bm[0], 0, 0});
-          members.push_back(bm);
+          if (S.members.size() <= nvm) S.members.resize(nvm + 1);
+          S.members[nvm++] = bm;
           for (int32_t m : bm) {
             own_lo[m] = L * kBlock;
             member[m] = 1;
           }
           cover = L;
         }
-        kids.push_back(Node{bm, L, cover});
+        kids.push_back(Node{std::move(bm), L, cover});
       }
       for (auto it = kids.rbegin(); it != kids.rend(); ++it) stack.push_back(std::move(*it));
     }
     if (d->cascade == 2 && !vseqs.empty()) {
       int64_t spared = 0, logical = 0;
       for (size_t v = 0; v < vseqs.size(); ++v)
-        spared += (int64_t)(members[v].size() - 1) * (vseqs[v].hi - vseqs[v].lo);
+        spared += (int64_t)(S.members[v].size() - 1) * (vseqs[v].hi - vseqs[v].lo);
       for (int s = 0; s < B; ++s)
         if (d->q_len[s] > 0) logical += (int64_t)d->q_start[s] + d->q_len[s];
       if (spared * kCascadeAutoSaveDiv < logical) {
         vseqs.clear();
-        members.clear();
+        nvm = 0;
         std::fill(own_lo.begin(), own_lo.end(), 0);
         std::fill(member.begin(), member.end(), 0);
       }
     }
+    P.cascade_lo.clear();
+    P.cascade_hi.clear();
+    P.cascade_seq.clear();
+    P.cascade_row_begin.clear();
+    P.cascade_rows.clear();
     for (size_t v = 0; v < vseqs.size(); ++v) {
-      vseqs[v].row_begin = (int32_t)P.vrow_src.size();
-      for (int32_t m : members[v])
-        for (int32_t r = 0; r < d->q_len[m]; ++r) P.vrow_src.push_back(row_off[m] + r);
-      vseqs[v].rows = (int32_t)P.vrow_src.size() - vseqs[v].row_begin;
+      vseqs[v].row_begin = (int32_t)vrow.size();
+      for (int32_t m : S.members[v])
+        for (int32_t r = 0; r < d->q_len[m]; ++r) vrow.push_back(row_off[m] + r);
+      vseqs[v].rows = (int32_t)vrow.size() - vseqs[v].row_begin;
       P.cascade_lo.push_back(vseqs[v].lo);
       P.cascade_hi.push_back(vseqs[v].hi);
       P.cascade_seq.push_back(vseqs[v].table_seq);
@@ -451,28 +535,31 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   auto unit_rows = [&](int u) { return u < B ? d->q_len[u] : vseqs[u - B].rows; };
   auto unit_lo = [&](int u) { return u < B ? own_lo[u] : vseqs[u - B].lo; };
   auto unit_hi = [&](int u) { return u < B ? d->q_start[u] + d->q_len[u] : vseqs[u - B].hi; };
+  auto unit_row = [&](int u) { return u < B ? u : vseqs[u - B].table_seq; };  // its block-table row
 
   // ---- tiles: runs of query tokens whose G heads fit one task --------------
   // A unit whose rows fit one wave task (rows * G <= 64) is one tile; longer
   // ones are cut into runs of 128/G tokens for the workgroup kernel.
   const int tok_per_wg = std::max(1, kMaxTaskRows / G);
-  std::vector<Tile> tiles;
+  std::vector<Tile>& tiles = S.tiles;
+  tiles.clear();
   for (int u = 0; u < U; ++u) {
     const int ql = unit_rows(u);
     if (ql == 0) continue;
     auto kv_end = [&](int t0, int nt) { return u < B ? d->q_start[u] + t0 + nt : vseqs[u - B].hi; };
     if ((int64_t)ql * G <= kMaxWaveRows) {
-      tiles.push_back(Tile{u, 0, ql, class_of_rows(ql * G), kv_end(0, ql)});
+      tiles.push_back(Tile{u, 0, ql, class_of_rows(ql * G), kv_end(0, ql), 0, 0, -1, 0, 0, 0});
       continue;
     }
     for (int t0 = 0; t0 < ql; t0 += tok_per_wg) {
       const int nt = std::min(tok_per_wg, ql - t0);
-      tiles.push_back(Tile{u, t0, nt, kNumClasses - 1, kv_end(t0, nt)});
+      tiles.push_back(Tile{u, t0, nt, kNumClasses - 1, kv_end(t0, nt), 0, 0, -1, 0, 0, 0});
     }
   }
 
   // ---- KV partitions per unit ------------------------------------------------
-  std::vector<int32_t> usplits(U, 0);
+  std::vector<int32_t>& usplits = S.usplits;
+  usplits.assign(U, 0);
   if (d->num_kv_splits > 0) {
     for (int u = 0; u < U; ++u) usplits[u] = unit_rows(u) > 0 ? d->num_kv_splits : 0;
   } else {
@@ -480,17 +567,19 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     // KV-stream bound) and workgroup tasks (128 rows, MFMA bound). A unit's
     // partition count is ceil(cost of its largest tile / quantum of its class).
     int64_t total[2] = {0, 0};
-    std::vector<int64_t> last_cost(U, 0);
-    std::vector<int> unit_kind(U, 0);
+    std::vector<int64_t>& last_cost = S.last_cost;
+    std::vector<int32_t>& unit_kind = S.unit_kind;
+    last_cost.assign(U, 0);
+    unit_kind.assign(U, 0);
     for (const Tile& t : tiles) {
       const int kind = kClassRows[t.cls] > kMaxWaveRows ? 1 : 0;
       const int64_t c = (int64_t)((t.kv_end - unit_lo(t.seq) + kBlock - 1) / kBlock) * unit_cost(t.cls);
-      total[kind] += c * d->num_kv_heads;
+      total[kind] += c * hkv;
       last_cost[t.seq] = std::max(last_cost[t.seq], c);
       unit_kind[t.seq] = kind;
     }
     const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
-    const int64_t target[2] = {cus * kTasksPerCu, cus * (P.row_mask.empty() ? kWgTasksPer2Cu : kWgTasksPer2CuTree) / 2};
+    const int64_t target[2] = {cus * kTasksPerCu, cus * (tree ? kWgTasksPer2CuTree : kWgTasksPer2Cu) / 2};
     int64_t quantum[2];
     for (int k = 0; k < 2; ++k)
       quantum[k] = std::max(kMinQuantum, (total[k] + target[k] - 1) / target[k]);
@@ -508,7 +597,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // u holds blocks [S_u, S_u + n_u) of the concatenation; cut it into pieces of
   // L blocks; a unit's partitions are its parts of the pieces it meets, and
   // piece j of kv head g is the work of one wave.
-  std::vector<char> sunit(U, 0);
+  std::vector<char>& sunit = S.sunit;
+  sunit.assign(U, 0);
   bool any_stream = false, any_other = V > 0;
   for (const Tile& t : tiles) {
     const bool dec = t.seq < B && t.cls == 0;
@@ -517,7 +607,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     any_other = any_other || !dec;
   }
   const bool stream = d->dtype == PMATTN_BF16 && d->num_kv_splits == 0 && any_stream && !any_other;
-  std::vector<int64_t> stream_start(U, 0);
+  std::vector<int64_t>& stream_start = S.stream_start;
+  stream_start.assign(U, 0);
   int64_t stream_len = 0, stream_pieces = 0;
   if (stream) {
     int64_t total = 0;
@@ -526,7 +617,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       if (sunit[u]) total += (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
     }
     const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
-    const int64_t per_head = std::max<int64_t>(1, cus * kStreamWavesPerCu / d->num_kv_heads);
+    const int64_t per_head = std::max<int64_t>(1, cus * kStreamWavesPerCu / hkv);
     stream_len = std::max(kStreamMinBlocks, (total + per_head - 1) / per_head);
     stream_pieces = (total + stream_len - 1) / stream_len;
     for (int u = 0; u < U; ++u) {
@@ -535,7 +626,10 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       usplits[u] = (int32_t)((stream_start[u] + n - 1) / stream_len - stream_start[u] / stream_len + 1);
     }
   }
-  std::vector<int32_t> uoff(U + 1, 0), ubeg, uend;
+  std::vector<int32_t>& uoff = S.uoff;
+  std::vector<int32_t>& ubeg = S.ubeg;
+  std::vector<int32_t>& uend = S.uend;
+  uoff.assign(U + 1, 0);
   for (int u = 0; u < U; ++u) uoff[u + 1] = uoff[u] + usplits[u];
   ubeg.resize(uoff[U]);
   uend.resize(uoff[U]);
@@ -568,176 +662,455 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   P.split_end.assign(uend.begin(), uend.begin() + uoff[B]);
   P.cascade_splits.assign(usplits.begin() + B, usplits.end());
 
-  // ---- tasks, partial records and merge rows --------------------------------
-  // Rows of cascade members collect their records from several tasks: their
-  // merge rows list record ids (rec_stride -1) instead of a stride.
-  std::vector<std::vector<pmattn_work_item>> by_class(2 * kNumClasses);
-  std::vector<int32_t> member_slot(P.num_rows, -1);
+  // ---- KV ranges of the tiles, partial records and table sizes -------------
+  // A tile's tasks are its kv heads times its non-empty partitions (clipped
+  // to the tile's keys). Partial records are numbered tile by tile, kv head
+  // by kv head: tile t, kv head g, its i-th partition, token row m write
+  // record rec0 + (g * k + i) * rows + m. Rows of cascade members collect
+  // their records from several tasks: their merge rows list record ids
+  // (rec_stride -1) instead of a stride.
+  std::vector<Range>& ranges = S.ranges;
+  ranges.clear();
+  int64_t records = 0, n_items = 0, n_merge = 0, n_rec_index = 0;
+  int64_t cls_items[2 * kNumClasses] = {};
+  for (size_t ti = 0; ti < tiles.size(); ++ti) {
+    Tile& t = tiles[ti];
+    const int u = t.seq;
+    t.range0 = (int32_t)ranges.size();
+    for (int p = 0; p < usplits[u]; ++p) {
+      const int32_t lo = ubeg[uoff[u] + p], hi = std::min(uend[uoff[u] + p], t.kv_end);
+      if (lo < hi) ranges.push_back(Range{(int32_t)ti, lo, hi, (hi - lo + kBlock - 1) / kBlock});
+    }
+    t.k = (int32_t)ranges.size() - t.range0;
+    const bool virt = u >= B, listed = virt || member[u];
+    t.row = unit_row(u);
+    t.row0 = virt ? vseqs[u - B].row_begin + t.tok_begin : row_off[u] + t.tok_begin;
+    t.pos0 = virt ? vseqs[u - B].hi + t.tok_begin : d->q_start[u] + t.tok_begin;
+    const int64_t trows = (int64_t)t.n_tok * G;
+    if (t.k > 1 || listed) {
+      t.rec0 = records;
+      records += hkv * t.k * trows;
+    }
+    n_items += (int64_t)t.k * hkv;
+    cls_items[t.cls + (virt ? kNumClasses : 0)] += (int64_t)t.k * hkv;
+    if (t.k > 1 && !listed) n_merge += hkv * trows;
+    if (listed) n_rec_index += hkv * trows * t.k;
+  }
+  std::vector<int32_t>& member_slot = S.member_slot;
   int32_t n_member_rows = 0;
+  member_slot.assign(rows, -1);
   for (int s = 0; s < B; ++s)
     if (member[s])
       for (int r = 0; r < d->q_len[s]; ++r) member_slot[row_off[s] + r] = n_member_rows++;
-  // records of cascade sharers' rows: one entry per (tile, kv head), expanded
-  // into rec_index below (count per (row, head), then fill)
-  struct Listed {
-    int64_t rec_base;
-    int32_t parts, trows, row0, g;
-    bool virt;
-  };
-  std::vector<Listed> listed_blocks;
-  int64_t records = 0;
-  for (const Tile& t : tiles) {
-    const int u = t.seq;
-    const bool virt = u >= B;
-    const int trows = t.n_tok * G;
-    const int base = uoff[u];
-    int k = 0;
-    for (int p = 0; p < usplits[u]; ++p)
-      if (ubeg[base + p] < std::min(uend[base + p], t.kv_end)) ++k;
-    const bool listed = virt || member[u];
-    const bool recs = k > 1 || listed;
-    const int32_t row0 = virt ? vseqs[u - B].row_begin + t.tok_begin : row_off[u] + t.tok_begin;
-    for (int g = 0; g < d->num_kv_heads; ++g) {
-      const int64_t rec_base = records;
-      if (recs) records += (int64_t)k * trows;
-      int made = 0;
-      for (int p = 0; p < usplits[u]; ++p) {
-        const int32_t lo = ubeg[base + p];
-        const int32_t hi = std::min(uend[base + p], t.kv_end);
-        if (lo >= hi) continue;
-        pmattn_work_item it;
-        it.seq = virt ? vseqs[u - B].table_seq : u;
-        it.kv_head = g;
-        it.row_begin = row0;
-        it.n_tok = t.n_tok;
-        it.pos_begin = virt ? vseqs[u - B].hi + t.tok_begin : d->q_start[u] + t.tok_begin;
-        it.kv_begin = lo;
-        it.kv_end = hi;
-        it.part = recs ? (int32_t)(rec_base + (int64_t)made * trows) : -1;
-        by_class[t.cls + (virt ? kNumClasses : 0)].push_back(it);
-        ++made;
-      }
-      if (listed && made) listed_blocks.push_back(Listed{rec_base, made, trows, row0, g, virt});
-      if (k > 1 && !listed)
-        for (int m = 0; m < trows; ++m)
-          P.merge_rows.push_back(pmattn_merge_row{(int32_t)(rec_base + m), trows, k, row0 + m / G, g * G + m % G});
-    }
-  }
-  if (n_member_rows > 0) {
-    const size_t keys = (size_t)n_member_rows * d->num_q_heads;
-    auto key_of = [&](const Listed& lb, int m) {
-      const int32_t row = lb.virt ? P.vrow_src[lb.row0 + m / G] : lb.row0 + m / G;
-      return (size_t)member_slot[row] * d->num_q_heads + lb.g * G + m % G;
-    };
-    std::vector<int32_t> start(keys + 1, 0);
-    for (const Listed& lb : listed_blocks)
-      for (int m = 0; m < lb.trows; ++m) start[key_of(lb, m) + 1] += lb.parts;
-    for (size_t k = 0; k < keys; ++k) start[k + 1] += start[k];
-    P.rec_index.resize(start[keys]);
-    std::vector<int32_t> fill(start.begin(), start.end() - 1);
-    for (const Listed& lb : listed_blocks)
-      for (int m = 0; m < lb.trows; ++m) {
-        int32_t& at = fill[key_of(lb, m)];
-        for (int p = 0; p < lb.parts; ++p) P.rec_index[at++] = (int32_t)(lb.rec_base + (int64_t)p * lb.trows + m);
-      }
-    for (int s = 0; s < B; ++s)
-      if (member[s])
-        for (int r = 0; r < d->q_len[s]; ++r)
-          for (int h = 0; h < d->num_q_heads; ++h) {
-            const size_t k = (size_t)member_slot[row_off[s] + r] * d->num_q_heads + h;
-            P.merge_rows.push_back(pmattn_merge_row{start[k], -1, start[k + 1] - start[k], row_off[s] + r, h});
-          }
-  }
-  if (records > INT32_MAX / 2) return fail(PMATTN_E_INVALID, "too many partial records");
+  n_merge += (int64_t)n_member_rows * d->num_q_heads;
+  if (records > INT32_MAX / 2 || n_items > INT32_MAX / 2 || n_merge > INT32_MAX / 2)
+    return fail(PMATTN_E_INVALID, "too many tasks or partial records");
   P.num_records = (int32_t)records;
 
-  // ---- order: largest estimated cost first within each class (LPT) --------
-  uint64_t rng = d->work_shuffle_seed;
-  P.class_begin.push_back(0);
+  // classes in use, and the kernel that serves the plan
+  P.class_rows.clear();
+  P.class_cascade.clear();
+  P.class_begin.assign(1, 0);
+  bool has_wave = false, has_wg = false;
   for (int c = 0; c < 2 * kNumClasses; ++c) {
-    auto& v = by_class[c];
-    if (v.empty()) continue;
-    std::vector<int64_t> cost(v.size());
-    for (size_t i = 0; i < v.size(); ++i)
-      cost[i] = (int64_t)((v[i].kv_end - v[i].kv_begin + kBlock - 1) / kBlock) * unit_cost(c % kNumClasses);
-    std::vector<size_t> idx(v.size());
-    std::iota(idx.begin(), idx.end(), 0);
-    std::stable_sort(idx.begin(), idx.end(), [&](size_t a, size_t b) { return cost[a] > cost[b]; });
-    if (stream && c == 0) {
-      std::vector<int64_t> ulo(B);
-      for (int u = 0; u < B; ++u) ulo[u] = unit_lo(u);
-      idx = stream_order(v, stream_start, ulo, stream_len, stream_pieces, d->num_kv_heads, P.slot_begin);
-      P.slot_class = (int32_t)P.class_rows.size();
-    } else
-      idx = xcd_order(v, idx, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1,
-                      d->num_kv_heads);
-    if (d->work_shuffle_seed)
-      for (size_t i = idx.size(); i > 1; --i) std::swap(idx[i - 1], idx[splitmix64(rng) % i]);
-    for (size_t i : idx) P.items.push_back(v[i]);
+    if (!cls_items[c]) continue;
     P.class_rows.push_back(kClassRows[c % kNumClasses]);
     P.class_cascade.push_back(c >= kNumClasses ? 1 : 0);
-    P.class_begin.push_back((int32_t)P.items.size());
+    P.class_begin.push_back(P.class_begin.back() + (int32_t)cls_items[c]);
+    (kClassRows[c % kNumClasses] <= kClassRows[0] ? has_wave : has_wg) = true;
+  }
+  // Mixed-batch kernel: a bf16 batch without token trees that mixes 16-row
+  // wave tasks with larger ones (a plan of 16- and 32-row tasks only is mixed
+  // too: its 32-row tasks run as wave tasks beside the 16-row ones)
+  P.mixed = d->dtype == PMATTN_BF16 && !tree && has_wave && has_wg;
+  // the mixed table's streams per XCD: [0] workgroup tiles of more than 64
+  // rows, [1] other workgroup tasks, [2] 16-row wave tasks, [3] 17..32-row
+  // wave tasks
+  auto mix_kind = [](int rows) { return rows <= kClassRows[0] ? 2 : rows <= kClassRows[1] ? 3 : rows > kMaxWaveRows ? 0 : 1; };
+  int64_t mix_n[4][kXcds] = {};
+  int64_t n_mix_entries = 0, n_bundles = 0;
+  if (P.mixed) {
+    for (const Tile& t : tiles)
+      for (int g = 0; g < hkv; ++g) mix_n[mix_kind(kClassRows[t.cls])][xcd_of(g, unit_row(t.seq), hkv)] += t.k;
+    for (int x = 0; x < kXcds; ++x) {
+      const int64_t nb = (mix_n[2][x] + kWaveTasksPerWg - 1) / kWaveTasksPerWg +
+                         (mix_n[3][x] + kWaveTasksPerWg - 1) / kWaveTasksPerWg;
+      n_bundles += nb;
+      n_mix_entries += mix_n[0][x] + mix_n[1][x] + nb;
+    }
+  }
+  const int64_t n_slots = stream ? hkv * stream_pieces : 0;
+
+  // ---- workspace layout and the upload image --------------------------------
+  const size_t sz_items = n_items * sizeof(pmattn_work_item), sz_merge = n_merge * sizeof(pmattn_merge_row),
+               sz_mask = S.row_mask.size() * sizeof(uint64_t), sz_append = S.units.size() * sizeof(pmattn_append_unit),
+               sz_rec = n_rec_index * sizeof(int32_t), sz_vrow = vrow.size() * sizeof(int32_t),
+               sz_slot = (stream ? n_slots + 1 : 0) * sizeof(int32_t), sz_istream = n_items * sizeof(int32_t),
+               sz_mix = n_mix_entries * sizeof(int32_t), sz_bundles = n_bundles * kWaveTasksPerWg * sizeof(int32_t);
+  P.off_items = 0;
+  P.off_merge = align_up(P.off_items + sz_items, kAlign);
+  P.off_row_mask = align_up(P.off_merge + sz_merge, kAlign);
+  P.off_append = align_up(P.off_row_mask + sz_mask, kAlign);
+  P.off_rec_index = align_up(P.off_append + sz_append, kAlign);
+  P.off_vrow = align_up(P.off_rec_index + sz_rec, kAlign);
+  P.off_slot = align_up(P.off_vrow + sz_vrow, kAlign);
+  P.off_istream = align_up(P.off_slot + sz_slot, kAlign);
+  P.off_mix_table = align_up(P.off_istream + sz_istream, kAlign);
+  P.off_mix_bundles = align_up(P.off_mix_table + sz_mix, kAlign);
+  P.off_upload_end = align_up(P.off_mix_bundles + sz_bundles, kAlign);
+  P.off_part_o = P.off_upload_end;
+  P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
+  P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
+  P.blob.reset(P.off_upload_end ? new unsigned char[P.off_upload_end] : nullptr);
+  unsigned char* blob = P.blob.get();
+  {
+    // zero the alignment gaps, so that the image is a function of the plan
+    const size_t off[] = {P.off_items, P.off_merge, P.off_row_mask, P.off_append, P.off_rec_index, P.off_vrow,
+                          P.off_slot, P.off_istream, P.off_mix_table, P.off_mix_bundles, P.off_upload_end};
+    const size_t sz[] = {sz_items, sz_merge, sz_mask, sz_append, sz_rec, sz_vrow, sz_slot, sz_istream, sz_mix, sz_bundles};
+    for (int i = 0; i < 10; ++i)
+      if (off[i + 1] > off[i] + sz[i]) std::memset(blob + off[i] + sz[i], 0, off[i + 1] - off[i] - sz[i]);
+  }
+  auto* items = reinterpret_cast<pmattn_work_item*>(blob + P.off_items);
+  auto* merge = reinterpret_cast<pmattn_merge_row*>(blob + P.off_merge);
+  auto* rec_index = reinterpret_cast<int32_t*>(blob + P.off_rec_index);
+  auto* slot_begin = reinterpret_cast<int32_t*>(blob + P.off_slot);
+  auto* item_stream = reinterpret_cast<int32_t*>(blob + P.off_istream);
+  auto* mix_table = reinterpret_cast<int32_t*>(blob + P.off_mix_table);
+  auto* mix_bundles = reinterpret_cast<int32_t*>(blob + P.off_mix_bundles);
+  if (sz_mask) std::memcpy(blob + P.off_row_mask, S.row_mask.data(), sz_mask);
+  if (sz_append) std::memcpy(blob + P.off_append, S.units.data(), sz_append);
+  if (sz_vrow) std::memcpy(blob + P.off_vrow, vrow.data(), sz_vrow);
+  P.items = {items, (size_t)n_items};
+  P.merge_rows = {merge, (size_t)n_merge};
+  P.row_mask = {reinterpret_cast<const uint64_t*>(blob + P.off_row_mask), S.row_mask.size()};
+  P.append_units = {reinterpret_cast<const pmattn_append_unit*>(blob + P.off_append), S.units.size()};
+  P.rec_index = {rec_index, (size_t)n_rec_index};
+  P.vrow_src = {reinterpret_cast<const int32_t*>(blob + P.off_vrow), vrow.size()};
+  P.slot_begin = {slot_begin, stream ? (size_t)n_slots + 1 : 0};
+  P.item_stream = {item_stream, (size_t)n_items};
+  P.mix_table = {mix_table, (size_t)n_mix_entries};
+  P.mix_bundles = {mix_bundles, (size_t)(n_bundles * kWaveTasksPerWg)};
+
+  // ---- merge rows -------------------------------------------------------------
+  // Rows split over several partitions of one tile: nparts records at a
+  // stride; rows of cascade sharers: their record lists (rec_index), one entry
+  // per (tile, kv head) collected below.
+  {
+    std::vector<Listed>& listed = S.listed;
+    listed.clear();
+    int64_t nm = 0;
+    P.merge_max_parts = 0;
+    for (const Tile& t : tiles) {
+      if (!t.k) continue;
+      const int u = t.seq;
+      const bool virt = u >= B, lst = virt || member[u];
+      const int32_t trows = t.n_tok * G;
+      for (int g = 0; g < hkv; ++g) {
+        const int64_t rec_base = t.rec0 + (int64_t)g * t.k * trows;
+        if (lst) listed.push_back(Listed{rec_base, t.k, trows, t.row0, g, virt});
+        else if (t.k > 1)
+          for (int tok = 0, m = 0; tok < t.n_tok; ++tok)
+            for (int i = 0; i < G; ++i, ++m)
+              merge[nm++] = pmattn_merge_row{(int32_t)(rec_base + m), trows, t.k, t.row0 + tok, g * G + i};
+      }
+      if (!lst && t.k > 1) P.merge_max_parts = std::max(P.merge_max_parts, t.k);
+    }
+    if (n_member_rows > 0) {
+      const size_t keys = (size_t)n_member_rows * d->num_q_heads;
+      auto key_of = [&](const Listed& lb, int m) {
+        const int32_t row = lb.virt ? vrow[lb.row0 + m / G] : lb.row0 + m / G;
+        return (size_t)member_slot[row] * d->num_q_heads + lb.g * G + m % G;
+      };
+      std::vector<int32_t>& start = S.rec_start;
+      start.assign(keys + 1, 0);
+      for (const Listed& lb : listed)
+        for (int m = 0; m < lb.trows; ++m) start[key_of(lb, m) + 1] += lb.parts;
+      for (size_t k = 0; k < keys; ++k) start[k + 1] += start[k];
+      std::vector<int32_t>& fill = S.rec_fill;
+      fill.assign(start.begin(), start.end() - 1);
+      for (const Listed& lb : listed)
+        for (int m = 0; m < lb.trows; ++m) {
+          int32_t& at = fill[key_of(lb, m)];
+          for (int p = 0; p < lb.parts; ++p) rec_index[at++] = (int32_t)(lb.rec_base + (int64_t)p * lb.trows + m);
+        }
+      for (int s = 0; s < B; ++s)
+        if (member[s])
+          for (int r = 0; r < d->q_len[s]; ++r)
+            for (int h = 0; h < d->num_q_heads; ++h) {
+              const size_t k = (size_t)member_slot[row_off[s] + r] * d->num_q_heads + h;
+              const int32_t np = start[k + 1] - start[k];
+              merge[nm++] = pmattn_merge_row{start[k], -1, np, row_off[s] + r, h};
+              P.merge_max_parts = std::max(P.merge_max_parts, np);
+            }
+    }
   }
 
-  // ---- streaming tasks: KV no other tile reads --------------------------------
-  // A block read by two row tiles (a shared prefix, or the tiles of one long
-  // prefill chunk) is worth keeping in the caches: the second reader often
-  // finds it there. A task none of whose blocks is read that way streams its
-  // K/V with non-temporal loads. Readers are row tiles, named by their first
-  // row (real or virtual); the split and kv-head tasks of one tile read
-  // disjoint bytes. A class is 1 when all its tasks stream, 0 when none does,
-  // 2 when the kernel must look up each task's flag. (Measured on MI355X: the 64-sequence decode batch 69% -> 77%
-  // of HBM peak with non-temporal K/V; the long-decode batch, whose blocks
-  // are shared in pairs, 69.5% -> 63.4% had all of it streamed.)
+  // ---- row walk: who reads each pool block --------------------------------
+  // Readers are row tiles. A table row's blocks are read by the ranges of its
+  // own tiles, and by those of the virtual tiles whose keys it holds. Each
+  // row is swept once, segment by segment (runs of block positions under the
+  // same ranges; a tile's ranges never share a block, since partitions start
+  // on block boundaries). A block is marked with its one reading tile (and
+  // that tile's range) and with the one sequence that sees it; it becomes
+  // shared when a segment under two ranges covers it, or when another
+  // reader (or sequence) marks it later.
+  //
+  // Streaming tasks: KV no other tile reads. A block read by two row tiles (a
+  // shared prefix, or the tiles of one long prefill chunk) is worth keeping
+  // in the caches: the second reader often finds it there. A task none of
+  // whose blocks is read that way streams its K/V with non-temporal loads
+  // (a range loses its flag when one of its blocks becomes shared). A class
+  // is 1 when all its tasks stream, 0 when none does, 2 when the kernel must
+  // look up each task's flag. (Measured on MI355X: the 64-sequence decode
+  // batch 69% -> 77% of HBM peak with non-temporal K/V; the long-decode batch,
+  // whose blocks are shared in pairs, 69.5% -> 63.4% had all of it streamed.)
+  std::vector<Mark>& marks = S.marks;
+  if (marks.size() < (size_t)d->num_pool_blocks) {
+    marks.resize(d->num_pool_blocks, Mark{0, 0, 0, 0});
+    S.tstamp.resize(d->num_pool_blocks, 0);
+  }
+  if (++S.gen == 0) {
+    std::fill(marks.begin(), marks.end(), Mark{0, 0, 0, 0});
+    std::fill(S.tstamp.begin(), S.tstamp.end(), 0u);
+    S.gen = 1;
+  }
+  const uint32_t gen = S.gen;
+  const uint32_t nranges = (uint32_t)ranges.size();
+  std::vector<char>& rstream = S.rstream;
+  rstream.assign(nranges, 1);
   {
-    // Tasks of one tile and partition differ only in their kv head, so each
-    // distinct (reader, key range) is walked once.
-    // per block: -1 unread, its only reader so far (>= 0), or kMulti
-    constexpr int32_t kMulti = -2;
-    std::vector<int32_t> reader_of(d->num_pool_blocks, -1);
-    auto for_blocks = [&](const pmattn_work_item& it, auto&& fn) {
-      const int32_t* row = d->block_table + (int64_t)it.seq * d->bt_stride;
-      for (int32_t j = it.kv_begin / kBlock; j * kBlock < it.kv_end; ++j) fn(row[j]);
-    };
-    // distinct ranges per reader as linked lists (a reader has one range per
-    // KV partition of its tile); readers are row indices, real rows first
-    std::vector<int32_t> head(row_off[B] + P.vrow_src.size(), -1), next;
-    std::vector<size_t> reps;        // one task per distinct (reader, range)
-    std::vector<int32_t> item_range(P.items.size());
-    for (size_t c = 0; c + 1 < P.class_begin.size(); ++c)
-      for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
-        const pmattn_work_item& it = P.items[i];
-        const int32_t reader = P.class_cascade[c] ? row_off[B] + it.row_begin : it.row_begin;
-        int32_t r = head[reader];
-        while (r >= 0 && (P.items[reps[r]].kv_begin != it.kv_begin || P.items[reps[r]].kv_end != it.kv_end)) r = next[r];
-        if (r >= 0) {
-          item_range[i] = r;
-          continue;
-        }
-        item_range[i] = (int32_t)reps.size();
-        next.push_back(head[reader]);
-        head[reader] = (int32_t)reps.size();
-        reps.push_back(i);
-        for_blocks(it, [&](int32_t b) {
-          const int32_t rd = reader_of[b];
-          if (rd != reader && rd != kMulti) reader_of[b] = rd == -1 ? reader : kMulti;
-        });
+    std::vector<uint32_t>& rkey = S.key;
+    std::vector<uint32_t>& rorder = S.row_list;
+    rkey.resize(nranges);
+    rorder.resize(nranges);
+    for (uint32_t r = 0; r < nranges; ++r) rkey[r] = (uint32_t)unit_row(tiles[ranges[r].tile].seq);
+    counting_order(rkey.data(), nranges, (size_t)B, S.cnt, rorder.data());
+    std::vector<Event>& ev = S.events;
+    std::vector<uint32_t>& active = S.active;
+    for (uint32_t a = 0, e; a < nranges; a = e) {
+      const int s = (int)rkey[rorder[a]];
+      ev.clear();
+      for (e = a; e < nranges && (int)rkey[rorder[e]] == s; ++e) {
+        const uint32_t id = rorder[e];
+        const Range& r = ranges[id];
+        ev.push_back(Event{r.lo / kBlock, id, 1});
+        ev.push_back(Event{(r.hi + kBlock - 1) / kBlock, id, 0});
       }
-    std::vector<int32_t> rep_stream(reps.size());
-    for (size_t r = 0; r < reps.size(); ++r) {
-      const pmattn_work_item& it = P.items[reps[r]];
-      const int32_t* row = d->block_table + (int64_t)it.seq * d->bt_stride;
-      int32_t j = it.kv_begin / kBlock;
-      while (j * kBlock < it.kv_end && reader_of[row[j]] != kMulti) ++j;
-      rep_stream[r] = j * kBlock >= it.kv_end ? 1 : 0;
+      // by position, ends before starts
+      if (ev.size() <= 32) {
+        for (size_t i = 1; i < ev.size(); ++i)
+          for (size_t j = i; j > 0 && ev[j] < ev[j - 1]; --j) std::swap(ev[j], ev[j - 1]);
+      } else {
+        std::sort(ev.begin(), ev.end());
+      }
+      const int32_t* row = bt_row(s);
+      active.clear();
+      int32_t nvirt = 0;
+      for (size_t i = 0; i < ev.size();) {
+        const int32_t p = ev[i].pos;
+        for (; i < ev.size() && ev[i].pos == p; ++i) {
+          const Event& x = ev[i];
+          const bool virt = tiles[ranges[x.range].tile].seq >= B;
+          if (x.start) {
+            active.push_back(x.range);
+            nvirt += virt;
+          } else {
+            active.erase(std::find(active.begin(), active.end(), x.range));
+            nvirt -= virt;
+          }
+        }
+        if (active.empty() || i == ev.size()) continue;
+        const int32_t q = ev[i].pos;  // the segment is [p, q)
+        const int32_t who = nvirt ? kMulti : s;
+        if (active.size() == 1) {
+          const int32_t rid = (int32_t)active[0], tile = ranges[rid].tile;
+          bool shared = false;
+          for (int32_t j = p; j < q; ++j) {
+            Mark& m = marks[row[j]];
+            if (m.gen != gen) {
+              m = Mark{gen, tile, who, rid};
+              continue;
+            }
+            if (m.reader != tile) {
+              if (m.reader != kMulti) {
+                rstream[m.range] = 0;
+                m.reader = kMulti;
+              }
+              shared = true;
+            }
+            if (m.seq != who && m.seq != kMulti) m.seq = kMulti;
+          }
+          if (shared) rstream[rid] = 0;
+        } else {
+          for (uint32_t id : active) rstream[id] = 0;
+          for (int32_t j = p; j < q; ++j) {
+            Mark& m = marks[row[j]];
+            if (m.gen != gen) {
+              m = Mark{gen, kMulti, who, -1};
+              continue;
+            }
+            if (m.reader != kMulti) {
+              rstream[m.range] = 0;
+              m.reader = kMulti;
+            }
+            if (m.seq != who && m.seq != kMulti) m.seq = kMulti;
+          }
+        }
+      }
     }
-    P.item_stream.assign(P.items.size(), 0);
-    for (size_t c = 0; c + 1 < P.class_begin.size(); ++c) {
-      int32_t n = 0;
-      for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) n += P.item_stream[i] = rep_stream[item_range[i]];
-      const int32_t total = P.class_begin[c + 1] - P.class_begin[c];
-      P.class_stream.push_back(n == total ? 1 : n == 0 ? 0 : 2);
+  }
+  // The append check: a block that one sequence writes and no other sequence
+  // sees, and that no other unit writes, cannot conflict; otherwise the exact
+  // check decides.
+  {
+    bool exact = false;
+    for (const Target& t : S.targets) {
+      const Mark& m = marks[t.blk];
+      exact = exact || S.tstamp[t.blk] == gen || m.gen != gen || m.seq != t.seq;
+      S.tstamp[t.blk] = gen;
     }
+    P.append_conflict = exact ? exact_append_check(d, S.targets) : std::string();
+  }
+
+  // ---- order: largest estimated cost first within each class (LPT) --------
+  // Within a class, tasks are ordered by XCD and, per XCD, by estimated cost
+  // descending (KV blocks: the class fixes the cost per block), ties in
+  // generation order (tile, kv head, partition); workgroup slots then take
+  // them per XCD (deal). Equal-work decode plans deal wave slots instead.
+  uint64_t rng = d->work_shuffle_seed;
+  const int rep = hkv >= kXcds ? 1 : (kXcds + hkv - 1) / hkv;  // XCDs per kv head
+  std::vector<uint32_t>& tile_first = S.tile_first;
+  std::vector<uint32_t>& tile_list = S.tile_list;
+  {
+    std::vector<uint32_t>& tkey = S.key;
+    tkey.resize(tiles.size());
+    tile_list.resize(tiles.size());
+    for (size_t i = 0; i < tiles.size(); ++i) tkey[i] = tiles[i].cls + (tiles[i].seq >= B ? kNumClasses : 0);
+    counting_order(tkey.data(), (uint32_t)tiles.size(), 2 * kNumClasses, S.cnt, tile_list.data());
+    tile_first.assign(2 * kNumClasses + 1, 0);
+    for (size_t i = 0; i < tiles.size(); ++i) ++tile_first[tkey[i] + 1];
+    for (int c = 0; c < 2 * kNumClasses; ++c) tile_first[c + 1] += tile_first[c];
+  }
+  std::vector<Cand>& cand = S.cand;  // a class's tasks in generation order
+  std::vector<uint32_t>& key = S.key;
+  std::vector<uint32_t>& order = S.order;
+  // per class and XCD, the class's tasks in queue order (largest first), as
+  // item indices: qitem[class_begin + [qseg[c][x], qseg[c][x + 1]) )
+  std::vector<int32_t>& qitem = S.qitem;
+  qitem.resize(n_items);
+  size_t qseg[2 * kNumClasses][kXcds + 1] = {};
+  int64_t pos = 0;
+  P.slot_class = -1;
+  P.class_stream.clear();
+  for (int c = 0, ci = 0; c < 2 * kNumClasses; ++c) {
+    if (!cls_items[c]) continue;
+    const uint32_t n = (uint32_t)cls_items[c];
+    cand.resize(n);
+    key.resize(n);
+    order.resize(2 * (size_t)n);
+    uint32_t* out = order.data() + n;
+    uint32_t i = 0, maxb = 0;
+    for (uint32_t k = tile_first[c]; k < tile_first[c + 1]; ++k) {
+      const Tile& t = tiles[tile_list[k]];
+      const uint32_t xo = (uint32_t)(unit_row(t.seq) % rep);
+      for (int g = 0; g < hkv; ++g) {
+        const uint32_t x = ((uint32_t)g * rep + xo) % kXcds;
+        for (int32_t r = t.range0; r < t.range0 + t.k; ++r) cand[i++] = Cand{(uint32_t)r, (uint16_t)g, (uint16_t)x};
+      }
+      for (int32_t r = t.range0; r < t.range0 + t.k; ++r) maxb = std::max(maxb, (uint32_t)ranges[r].nblk);
+    }
+    // writes task `ci` of the class at item index `at` (in dispatch order
+    // directly, or after the shuffle)
+    int32_t nstream = 0;
+    const bool direct = !d->work_shuffle_seed;
+    auto emit = [&](int64_t at, uint32_t ci) {
+      const Cand& cd = cand[ci];
+      const Range& rg = ranges[cd.range];
+      const Tile& t = tiles[rg.tile];
+      pmattn_work_item& it = items[at];
+      it.seq = t.row;
+      it.kv_head = cd.g;
+      it.row_begin = t.row0;
+      it.n_tok = t.n_tok;
+      it.pos_begin = t.pos0;
+      it.kv_begin = rg.lo;
+      it.kv_end = rg.hi;
+      it.part = t.rec0 < 0 ? -1 : (int32_t)(t.rec0 + ((int64_t)cd.g * t.k + (cd.range - t.range0)) * t.n_tok * G);
+      nstream += item_stream[at] = rstream[cd.range];
+    };
+    uint32_t nout = 0;
+    if (stream && c == 0) {
+      // Slot (g, j) is the run of tasks of kv head g inside piece j, in unit
+      // order (each unit's partition p lies in piece start_u / len + p;
+      // partitions start at piece boundaries or at the unit's first key, so
+      // the first block tells the piece). Slots go to XCDs like tasks (kv head
+      // g on XCD g; with fewer than kXcds heads, piece j of head g on XCD
+      // g * rep + j % rep), four per workgroup.
+      for (uint32_t k = 0; k < n; ++k) {
+        const Range& r = ranges[cand[k].range];
+        const int u = tiles[r.tile].seq;
+        key[k] = (uint32_t)(cand[k].g * stream_pieces + (stream_start[u] + (r.lo - unit_lo(u)) / kBlock) / stream_len);
+      }
+      uint32_t* byslot = order.data();
+      counting_order(key.data(), n, (size_t)n_slots, S.cnt, byslot);
+      std::vector<int32_t>& sfirst = S.slot_first;  // tasks of slot q: byslot[sfirst[q], sfirst[q + 1])
+      sfirst.assign(n_slots + 1, 0);
+      for (uint32_t k = 0; k < n; ++k) ++sfirst[key[k] + 1];
+      for (int64_t q = 0; q < n_slots; ++q) sfirst[q + 1] += sfirst[q];
+      // queues of slots per XCD, each in slot order
+      std::vector<uint32_t>& qkey = S.slot_key;
+      std::vector<uint32_t>& qorder = S.slot_order;
+      qkey.resize(n_slots);
+      qorder.resize(n_slots);
+      size_t qb[kXcds], qe[kXcds] = {};
+      for (int g = 0; g < hkv; ++g)
+        for (int64_t j = 0; j < stream_pieces; ++j)
+          ++qe[qkey[g * stream_pieces + j] = (uint32_t)((g * rep + (int)(j % rep)) % kXcds)];
+      counting_order(qkey.data(), (uint32_t)n_slots, kXcds, S.cnt, qorder.data());
+      for (size_t x = 0, acc = 0; x < kXcds; ++x) {
+        qb[x] = acc;
+        qe[x] = acc += qe[x];
+      }
+      slot_begin[0] = 0;
+      int64_t w = 0;
+      deal(qb, qe, kWaveTasksPerWg, [&](size_t e) {
+        const uint32_t q = qorder[e];
+        for (int32_t k = sfirst[q]; k < sfirst[q + 1]; ++k) {
+          if (direct) emit(pos + nout, byslot[k]);
+          out[nout++] = byslot[k];
+        }
+        slot_begin[++w] = (int32_t)nout;
+      });
+      P.slot_class = ci;
+    } else {
+      const uint32_t nb = maxb + 1;
+      size_t* qs = qseg[c];
+      size_t qb[kXcds], qe[kXcds] = {};
+      for (uint32_t k = 0; k < n; ++k) {
+        key[k] = cand[k].x * nb + (maxb - (uint32_t)ranges[cand[k].range].nblk);
+        ++qe[cand[k].x];
+      }
+      uint32_t* sorted = order.data();
+      counting_order(key.data(), n, (size_t)kXcds * nb, S.cnt, sorted);
+      for (size_t x = 0, acc = 0; x < kXcds; ++x) {
+        qs[x] = qb[x] = acc;
+        qs[x + 1] = qe[x] = acc += qe[x];
+      }
+      int32_t* qi = qitem.data() + pos;
+      deal(qb, qe, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1, [&](size_t e) {
+        qi[e] = (int32_t)(pos + nout);
+        if (direct) emit(pos + nout, sorted[e]);
+        out[nout++] = sorted[e];
+      });
+    }
+    if (d->work_shuffle_seed) {
+      shuffle(out, n, rng);
+      for (uint32_t k = 0; k < n; ++k) emit(pos + k, out[k]);
+    }
+    P.class_stream.push_back(nstream == (int32_t)n ? 1 : nstream == 0 ? 0 : 2);
+    pos += n;
+    ++ci;
   }
 
   // ---- mixed-batch kernel table ----------------------------------------------
@@ -747,147 +1120,132 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // tasks from one table, ordered by cost across cores). Each workgroup runs
   // one table entry: a workgroup task (K/V staged once in LDS for its four
   // waves) or a bundle of four wave tasks (one per wave, each streaming its
-  // own K/V). Per XCD (kv head g on XCD g, as in xcd_order, so that readers
-  // of a block meet in one L2), both kinds are taken largest first and
+  // own K/V). Per XCD (kv head g on XCD g, as for the class order, so that
+  // readers of a block meet in one L2), both kinds are taken largest first and
   // interleaved in proportion to their estimated cost, so that every CU holds
   // some of each while they run (decode streams HBM beside MFMA-bound prefill
   // tiles; POD-Attention, XY-Serve review reference list) and both kinds end
   // together. Bundles hold four wave tasks of neighbouring cost.
-  {
-    bool has_wave = false, has_wg = false;
-    for (int32_t rows : P.class_rows) (rows <= kClassRows[0] ? has_wave : has_wg) = true;
-    P.mixed = d->dtype == PMATTN_BF16 && P.row_mask.empty() && has_wave && has_wg;
-    // (a plan of 16- and 32-row tasks only is mixed too: its 32-row tasks run
-    // as wave tasks beside the 16-row ones)
-    if (P.mixed) {
-      const int rep = d->num_kv_heads >= kXcds ? 1 : (kXcds + d->num_kv_heads - 1) / d->num_kv_heads;
-      struct Entry {
-        int64_t cost;
-        int32_t e;
-      };
-      // streams: [0] workgroup tiles of more than 64 rows, [1] other workgroup
-      // tasks, [2] 16-row wave tasks, [3] 17..32-row wave tasks
-      std::vector<Entry> parts[4][kXcds];
+  if (P.mixed) {
+    // estimated duration (1/100 us) in this kernel, per KV block: see
+    // kMix*BlockCost (a bundle lasts as long as its longest task)
+    static constexpr int64_t per_block[4] = {kMixTileBlockCost, kMixSmallTaskBlockCost, kMixWaveBlockCost,
+                                             kMixWave32BlockCost};
+    auto nblk_of = [&](int32_t i) { return (items[i].kv_end - items[i].kv_begin + kBlock - 1) / kBlock; };
+    int64_t casc_from = 0;  // cascade classes come after the plain ones
+    for (int c = 0; c < kNumClasses; ++c) casc_from += cls_items[c];
+    auto is_cascade = [&](int32_t i) { return i >= casc_from ? 1 : 0; };
+    // Per stream k and XCD x, the tasks largest first, ties in plan order:
+    // mord[seg[k * kXcds + x], seg[k * kXcds + x + 1]), as item indices.
+    const uint32_t n = (uint32_t)n_items;
+    std::vector<int32_t>& mord = S.mix_code;
+    mord.resize(n);
+    size_t seg[4 * kXcds + 1] = {};
+    int cls_of_kind[4][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};  // (plain, cascade) class index
+    for (int c = 0; c < 2 * kNumClasses; ++c)
+      if (cls_items[c]) cls_of_kind[mix_kind(kClassRows[c % kNumClasses])][c >= kNumClasses] = c;
+    if (!d->work_shuffle_seed) {
+      // each class's XCD queues are in that order already: merge the plain
+      // and the cascade class of each stream (plain first on ties, as in plan
+      // order)
+      size_t w = 0;
+      for (int k = 0; k < 4; ++k)
+        for (int x = 0; x < kXcds; ++x) {
+          seg[k * kXcds + x] = w;
+          const int32_t *a = nullptr, *ae = nullptr, *b = nullptr, *be = nullptr;
+          for (int h = 0; h < 2; ++h) {
+            const int c = cls_of_kind[k][h];
+            if (c < 0) continue;
+            int64_t base = 0;
+            for (int cc = 0; cc < c; ++cc) base += cls_items[cc];
+            const int32_t* lo = qitem.data() + base + qseg[c][x];
+            const int32_t* hi = qitem.data() + base + qseg[c][x + 1];
+            if (h == 0) a = lo, ae = hi;
+            else b = lo, be = hi;
+          }
+          while (a != ae && b != be) mord[w++] = nblk_of(*b) > nblk_of(*a) ? *b++ : *a++;
+          while (a != ae) mord[w++] = *a++;
+          while (b != be) mord[w++] = *b++;
+        }
+      seg[4 * kXcds] = w;
+    } else {
+      // shuffled class order: sort again (stable counting sort)
+      uint32_t maxb = 0;
+      for (uint32_t i = 0; i < n; ++i) maxb = std::max(maxb, (uint32_t)nblk_of(i));
+      const uint32_t nb = maxb + 1;
+      key.resize(n);
+      order.resize(n);
       for (size_t c = 0; c + 1 < P.class_begin.size(); ++c) {
-        const int rows = P.class_rows[c];
-        const int k = rows <= kClassRows[0] ? 2 : rows <= kClassRows[1] ? 3 : rows > kMaxWaveRows ? 0 : 1;
+        const int kd = mix_kind(P.class_rows[c]);
         for (int32_t i = P.class_begin[c]; i < P.class_begin[c + 1]; ++i) {
-          const pmattn_work_item& it = P.items[i];
-          const int x = (d->num_kv_heads >= kXcds ? it.kv_head : it.kv_head * rep + it.seq % rep) % kXcds;
-          const int64_t nblk = (it.kv_end - it.kv_begin + kBlock - 1) / kBlock;
-          // estimated duration (1/100 us) in this kernel, per KV block: see
-          // kMix*BlockCost (a bundle lasts as long as its longest task)
-          static constexpr int64_t per_block[4] = {kMixTileBlockCost, kMixSmallTaskBlockCost, kMixWaveBlockCost,
-                                                   kMixWave32BlockCost};
-          parts[k][x].push_back(Entry{nblk * per_block[k], i * 2 + P.class_cascade[c]});
+          const uint32_t bucket = kd * kXcds + xcd_of(items[i].kv_head, items[i].seq, hkv);
+          key[i] = bucket * nb + (maxb - (uint32_t)nblk_of(i));
+          ++seg[bucket + 1];
         }
       }
-      std::vector<std::vector<int32_t>> lists(kXcds);
-      for (int x = 0; x < kXcds; ++x) {
-        std::vector<Entry> streams[4];
-        for (int k = 0; k < 4; ++k) {
-          auto& v = parts[k][x];
-          std::stable_sort(v.begin(), v.end(), [](const Entry& a, const Entry& b) { return a.cost > b.cost; });
-          if (d->work_shuffle_seed)
-            for (size_t i = v.size(); i > 1; --i) std::swap(v[i - 1], v[splitmix64(rng) % i]);
-          if (k < 2) {
-            for (const Entry& en : v) streams[k].push_back(Entry{en.cost, 4 * (en.e >> 1) + 2 * (en.e & 1)});
-            continue;
-          }
-          // bundles of four wave tasks of neighbouring cost
-          for (size_t i = 0; i < v.size(); i += kWaveTasksPerWg) {
-            const int32_t b = (int32_t)(P.mix_bundles.size() / kWaveTasksPerWg);
-            for (size_t j = i; j < i + kWaveTasksPerWg; ++j) P.mix_bundles.push_back(j < v.size() ? v[j].e : -1);
-            streams[k].push_back(Entry{v[i].cost, 4 * b + 1});  // the bundle's longest task
-          }
-        }
-        // Interleave in proportion to estimated duration (next comes the
-        // stream that has used the smallest share of its own total), in
-        // groups of kSeRoundRobin entries of one stream and neighbouring cost.
-        // Within an XCD the hardware deals workgroups to its shader engines
-        // round-robin and in order (measured on MI355X: entry k of an XCD
-        // always lands on engine k % 4 of a fixed per-XCD order), so a group
-        // puts one entry of the same kind on every engine: the engines free
-        // their slots at the same pace (one full engine blocks dispatch to
-        // the others) and each engine's CUs see every kind in turn.
-        int64_t tot[4] = {0, 0, 0, 0}, used[4] = {0, 0, 0, 0};
-        size_t h[4] = {0, 0, 0, 0};
-        for (int k = 0; k < 4; ++k)
-          for (const Entry& en : streams[k]) tot[k] += en.cost;
-        for (;;) {
-          int k = -1;
-          for (int j = 0; j < 4; ++j) {
-            if (h[j] == streams[j].size()) continue;
-            if (k < 0 || (__int128)used[j] * tot[k] < (__int128)used[k] * tot[j]) k = j;
-          }
-          if (k < 0) break;
-          for (int g = 0; g < kSeRoundRobin && h[k] < streams[k].size(); ++g) {
-            const Entry& en = streams[k][h[k]++];
-            used[k] += en.cost;
-            lists[x].push_back(en.e);
-          }
-        }
-      }
-      // workgroup i runs on XCD i % kXcds; an XCD whose list ran out is
-      // topped up from the one with the most entries left
-      size_t total = 0;
-      for (const auto& l : lists) total += l.size();
-      std::vector<size_t> head(kXcds, 0);
-      for (size_t slot = 0; P.mix_table.size() < total; ++slot) {
-        int x = (int)(slot % kXcds);
-        if (head[x] == lists[x].size()) {
-          size_t best = 0;
-          for (int y = 0; y < kXcds; ++y)
-            if (lists[y].size() - head[y] > best) best = lists[y].size() - head[y], x = y;
-        }
-        P.mix_table.push_back(lists[x][head[x]++]);
-      }
+      counting_order(key.data(), n, (size_t)4 * kXcds * nb, S.cnt, order.data());
+      for (int k = 0; k < 4 * kXcds; ++k) seg[k + 1] += seg[k];
+      for (uint32_t i = 0; i < n; ++i) mord[i] = (int32_t)order[i];
     }
+    std::vector<MixEntry>* streams = S.mix_streams;
+    std::vector<int32_t>& cat = S.mix_cat;  // the XCDs' lists, end to end
+    cat.clear();
+    size_t lb[kXcds], le[kXcds];
+    int32_t nbund = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      for (int k = 0; k < 4; ++k) {
+        int32_t* v = mord.data() + seg[k * kXcds + x];
+        const size_t m = seg[k * kXcds + x + 1] - seg[k * kXcds + x];
+        if (d->work_shuffle_seed) shuffle(v, m, rng);
+        streams[k].clear();
+        if (k < 2) {
+          for (size_t j = 0; j < m; ++j)
+            streams[k].push_back(MixEntry{nblk_of(v[j]) * per_block[k], 4 * v[j] + 2 * is_cascade(v[j])});
+          continue;
+        }
+        // bundles of four wave tasks of neighbouring cost
+        for (size_t j = 0; j < m; j += kWaveTasksPerWg) {
+          for (size_t q = j; q < j + kWaveTasksPerWg; ++q)
+            mix_bundles[nbund * kWaveTasksPerWg + (q - j)] = q < m ? 2 * v[q] + is_cascade(v[q]) : -1;
+          streams[k].push_back(MixEntry{nblk_of(v[j]) * per_block[k], 4 * nbund + 1});  // the bundle's longest task
+          ++nbund;
+        }
+      }
+      // Interleave in proportion to estimated duration (next comes the
+      // stream that has used the smallest share of its own total), in
+      // groups of kSeRoundRobin entries of one stream and neighbouring cost.
+      // Within an XCD the hardware deals workgroups to its shader engines
+      // round-robin and in order (measured on MI355X: entry k of an XCD
+      // always lands on engine k % 4 of a fixed per-XCD order), so a group
+      // puts one entry of the same kind on every engine: the engines free
+      // their slots at the same pace (one full engine blocks dispatch to
+      // the others) and each engine's CUs see every kind in turn.
+      lb[x] = cat.size();
+      int64_t tot[4] = {0, 0, 0, 0}, used[4] = {0, 0, 0, 0};
+      size_t h[4] = {0, 0, 0, 0};
+      for (int k = 0; k < 4; ++k)
+        for (const MixEntry& en : streams[k]) tot[k] += en.cost;
+      for (;;) {
+        int k = -1;
+        for (int j = 0; j < 4; ++j) {
+          if (h[j] == streams[j].size()) continue;
+          if (k < 0 || (__int128)used[j] * tot[k] < (__int128)used[k] * tot[j]) k = j;
+        }
+        if (k < 0) break;
+        for (int g = 0; g < kSeRoundRobin && h[k] < streams[k].size(); ++g) {
+          const MixEntry& en = streams[k][h[k]++];
+          used[k] += en.cost;
+          cat.push_back(en.e);
+        }
+      }
+      le[x] = cat.size();
+    }
+    // workgroup i runs on XCD i % kXcds; an XCD whose list ran out is
+    // topped up from the one with the most entries left
+    int64_t nt = 0;
+    deal(lb, le, 1, [&](size_t e) { mix_table[nt++] = cat[e]; });
   }
 
-  for (const pmattn_merge_row& mr : P.merge_rows) P.merge_max_parts = std::max(P.merge_max_parts, mr.nparts);
-
-  // ---- workspace layout and the upload image --------------------------------
-  P.off_items = 0;
-  P.off_merge = align_up(P.off_items + P.items.size() * sizeof(pmattn_work_item), kAlign);
-  P.off_row_mask = align_up(P.off_merge + P.merge_rows.size() * sizeof(pmattn_merge_row), kAlign);
-  P.off_append = align_up(P.off_row_mask + P.row_mask.size() * sizeof(uint64_t), kAlign);
-  P.off_rec_index = align_up(P.off_append + P.append_units.size() * sizeof(pmattn_append_unit), kAlign);
-  P.off_vrow = align_up(P.off_rec_index + P.rec_index.size() * sizeof(int32_t), kAlign);
-  P.off_slot = align_up(P.off_vrow + P.vrow_src.size() * sizeof(int32_t), kAlign);
-  P.off_istream = align_up(P.off_slot + P.slot_begin.size() * sizeof(int32_t), kAlign);
-  P.off_mix_table = align_up(P.off_istream + P.item_stream.size() * sizeof(int32_t), kAlign);
-  P.off_mix_bundles = align_up(P.off_mix_table + P.mix_table.size() * sizeof(int32_t), kAlign);
-  P.off_upload_end = align_up(P.off_mix_bundles + P.mix_bundles.size() * sizeof(int32_t), kAlign);
-  P.off_part_o = P.off_upload_end;
-  P.off_part_lse = align_up(P.off_part_o + (size_t)records * P.head_dim * sizeof(float), kAlign);
-  P.ws_bytes = std::max(kAlign, align_up(P.off_part_lse + (size_t)records * sizeof(float), kAlign));
-  P.upload_blob.assign(P.off_upload_end, 0);
-  if (!P.items.empty())
-    std::memcpy(P.upload_blob.data() + P.off_items, P.items.data(),
-                P.items.size() * sizeof(pmattn_work_item));
-  if (!P.merge_rows.empty())
-    std::memcpy(P.upload_blob.data() + P.off_merge, P.merge_rows.data(),
-                P.merge_rows.size() * sizeof(pmattn_merge_row));
-  if (!P.row_mask.empty())
-    std::memcpy(P.upload_blob.data() + P.off_row_mask, P.row_mask.data(),
-                P.row_mask.size() * sizeof(uint64_t));
-  if (!P.append_units.empty())
-    std::memcpy(P.upload_blob.data() + P.off_append, P.append_units.data(),
-                P.append_units.size() * sizeof(pmattn_append_unit));
-  if (!P.rec_index.empty())
-    std::memcpy(P.upload_blob.data() + P.off_rec_index, P.rec_index.data(), P.rec_index.size() * sizeof(int32_t));
-  if (!P.vrow_src.empty())
-    std::memcpy(P.upload_blob.data() + P.off_vrow, P.vrow_src.data(), P.vrow_src.size() * sizeof(int32_t));
-  if (!P.slot_begin.empty())
-    std::memcpy(P.upload_blob.data() + P.off_slot, P.slot_begin.data(), P.slot_begin.size() * sizeof(int32_t));
-  if (!P.item_stream.empty())
-    std::memcpy(P.upload_blob.data() + P.off_istream, P.item_stream.data(), P.item_stream.size() * sizeof(int32_t));
-  if (!P.mix_table.empty())
-    std::memcpy(P.upload_blob.data() + P.off_mix_table, P.mix_table.data(), P.mix_table.size() * sizeof(int32_t));
-  if (!P.mix_bundles.empty())
-    std::memcpy(P.upload_blob.data() + P.off_mix_bundles, P.mix_bundles.data(),
-                P.mix_bundles.size() * sizeof(int32_t));
   P.id = g_next_plan_id.fetch_add(1);
   return PMATTN_OK;
 }
@@ -930,7 +1288,24 @@ pmattn_status pmattn_plan_workspace_bytes(pmattn_plan_t plan, size_t* bytes) {
 pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   clear_error();
   if (!plan || !t) return fail(PMATTN_E_INVALID, "NULL argument");
-  const Plan& P = plan->p;
+  Plan& P = plan->p;
+  try {
+    // the row tables are built on first export (nothing on the launch path
+    // reads them)
+    std::call_once(P.rows_once, [&P] {
+      P.row_seq.resize(P.num_rows);
+      P.row_pos.resize(P.num_rows);
+      for (int s = 0; s < P.num_seqs; ++s)
+        for (int32_t r = P.seq_row_off[s]; r < P.seq_row_off[s + 1]; ++r) {
+          P.row_seq[r] = s;
+          P.row_pos[r] = P.seq_q_start[s] + (r - P.seq_row_off[s]);
+        }
+    });
+  } catch (const std::bad_alloc&) {
+    return fail(PMATTN_E_NOMEM, "host allocation failed while exporting");
+  } catch (...) {
+    return fail(PMATTN_E_INVALID, "unexpected error while exporting");
+  }
   t->num_rows = P.num_rows;
   t->row_seq = P.row_seq.data();
   t->row_pos = P.row_pos.data();
@@ -963,7 +1338,7 @@ pmattn_status pmattn_plan_export(pmattn_plan_t plan, pmattn_plan_tables* t) {
   t->num_rec_index = (int32_t)P.rec_index.size();
   t->rec_index = P.rec_index.data();
   t->num_slots = P.slot_begin.empty() ? 0 : (int32_t)P.slot_begin.size() - 1;
-  t->slot_begin = P.slot_begin.empty() ? nullptr : P.slot_begin.data();
+  t->slot_begin = P.slot_begin.data();
   t->class_stream = P.class_stream.data();
   t->item_stream = P.item_stream.data();
   t->mixed_kernel = P.mixed ? 1 : 0;

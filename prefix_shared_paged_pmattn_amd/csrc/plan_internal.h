@@ -4,6 +4,8 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -32,6 +34,19 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Read-only view of one table inside the plan's upload image.
+template <typename T>
+struct Table {
+  const T* ptr = nullptr;
+  size_t n = 0;
+  const T* data() const { return n ? ptr : nullptr; }
+  size_t size() const { return n; }
+  bool empty() const { return n == 0; }
+  const T& operator[](size_t i) const { return ptr[i]; }
+  const T* begin() const { return ptr; }
+  const T* end() const { return ptr + n; }
+};
+
 struct Plan {
   uint64_t id = 0;
   // batch shape
@@ -39,20 +54,14 @@ struct Plan {
   int32_t hq = 0, hkv = 0, group = 0, head_dim = 0, dtype = 0;
   float scale = 0.f;
   // canonical tables
-  std::vector<int32_t> row_seq, row_pos;
   std::vector<int32_t> num_splits, split_offset, split_begin, split_end;
-  std::vector<pmattn_work_item> items;
   std::vector<int32_t> class_rows, class_begin, class_cascade;
-  // per task: 1 when no block it reads is read by another sequence's tasks
-  // (the kernel then streams its K/V with non-temporal loads); per class: 1
-  // all tasks, 0 none, 2 some
-  std::vector<int32_t> item_stream, class_stream;
-  std::vector<pmattn_merge_row> merge_rows;
+  // per class: 1 when all its tasks stream their K/V with non-temporal loads
+  // (no block they read is read by another row tile), 0 none, 2 some (the
+  // kernel reads the per-task flags, item_stream)
+  std::vector<int32_t> class_stream;
   int32_t merge_max_parts = 0;  // largest nparts of any merge row
-  // equal-work decode plans: wave w runs tasks [slot_begin[w], slot_begin[w + 1])
-  // of the plan's single class; empty when every task is its own wave
-  std::vector<int32_t> slot_begin;
-  int32_t slot_class = -1;  // the class slot_begin belongs to
+  int32_t slot_class = -1;      // the class slot_begin belongs to
   int32_t num_records = 0;
   // Mixed-batch kernel (bf16 plans without token trees holding both 16-row
   // wave tasks and larger tasks): one workgroup per table entry, either one
@@ -60,25 +69,38 @@ struct Plan {
   // tasks, one per wave (entry 4 * bundle + 1; bundle slots item * 2 +
   // cascade, or -1 for none).
   bool mixed = false;
-  std::vector<int32_t> mix_table, mix_bundles;
-  // tree masks, one per row, present only when some sequence is a tree
-  std::vector<uint64_t> row_mask;
-  // cascade (shared-prefix) virtual sequences, their rows, and the record
-  // lists of the rows they merge into
-  std::vector<int32_t> cascade_lo, cascade_hi, cascade_seq, cascade_row_begin, cascade_rows,
-      cascade_splits, vrow_src, rec_index;
-  // KV append units; a non-empty message marks a target slot that another
-  // sequence can see (or two rows write): the append refuses such a plan
-  std::vector<pmattn_append_unit> append_units;
-  std::string append_conflict;
-  // workspace layout (bytes): [items | merge rows | row masks | append units |
-  // record index | virtual row sources | wave slots | task stream flags |
-  // mixed table | mixed bundles | partial O | partial lse]; everything before
-  // the partials is uploaded
+  // cascade (shared-prefix) virtual sequences
+  std::vector<int32_t> cascade_lo, cascade_hi, cascade_seq, cascade_row_begin, cascade_rows, cascade_splits;
+
+  // Upload image: bytes [0, off_upload_end) of the workspace, laid out as
+  // [items | merge rows | row masks | append units | record index | virtual
+  // row sources | wave slots | task stream flags | mixed table | mixed
+  // bundles]; the partial records follow it in the workspace (off_part_o,
+  // off_part_lse). The tables below are views into it.
+  std::unique_ptr<unsigned char[]> blob;
+  Table<pmattn_work_item> items;
+  Table<pmattn_merge_row> merge_rows;
+  Table<uint64_t> row_mask;  // tree masks, one per row; empty unless some sequence is a tree
+  Table<pmattn_append_unit> append_units;
+  Table<int32_t> rec_index, vrow_src;
+  // equal-work decode plans: wave w runs tasks [slot_begin[w], slot_begin[w + 1])
+  // of class slot_class; empty when every task is its own wave
+  Table<int32_t> slot_begin;
+  Table<int32_t> item_stream;
+  Table<int32_t> mix_table, mix_bundles;
   size_t off_items = 0, off_merge = 0, off_row_mask = 0, off_append = 0, off_rec_index = 0,
          off_vrow = 0, off_slot = 0, off_istream = 0, off_mix_table = 0, off_mix_bundles = 0,
          off_upload_end = 0, off_part_o = 0, off_part_lse = 0, ws_bytes = 0;
-  std::vector<unsigned char> upload_blob;  // bytes [0, off_part_o) of the workspace
+
+  // KV append check: empty, or why pmattn_kv_append must refuse this plan (a
+  // target slot that another sequence can see, or that two rows write)
+  std::string append_conflict;
+
+  // Row tables (row_seq, row_pos): built on first export from the per-sequence
+  // query starts and row offsets; nothing on the launch path reads them.
+  std::vector<int32_t> seq_q_start, seq_row_off;
+  std::once_flag rows_once;
+  std::vector<int32_t> row_seq, row_pos;
 };
 
 // thread-local error message helpers (plan.cpp)
