@@ -151,14 +151,11 @@ def plan(q_len, seq_len, q_start, block_table, *, num_pool_blocks: int, num_q_he
         tp = _i32(tree_parent)
         if tp.shape != (rows,):
             raise ValueError("tree_parent needs one entry per query row")
-    d = L.PlanDesc(num_seqs=b, q_len=ql.ctypes.data, seq_len=sl.ctypes.data, q_start=qs.ctypes.data,
-                   block_table=bt.ctypes.data, bt_stride=int(bt.shape[1]),
-                   num_pool_blocks=int(num_pool_blocks), block_size=16,
-                   num_q_heads=int(num_q_heads), num_kv_heads=int(num_kv_heads),
-                   head_dim=int(head_dim), dtype=_dtype_code(dtype), scale=float(scale),
-                   num_kv_splits=int(num_kv_splits), num_cus=int(num_cus),
-                   work_shuffle_seed=int(work_shuffle_seed),
-                   tree_parent=tp.ctypes.data if tp is not None else None, cascade=int(cascade))
+    # (positional, in the field order of pmattn_plan_desc)
+    d = L.PlanDesc(b, ql.ctypes.data, sl.ctypes.data, qs.ctypes.data, bt.ctypes.data, int(bt.shape[1]),
+                   int(num_pool_blocks), 16, int(num_q_heads), int(num_kv_heads), int(head_dim),
+                   _dtype_code(dtype), float(scale), int(num_kv_splits), int(num_cus), int(work_shuffle_seed),
+                   tp.ctypes.data if tp is not None else None, int(cascade))
     h = ctypes.c_void_p()
     _check(L.load().pmattn_plan(ctypes.byref(d), ctypes.byref(h)))
     shape = dict(num_seqs=b, num_rows=rows, bt_stride=int(bt.shape[1]),

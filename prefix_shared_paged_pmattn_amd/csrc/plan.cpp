@@ -22,6 +22,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <new>
 #include <numeric>
 
@@ -132,8 +133,8 @@ void counting_order(const uint32_t* key, uint32_t n, size_t nkeys, std::vector<u
 // common array) to workgroup slots: slot i, which the hardware gives to XCD
 // i % kXcds, takes the next `per_wg` entries of that XCD's queue, topped up
 // from the queue with the most entries left once that one runs out (so that
-// every slot but the last holds exactly per_wg entries). emit(e) receives
-// each entry's index in the common array, in dispatch order.
+// every slot but the last holds exactly per_wg entries). emit(x, e) receives
+// each entry's queue and its index in the common array, in dispatch order.
 template <typename Emit>
 void deal(const size_t* beg, const size_t* end, int per_wg, Emit&& emit) {
   size_t head[kXcds], total = 0, done = 0;
@@ -143,13 +144,17 @@ void deal(const size_t* beg, const size_t* end, int per_wg, Emit&& emit) {
   }
   for (size_t slot = 0; done < total; ++slot) {
     int x = (int)(slot % kXcds);
-    for (int k = 0; k < per_wg && done < total; ++k, ++done) {
+    for (size_t take = std::min<size_t>(per_wg, total - done); take > 0;) {
       if (head[x] == end[x]) {
         size_t best = 0;
         for (int y = 0; y < kXcds; ++y)
           if (end[y] - head[y] > best) best = end[y] - head[y], x = y;
       }
-      emit(head[x]++);
+      const size_t m = std::min(take, end[x] - head[x]);
+      for (size_t e = head[x]; e < head[x] + m; ++e) emit(x, e);
+      head[x] += m;
+      take -= m;
+      done += m;
     }
   }
 }
@@ -167,7 +172,11 @@ struct Tile {
 // One KV partition of one tile, clipped to the tile's keys: the tasks of the
 // tile's kv heads over these keys.
 struct Range {
-  int32_t tile, lo, hi, nblk;  // nblk: blocks' worth of keys, ceil((hi - lo) / 16)
+  int32_t tile, lo, hi;
+  int32_t nblk;  // blocks' worth of keys, ceil((hi - lo) / 16)
+  int32_t step;  // record offset between its kv heads' tasks (k * rows), if it has records
+  int32_t row;   // its block-table row
+  uint32_t seq;  // the sequence that sees its keys (kSeqMulti for a virtual tile)
 };
 
 // A task of a class before ordering: a range, a kv head and its XCD.
@@ -176,13 +185,19 @@ struct Cand {
   uint16_t g, x;
 };
 
-// Per pool block, valid while gen is the current plan's: the one row tile
-// reading it (or kMulti) and the range it reads it through, and the one
-// sequence that sees it (or kMulti).
-constexpr int32_t kMulti = -2;
+// A task in its class's XCD queue: its item index and KV blocks.
+struct QItem {
+  int32_t item, nblk;
+};
+
+// Per pool block, valid while gen is the current plan's. state, bit 31
+// clear: the block's one reader is range `state` (so its one reader tile is
+// that range's tile, and the sequence that sees it is that tile's, unless
+// the tile is virtual); bit 31 set: several tiles read it, and the low bits
+// name the one sequence that sees it, or kSeqMulti.
+constexpr uint32_t kMultiBit = 0x80000000u, kSeqMulti = 0x7FFFFFFFu;
 struct Mark {
-  uint32_t gen;
-  int32_t reader, seq, range;
+  uint32_t gen, state;
 };
 
 // A range's first block (start) or one past its last, along its table row.
@@ -228,18 +243,21 @@ struct Scratch {
   std::vector<uint64_t> row_mask, anc;
   std::vector<Listed> listed;
   std::vector<uint32_t> key, order, cnt, row_list, tile_first, tile_list;
-  std::vector<Cand> cand;
-  std::vector<int32_t> qitem;
+  std::vector<Cand> cand, queue, outc;
+  std::vector<pmattn_work_item> rtask;
+  std::vector<QItem> qitem;
+  std::vector<uint32_t> rlist;
   std::vector<char> rstream;
   std::vector<int32_t> rec_start, rec_fill, slot_first;
   std::vector<uint64_t> pairs;
-  std::vector<int32_t> mix_cat, mix_code;
+  std::vector<int32_t> mix_cat;
+  std::vector<QItem> mix_order;
   std::vector<MixEntry> mix_streams[4];
   std::vector<uint32_t> slot_key, slot_order;
   std::vector<int64_t> last_cost;
   std::vector<int32_t> unit_kind;
   std::vector<Event> events;
-  std::vector<uint32_t> active;
+  std::vector<uint32_t> active, active_slot;
   std::vector<Mark> marks;
   std::vector<uint32_t> tstamp;  // per pool block: the last plan that appends to it
   uint32_t gen = 0;
@@ -679,9 +697,14 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     t.range0 = (int32_t)ranges.size();
     for (int p = 0; p < usplits[u]; ++p) {
       const int32_t lo = ubeg[uoff[u] + p], hi = std::min(uend[uoff[u] + p], t.kv_end);
-      if (lo < hi) ranges.push_back(Range{(int32_t)ti, lo, hi, (hi - lo + kBlock - 1) / kBlock});
+      if (lo < hi) ranges.push_back(Range{(int32_t)ti, lo, hi, (hi - lo + kBlock - 1) / kBlock, 0, 0, 0});
     }
     t.k = (int32_t)ranges.size() - t.range0;
+    for (int32_t r = t.range0; r < t.range0 + t.k; ++r) {
+      ranges[r].step = t.k * t.n_tok * G;
+      ranges[r].row = unit_row(u);
+      ranges[r].seq = u < B ? (uint32_t)u : kSeqMulti;
+    }
     const bool virt = u >= B, listed = virt || member[u];
     t.row = unit_row(u);
     t.row0 = virt ? vseqs[u - B].row_begin + t.tok_begin : row_off[u] + t.tok_begin;
@@ -695,6 +718,15 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     cls_items[t.cls + (virt ? kNumClasses : 0)] += (int64_t)t.k * hkv;
     if (t.k > 1 && !listed) n_merge += hkv * trows;
     if (listed) n_rec_index += hkv * trows * t.k;
+  }
+  // each range's task, less its kv head: kv head g takes part + g * k * rows
+  std::vector<pmattn_work_item>& rtask = S.rtask;
+  rtask.resize(ranges.size());
+  for (size_t r = 0; r < ranges.size(); ++r) {
+    const Range& rg = ranges[r];
+    const Tile& t = tiles[rg.tile];
+    rtask[r] = pmattn_work_item{t.row, 0, t.row0, t.n_tok, t.pos0, rg.lo, rg.hi,
+                                t.rec0 < 0 ? -1 : (int32_t)(t.rec0 + (int64_t)(r - t.range0) * t.n_tok * G)};
   }
   std::vector<int32_t>& member_slot = S.member_slot;
   int32_t n_member_rows = 0;
@@ -817,22 +849,32 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       if (!lst && t.k > 1) P.merge_max_parts = std::max(P.merge_max_parts, t.k);
     }
     if (n_member_rows > 0) {
+      // key of (member row, q head): member_slot * Hq + head; each listed
+      // block adds its `parts` records to the keys of its rows
       const size_t keys = (size_t)n_member_rows * d->num_q_heads;
-      auto key_of = [&](const Listed& lb, int m) {
-        const int32_t row = lb.virt ? vrow[lb.row0 + m / G] : lb.row0 + m / G;
-        return (size_t)member_slot[row] * d->num_q_heads + lb.g * G + m % G;
+      auto row_key = [&](const Listed& lb, int tok) {  // key of the block's token row, head g * G
+        const int32_t row = lb.virt ? vrow[lb.row0 + tok] : lb.row0 + tok;
+        return (size_t)member_slot[row] * d->num_q_heads + (size_t)lb.g * G;
       };
       std::vector<int32_t>& start = S.rec_start;
       start.assign(keys + 1, 0);
       for (const Listed& lb : listed)
-        for (int m = 0; m < lb.trows; ++m) start[key_of(lb, m) + 1] += lb.parts;
+        for (int tok = 0, ntok = lb.trows / G; tok < ntok; ++tok) {
+          int32_t* c = start.data() + row_key(lb, tok) + 1;
+          for (int i = 0; i < G; ++i) c[i] += lb.parts;
+        }
       for (size_t k = 0; k < keys; ++k) start[k + 1] += start[k];
       std::vector<int32_t>& fill = S.rec_fill;
       fill.assign(start.begin(), start.end() - 1);
       for (const Listed& lb : listed)
-        for (int m = 0; m < lb.trows; ++m) {
-          int32_t& at = fill[key_of(lb, m)];
-          for (int p = 0; p < lb.parts; ++p) rec_index[at++] = (int32_t)(lb.rec_base + (int64_t)p * lb.trows + m);
+        for (int tok = 0, ntok = lb.trows / G; tok < ntok; ++tok) {
+          int32_t* at = fill.data() + row_key(lb, tok);
+          const int64_t rec = lb.rec_base + (int64_t)tok * G;  // record of (part 0, token tok, head 0)
+          for (int i = 0; i < G; ++i) {
+            int32_t* out = rec_index + at[i];
+            for (int p = 0; p < lb.parts; ++p) out[p] = (int32_t)(rec + (int64_t)p * lb.trows + i);
+            at[i] += lb.parts;
+          }
         }
       for (int s = 0; s < B; ++s)
         if (member[s])
@@ -867,11 +909,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // whose blocks are shared in pairs, 69.5% -> 63.4% had all of it streamed.)
   std::vector<Mark>& marks = S.marks;
   if (marks.size() < (size_t)d->num_pool_blocks) {
-    marks.resize(d->num_pool_blocks, Mark{0, 0, 0, 0});
+    marks.resize(d->num_pool_blocks, Mark{0, 0});
     S.tstamp.resize(d->num_pool_blocks, 0);
   }
   if (++S.gen == 0) {
-    std::fill(marks.begin(), marks.end(), Mark{0, 0, 0, 0});
+    std::fill(marks.begin(), marks.end(), Mark{0, 0});
     std::fill(S.tstamp.begin(), S.tstamp.end(), 0u);
     S.gen = 1;
   }
@@ -879,15 +921,18 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   const uint32_t nranges = (uint32_t)ranges.size();
   std::vector<char>& rstream = S.rstream;
   rstream.assign(nranges, 1);
+  auto seq_of_range = [&](uint32_t r) { return ranges[r].seq; };
   {
     std::vector<uint32_t>& rkey = S.key;
     std::vector<uint32_t>& rorder = S.row_list;
     rkey.resize(nranges);
     rorder.resize(nranges);
-    for (uint32_t r = 0; r < nranges; ++r) rkey[r] = (uint32_t)unit_row(tiles[ranges[r].tile].seq);
+    for (uint32_t r = 0; r < nranges; ++r) rkey[r] = (uint32_t)ranges[r].row;
     counting_order(rkey.data(), nranges, (size_t)B, S.cnt, rorder.data());
     std::vector<Event>& ev = S.events;
-    std::vector<uint32_t>& active = S.active;
+    std::vector<uint32_t>& active = S.active;  // the ranges over the current position
+    std::vector<uint32_t>& slot_of = S.active_slot;  // a range's index in active
+    slot_of.resize(nranges);
     for (uint32_t a = 0, e; a < nranges; a = e) {
       const int s = (int)rkey[rorder[a]];
       ev.clear();
@@ -911,50 +956,63 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
         const int32_t p = ev[i].pos;
         for (; i < ev.size() && ev[i].pos == p; ++i) {
           const Event& x = ev[i];
-          const bool virt = tiles[ranges[x.range].tile].seq >= B;
+          const bool virt = ranges[x.range].seq == kSeqMulti;
           if (x.start) {
+            // every range under a segment of two or more reads shared blocks
+            // (the ranges that end here have left already)
+            slot_of[x.range] = (uint32_t)active.size();
             active.push_back(x.range);
+            if (active.size() >= 2) {
+              rstream[x.range] = 0;
+              rstream[active[0]] = 0;
+            }
             nvirt += virt;
           } else {
-            active.erase(std::find(active.begin(), active.end(), x.range));
+            const uint32_t at = slot_of[x.range], last = active.back();
+            active[at] = last;
+            slot_of[last] = at;
+            active.pop_back();
             nvirt -= virt;
           }
         }
         if (active.empty() || i == ev.size()) continue;
         const int32_t q = ev[i].pos;  // the segment is [p, q)
-        const int32_t who = nvirt ? kMulti : s;
+        const uint32_t who = nvirt ? kSeqMulti : (uint32_t)s;
+        // a block read so far by range `st` alone: it is shared now
+        auto to_multi = [&](Mark& m, uint32_t st) {
+          rstream[st] = 0;
+          m.state = kMultiBit | (seq_of_range(st) == who ? who : kSeqMulti);
+        };
         if (active.size() == 1) {
-          const int32_t rid = (int32_t)active[0], tile = ranges[rid].tile;
+          const uint32_t rid = active[0];
+          const int32_t tile = ranges[rid].tile;
           bool shared = false;
           for (int32_t j = p; j < q; ++j) {
             Mark& m = marks[row[j]];
             if (m.gen != gen) {
-              m = Mark{gen, tile, who, rid};
+              m = Mark{gen, rid};
               continue;
             }
-            if (m.reader != tile) {
-              if (m.reader != kMulti) {
-                rstream[m.range] = 0;
-                m.reader = kMulti;
-              }
-              shared = true;
+            const uint32_t st = m.state;
+            if (!(st & kMultiBit)) {
+              if (ranges[st].tile == tile) continue;  // the same reader
+              to_multi(m, st);
+            } else if ((st & kSeqMulti) != who) {
+              m.state = kMultiBit | kSeqMulti;
             }
-            if (m.seq != who && m.seq != kMulti) m.seq = kMulti;
+            shared = true;
           }
           if (shared) rstream[rid] = 0;
         } else {
-          for (uint32_t id : active) rstream[id] = 0;
           for (int32_t j = p; j < q; ++j) {
             Mark& m = marks[row[j]];
             if (m.gen != gen) {
-              m = Mark{gen, kMulti, who, -1};
+              m = Mark{gen, kMultiBit | who};
               continue;
             }
-            if (m.reader != kMulti) {
-              rstream[m.range] = 0;
-              m.reader = kMulti;
-            }
-            if (m.seq != who && m.seq != kMulti) m.seq = kMulti;
+            const uint32_t st = m.state;
+            if (!(st & kMultiBit)) to_multi(m, st);
+            else if ((st & kSeqMulti) != who) m.state = kMultiBit | kSeqMulti;
           }
         }
       }
@@ -967,7 +1025,8 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     bool exact = false;
     for (const Target& t : S.targets) {
       const Mark& m = marks[t.blk];
-      exact = exact || S.tstamp[t.blk] == gen || m.gen != gen || m.seq != t.seq;
+      exact = exact || S.tstamp[t.blk] == gen || m.gen != gen ||
+              (m.state & kMultiBit ? m.state & kSeqMulti : seq_of_range(m.state)) != (uint32_t)t.seq;
       S.tstamp[t.blk] = gen;
     }
     P.append_conflict = exact ? exact_append_check(d, S.targets) : std::string();
@@ -992,12 +1051,14 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     for (size_t i = 0; i < tiles.size(); ++i) ++tile_first[tkey[i] + 1];
     for (int c = 0; c < 2 * kNumClasses; ++c) tile_first[c + 1] += tile_first[c];
   }
-  std::vector<Cand>& cand = S.cand;  // a class's tasks in generation order
+  std::vector<Cand>& cand = S.cand;  // (equal-work decode) the class's tasks in generation order
+  std::vector<Cand>& queue = S.queue;  // the class's tasks, per XCD, in queue order
+  std::vector<Cand>& outc = S.outc;    // ... and in dispatch order (when shuffled)
   std::vector<uint32_t>& key = S.key;
   std::vector<uint32_t>& order = S.order;
   // per class and XCD, the class's tasks in queue order (largest first), as
-  // item indices: qitem[class_begin + [qseg[c][x], qseg[c][x + 1]) )
-  std::vector<int32_t>& qitem = S.qitem;
+  // item indices and KV blocks: qitem[class_begin + [qseg[c][x], qseg[c][x + 1]) )
+  std::vector<QItem>& qitem = S.qitem;
   qitem.resize(n_items);
   size_t qseg[2 * kNumClasses][kXcds + 1] = {};
   int64_t pos = 0;
@@ -1006,37 +1067,16 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   for (int c = 0, ci = 0; c < 2 * kNumClasses; ++c) {
     if (!cls_items[c]) continue;
     const uint32_t n = (uint32_t)cls_items[c];
-    cand.resize(n);
-    key.resize(n);
-    order.resize(2 * (size_t)n);
-    uint32_t* out = order.data() + n;
-    uint32_t i = 0, maxb = 0;
-    for (uint32_t k = tile_first[c]; k < tile_first[c + 1]; ++k) {
-      const Tile& t = tiles[tile_list[k]];
-      const uint32_t xo = (uint32_t)(unit_row(t.seq) % rep);
-      for (int g = 0; g < hkv; ++g) {
-        const uint32_t x = ((uint32_t)g * rep + xo) % kXcds;
-        for (int32_t r = t.range0; r < t.range0 + t.k; ++r) cand[i++] = Cand{(uint32_t)r, (uint16_t)g, (uint16_t)x};
-      }
-      for (int32_t r = t.range0; r < t.range0 + t.k; ++r) maxb = std::max(maxb, (uint32_t)ranges[r].nblk);
-    }
-    // writes task `ci` of the class at item index `at` (in dispatch order
-    // directly, or after the shuffle)
+    outc.resize(n);
+    // writes a task at item index `at` (in dispatch order directly, or after
+    // the shuffle)
     int32_t nstream = 0;
     const bool direct = !d->work_shuffle_seed;
-    auto emit = [&](int64_t at, uint32_t ci) {
-      const Cand& cd = cand[ci];
-      const Range& rg = ranges[cd.range];
-      const Tile& t = tiles[rg.tile];
-      pmattn_work_item& it = items[at];
-      it.seq = t.row;
+    auto emit = [&](int64_t at, const Cand& cd) {
+      pmattn_work_item it = rtask[cd.range];
       it.kv_head = cd.g;
-      it.row_begin = t.row0;
-      it.n_tok = t.n_tok;
-      it.pos_begin = t.pos0;
-      it.kv_begin = rg.lo;
-      it.kv_end = rg.hi;
-      it.part = t.rec0 < 0 ? -1 : (int32_t)(t.rec0 + ((int64_t)cd.g * t.k + (cd.range - t.range0)) * t.n_tok * G);
+      if (it.part >= 0) it.part += cd.g * ranges[cd.range].step;
+      items[at] = it;
       nstream += item_stream[at] = rstream[cd.range];
     };
     uint32_t nout = 0;
@@ -1047,6 +1087,15 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       // the first block tells the piece). Slots go to XCDs like tasks (kv head
       // g on XCD g; with fewer than kXcds heads, piece j of head g on XCD
       // g * rep + j % rep), four per workgroup.
+      cand.resize(n);
+      key.resize(n);
+      order.resize(n);
+      uint32_t i = 0;
+      for (uint32_t k = tile_first[c]; k < tile_first[c + 1]; ++k) {
+        const Tile& t = tiles[tile_list[k]];
+        for (int g = 0; g < hkv; ++g)
+          for (int32_t r = t.range0; r < t.range0 + t.k; ++r) cand[i++] = Cand{(uint32_t)r, (uint16_t)g, 0};
+      }
       for (uint32_t k = 0; k < n; ++k) {
         const Range& r = ranges[cand[k].range];
         const int u = tiles[r.tile].seq;
@@ -1074,39 +1123,87 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       }
       slot_begin[0] = 0;
       int64_t w = 0;
-      deal(qb, qe, kWaveTasksPerWg, [&](size_t e) {
+      deal(qb, qe, kWaveTasksPerWg, [&](int, size_t e) {
         const uint32_t q = qorder[e];
         for (int32_t k = sfirst[q]; k < sfirst[q + 1]; ++k) {
-          if (direct) emit(pos + nout, byslot[k]);
-          out[nout++] = byslot[k];
+          if (direct) emit(pos + nout, cand[byslot[k]]);
+          else outc[nout] = cand[byslot[k]];
+          ++nout;
         }
         slot_begin[++w] = (int32_t)nout;
       });
       P.slot_class = ci;
     } else {
-      const uint32_t nb = maxb + 1;
-      size_t* qs = qseg[c];
+      // The class's ranges largest first, ties in generation order; each
+      // kv head's tasks then follow that order on their XCD. Within a run of
+      // one tile's ranges of equal size, heads come before partitions, as in
+      // generation order (tile, kv head, partition).
+      const uint32_t nr = (uint32_t)(n / hkv);
+      uint32_t maxb = 0;
+      std::vector<uint32_t>& rlist = S.rlist;
+      rlist.resize(nr);
+      key.resize(nr);
+      order.resize(nr);
       size_t qb[kXcds], qe[kXcds] = {};
-      for (uint32_t k = 0; k < n; ++k) {
-        key[k] = cand[k].x * nb + (maxb - (uint32_t)ranges[cand[k].range].nblk);
-        ++qe[cand[k].x];
+      uint32_t i = 0;
+      for (uint32_t k = tile_first[c]; k < tile_first[c + 1]; ++k) {
+        const Tile& t = tiles[tile_list[k]];
+        for (int32_t r = t.range0; r < t.range0 + t.k; ++r) {
+          rlist[i++] = (uint32_t)r;
+          maxb = std::max(maxb, (uint32_t)ranges[r].nblk);
+        }
+        const uint32_t xo = (uint32_t)(t.row % rep);
+        for (int g = 0; g < hkv; ++g) qe[((uint32_t)g * rep + xo) % kXcds] += t.k;
       }
-      uint32_t* sorted = order.data();
-      counting_order(key.data(), n, (size_t)kXcds * nb, S.cnt, sorted);
+      for (uint32_t k = 0; k < nr; ++k) key[k] = maxb - (uint32_t)ranges[rlist[k]].nblk;
+      counting_order(key.data(), nr, (size_t)maxb + 1, S.cnt, order.data());
+      size_t* qs = qseg[c];
+      size_t fillp[kXcds];
       for (size_t x = 0, acc = 0; x < kXcds; ++x) {
-        qs[x] = qb[x] = acc;
+        qs[x] = qb[x] = fillp[x] = acc;
         qs[x + 1] = qe[x] = acc += qe[x];
       }
-      int32_t* qi = qitem.data() + pos;
-      deal(qb, qe, kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1, [&](size_t e) {
-        qi[e] = (int32_t)(pos + nout);
-        if (direct) emit(pos + nout, sorted[e]);
-        out[nout++] = sorted[e];
-      });
+      const int per_wg = kClassRows[c % kNumClasses] <= kMaxWaveRows ? kWaveTasksPerWg : 1;
+      QItem* qi = qitem.data() + pos;
+      if (hkv == kXcds) {
+        // one kv head per XCD: every queue is the sorted range list
+        std::vector<uint32_t>& srt = S.slot_key;
+        srt.resize(nr);
+        for (uint32_t k = 0; k < nr; ++k) srt[k] = rlist[order[k]];
+        deal(qb, qe, per_wg, [&](int x, size_t e) {
+          const uint32_t r = srt[e - qb[x]];
+          if (P.mixed) qi[e] = QItem{(int32_t)(pos + nout), ranges[r].nblk};
+          const Cand cd{r, (uint16_t)x, (uint16_t)x};
+          if (direct) emit(pos + nout, cd);
+          else outc[nout] = cd;
+          ++nout;
+        });
+      } else {
+        queue.resize(n);
+        for (uint32_t a = 0, e; a < nr; a = e) {
+          const Range& ra = ranges[rlist[order[a]]];
+          for (e = a + 1; e < nr; ++e) {
+            const Range& rb = ranges[rlist[order[e]]];
+            if (rb.tile != ra.tile || rb.nblk != ra.nblk) break;
+          }
+          const uint32_t xo = (uint32_t)(tiles[ra.tile].row % rep);
+          for (int g = 0; g < hkv; ++g) {
+            const uint32_t x = ((uint32_t)g * rep + xo) % kXcds;
+            for (uint32_t k = a; k < e; ++k) queue[fillp[x]++] = Cand{rlist[order[k]], (uint16_t)g, (uint16_t)x};
+          }
+        }
+        deal(qb, qe, per_wg, [&](int, size_t e) {
+          const Cand& cd = queue[e];
+          if (P.mixed) qi[e] = QItem{(int32_t)(pos + nout), ranges[cd.range].nblk};
+          if (direct) emit(pos + nout, cd);
+          else outc[nout] = cd;
+          ++nout;
+        });
+      }
     }
-    if (d->work_shuffle_seed) {
-      shuffle(out, n, rng);
-      for (uint32_t k = 0; k < n; ++k) emit(pos + k, out[k]);
+    if (!direct) {
+      shuffle(outc.data(), n, rng);
+      for (uint32_t k = 0; k < n; ++k) emit(pos + k, outc[k]);
     }
     P.class_stream.push_back(nstream == (int32_t)n ? 1 : nstream == 0 ? 0 : 2);
     pos += n;
@@ -1131,14 +1228,14 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     // kMix*BlockCost (a bundle lasts as long as its longest task)
     static constexpr int64_t per_block[4] = {kMixTileBlockCost, kMixSmallTaskBlockCost, kMixWaveBlockCost,
                                              kMixWave32BlockCost};
-    auto nblk_of = [&](int32_t i) { return (items[i].kv_end - items[i].kv_begin + kBlock - 1) / kBlock; };
+    auto nblk_of = [&](uint32_t i) { return (items[i].kv_end - items[i].kv_begin + kBlock - 1) / kBlock; };
     int64_t casc_from = 0;  // cascade classes come after the plain ones
     for (int c = 0; c < kNumClasses; ++c) casc_from += cls_items[c];
     auto is_cascade = [&](int32_t i) { return i >= casc_from ? 1 : 0; };
     // Per stream k and XCD x, the tasks largest first, ties in plan order:
-    // mord[seg[k * kXcds + x], seg[k * kXcds + x + 1]), as item indices.
+    // mord[seg[k * kXcds + x], seg[k * kXcds + x + 1]).
     const uint32_t n = (uint32_t)n_items;
-    std::vector<int32_t>& mord = S.mix_code;
+    std::vector<QItem>& mord = S.mix_order;
     mord.resize(n);
     size_t seg[4 * kXcds + 1] = {};
     int cls_of_kind[4][2] = {{-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}};  // (plain, cascade) class index
@@ -1152,18 +1249,18 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       for (int k = 0; k < 4; ++k)
         for (int x = 0; x < kXcds; ++x) {
           seg[k * kXcds + x] = w;
-          const int32_t *a = nullptr, *ae = nullptr, *b = nullptr, *be = nullptr;
+          const QItem *a = nullptr, *ae = nullptr, *b = nullptr, *be = nullptr;
           for (int h = 0; h < 2; ++h) {
             const int c = cls_of_kind[k][h];
             if (c < 0) continue;
             int64_t base = 0;
             for (int cc = 0; cc < c; ++cc) base += cls_items[cc];
-            const int32_t* lo = qitem.data() + base + qseg[c][x];
-            const int32_t* hi = qitem.data() + base + qseg[c][x + 1];
+            const QItem* lo = qitem.data() + base + qseg[c][x];
+            const QItem* hi = qitem.data() + base + qseg[c][x + 1];
             if (h == 0) a = lo, ae = hi;
             else b = lo, be = hi;
           }
-          while (a != ae && b != be) mord[w++] = nblk_of(*b) > nblk_of(*a) ? *b++ : *a++;
+          while (a != ae && b != be) mord[w++] = b->nblk > a->nblk ? *b++ : *a++;
           while (a != ae) mord[w++] = *a++;
           while (b != be) mord[w++] = *b++;
         }
@@ -1185,7 +1282,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       }
       counting_order(key.data(), n, (size_t)4 * kXcds * nb, S.cnt, order.data());
       for (int k = 0; k < 4 * kXcds; ++k) seg[k + 1] += seg[k];
-      for (uint32_t i = 0; i < n; ++i) mord[i] = (int32_t)order[i];
+      for (uint32_t i = 0; i < n; ++i) mord[i] = QItem{(int32_t)order[i], nblk_of(order[i])};
     }
     std::vector<MixEntry>* streams = S.mix_streams;
     std::vector<int32_t>& cat = S.mix_cat;  // the XCDs' lists, end to end
@@ -1194,20 +1291,22 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     int32_t nbund = 0;
     for (int x = 0; x < kXcds; ++x) {
       for (int k = 0; k < 4; ++k) {
-        int32_t* v = mord.data() + seg[k * kXcds + x];
+        QItem* v = mord.data() + seg[k * kXcds + x];
         const size_t m = seg[k * kXcds + x + 1] - seg[k * kXcds + x];
         if (d->work_shuffle_seed) shuffle(v, m, rng);
-        streams[k].clear();
+        streams[k].resize(k < 2 ? m : (m + kWaveTasksPerWg - 1) / kWaveTasksPerWg);
+        MixEntry* st = streams[k].data();
         if (k < 2) {
           for (size_t j = 0; j < m; ++j)
-            streams[k].push_back(MixEntry{nblk_of(v[j]) * per_block[k], 4 * v[j] + 2 * is_cascade(v[j])});
+            st[j] = MixEntry{v[j].nblk * per_block[k], 4 * v[j].item + 2 * is_cascade(v[j].item)};
           continue;
         }
         // bundles of four wave tasks of neighbouring cost
         for (size_t j = 0; j < m; j += kWaveTasksPerWg) {
+          int32_t* slot = mix_bundles + (size_t)nbund * kWaveTasksPerWg;
           for (size_t q = j; q < j + kWaveTasksPerWg; ++q)
-            mix_bundles[nbund * kWaveTasksPerWg + (q - j)] = q < m ? 2 * v[q] + is_cascade(v[q]) : -1;
-          streams[k].push_back(MixEntry{nblk_of(v[j]) * per_block[k], 4 * nbund + 1});  // the bundle's longest task
+            slot[q - j] = q < m ? 2 * v[q].item + is_cascade(v[q].item) : -1;
+          st[j / kWaveTasksPerWg] = MixEntry{v[j].nblk * per_block[k], 4 * nbund + 1};  // the bundle's longest task
           ++nbund;
         }
       }
@@ -1225,25 +1324,46 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       size_t h[4] = {0, 0, 0, 0};
       for (int k = 0; k < 4; ++k)
         for (const MixEntry& en : streams[k]) tot[k] += en.cost;
+      // the share a stream has used, as a double: exact for the comparisons
+      // while every total stays below 2^26 (two different shares then differ
+      // by more than the rounding of either); larger totals compare exactly
+      const bool exact = std::max(std::max(tot[0], tot[1]), std::max(tot[2], tot[3])) >= (int64_t)1 << 26;
+      const double inf = std::numeric_limits<double>::infinity();
+      double share[4];
+      for (int k = 0; k < 4; ++k) share[k] = streams[k].empty() ? inf : 0.0;
       for (;;) {
-        int k = -1;
-        for (int j = 0; j < 4; ++j) {
-          if (h[j] == streams[j].size()) continue;
-          if (k < 0 || (__int128)used[j] * tot[k] < (__int128)used[k] * tot[j]) k = j;
+        int k = 0;
+        if (!exact) {
+          double best = share[0];
+          for (int j = 1; j < 4; ++j) {
+            const bool lt = share[j] < best;
+            best = lt ? share[j] : best;
+            k = lt ? j : k;
+          }
+          if (best == inf) break;
+        } else {
+          k = -1;
+          for (int j = 0; j < 4; ++j) {
+            if (h[j] == streams[j].size()) continue;
+            if (k < 0 || (__int128)used[j] * tot[k] < (__int128)used[k] * tot[j]) k = j;
+          }
+          if (k < 0) break;
         }
-        if (k < 0) break;
-        for (int g = 0; g < kSeRoundRobin && h[k] < streams[k].size(); ++g) {
-          const MixEntry& en = streams[k][h[k]++];
-          used[k] += en.cost;
-          cat.push_back(en.e);
+        const size_t m = std::min<size_t>(kSeRoundRobin, streams[k].size() - h[k]);
+        const MixEntry* en = streams[k].data() + h[k];
+        for (size_t g = 0; g < m; ++g) {
+          used[k] += en[g].cost;
+          cat.push_back(en[g].e);
         }
+        h[k] += m;
+        share[k] = h[k] == streams[k].size() ? inf : (double)used[k] / (double)tot[k];
       }
       le[x] = cat.size();
     }
     // workgroup i runs on XCD i % kXcds; an XCD whose list ran out is
     // topped up from the one with the most entries left
     int64_t nt = 0;
-    deal(lb, le, 1, [&](size_t e) { mix_table[nt++] = cat[e]; });
+    deal(lb, le, 1, [&](int, size_t e) { mix_table[nt++] = cat[e]; });
   }
 
   P.id = g_next_plan_id.fetch_add(1);
