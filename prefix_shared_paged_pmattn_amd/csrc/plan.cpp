@@ -251,7 +251,9 @@ struct Scratch {
   std::vector<int32_t> rec_start, rec_fill, slot_first;
   std::vector<uint64_t> pairs;
   std::vector<int32_t> mix_cat;
-  std::vector<QItem> mix_order;
+  std::vector<QItem> mix_order, gtmp;
+  std::vector<int32_t> group_of;
+  std::vector<uint32_t> gkey, gorder;
   std::vector<MixEntry> mix_streams[4];
   std::vector<uint32_t> slot_key, slot_order;
   std::vector<int64_t> last_cost;
@@ -1294,6 +1296,32 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
         QItem* v = mord.data() + seg[k * kXcds + x];
         const size_t m = seg[k * kXcds + x + 1] - seg[k * kXcds + x];
         if (d->work_shuffle_seed) shuffle(v, m, rng);
+        if (k == 0 && m > 1) {
+          // The tiles of one sequence side by side (its kv head's tiles are
+          // all on this XCD), so that they run at the same time and read its
+          // keys once into the L2; sequences in the order of their largest
+          // tile. (Measured on MI355X, mixed-chunk batch: in cost order the
+          // tiles of one prompt spread over a third of the XCD's entries,
+          // and the kernel fetched 3.34 GB beyond the L2 for 2.16 GB of
+          // distinct keys.)
+          std::vector<int32_t>& gid = S.group_of;  // -1 outside this block
+          if (gid.size() < (size_t)B) gid.resize(B, -1);
+          std::vector<uint32_t>& gkey = S.gkey;
+          std::vector<uint32_t>& gord = S.gorder;
+          std::vector<QItem>& tmp = S.gtmp;
+          gkey.resize(m);
+          gord.resize(m);
+          uint32_t ng = 0;
+          for (size_t j = 0; j < m; ++j) {
+            int32_t& g = gid[items[v[j].item].seq];
+            if (g < 0) g = (int32_t)ng++;
+            gkey[j] = (uint32_t)g;
+          }
+          counting_order(gkey.data(), (uint32_t)m, ng, S.cnt, gord.data());
+          tmp.assign(v, v + m);
+          for (size_t j = 0; j < m; ++j) v[j] = tmp[gord[j]];
+          for (size_t j = 0; j < m; ++j) gid[items[v[j].item].seq] = -1;
+        }
         streams[k].resize(k < 2 ? m : (m + kWaveTasksPerWg - 1) / kWaveTasksPerWg);
         MixEntry* st = streams[k].data();
         if (k < 2) {
