@@ -31,28 +31,37 @@ WG_TASKS_PER_2CU = 2       # 1 workgroup task per CU ...
 WG_TASKS_PER_2CU_TREE = 3  # ... 1.5 when the plan holds a token tree
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
-STREAM_WAVES_PER_CU = 3
+STREAM_WAVES_PER_CU = 3     # equal-work plans of 16-row tasks ...
+STREAM_WAVES_PER_CU_32 = 4  # ... and of 32-row tasks
 STREAM_MIN_BLOCKS = 16
 
 
 def stream_applies(q_len, group, dtype="bf16", num_kv_splits=0, virtual_units=0):
-    """Equal-work decode plans: bf16, automatic splits, no cascade group, and
-    every sequence with rows a single 16-row tile (q_len * G <= 16)."""
+    """Equal-work plans: bf16, automatic splits, no cascade group, and every
+    sequence with rows a single wave task of one class: all 16-row tiles
+    (q_len * G <= 16) or all 32-row tiles (16 < q_len * G <= 32)."""
     q_len = np.asarray(q_len, np.int64)
-    return (dtype == "bf16" and num_kv_splits == 0 and virtual_units == 0 and bool((q_len > 0).any())
-            and bool((q_len[q_len > 0] * group <= CLASS_ROWS[0]).all()))
+    r = q_len[q_len > 0] * group
+    return (dtype == "bf16" and num_kv_splits == 0 and virtual_units == 0 and r.size > 0
+            and (bool((r <= CLASS_ROWS[0]).all()) or bool(((r > CLASS_ROWS[0]) & (r <= CLASS_ROWS[1])).all())))
 
 
-def stream_bounds(lo, hi, rows, num_kv_heads, num_cus=0):
+def stream_waves_per_cu(q_len, group):
+    """Waves per CU of an equal-work plan: by the class of its tasks."""
+    q_len = np.asarray(q_len, np.int64)
+    return STREAM_WAVES_PER_CU if int(q_len.max()) * group <= CLASS_ROWS[0] else STREAM_WAVES_PER_CU_32
+
+
+def stream_bounds(lo, hi, rows, num_kv_heads, num_cus=0, waves_per_cu=STREAM_WAVES_PER_CU):
     """Partition bounds of every unit (key ranges [lo, hi), ``rows`` > 0 for
-    units with work) in an equal-work decode plan. The units' blocks are laid
-    end to end in unit order; pieces of L blocks, L = max(16, ceil(total /
-    (CUs x 3 / Hkv))), cut them; a unit's partitions are its parts of the
+    units with work) in an equal-work plan. The units' blocks are laid end to
+    end in unit order; pieces of L blocks, L = max(16, ceil(total / (CUs x
+    waves_per_cu / Hkv))), cut them; a unit's partitions are its parts of the
     pieces it meets. Returns one list of (begin, end) per unit."""
     nblk = [-(-(int(h) - int(l)) // BLOCK) if r > 0 else 0 for l, h, r in zip(lo, hi, rows)]
     total = sum(nblk)
     cus = num_cus if num_cus > 0 else 256
-    per_head = max(1, cus * STREAM_WAVES_PER_CU // num_kv_heads)
+    per_head = max(1, cus * waves_per_cu // num_kv_heads)
     L = max(STREAM_MIN_BLOCKS, -(-total // per_head))
     out, start = [], 0
     for l, h, n in zip(lo, hi, nblk):
@@ -195,7 +204,8 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0, 
         out[q_len > 0] = num_kv_splits
         return out
     if stream_applies(q_len, group, dtype):
-        bounds = stream_bounds(np.zeros_like(q_start), q_start + q_len, q_len, num_kv_heads, num_cus)
+        bounds = stream_bounds(np.zeros_like(q_start), q_start + q_len, q_len, num_kv_heads, num_cus,
+                               stream_waves_per_cu(q_len, group))
         return np.array([len(b) for b in bounds], np.int32)
     total = [0, 0]
     last = np.zeros(q_len.shape[0], np.int64)
@@ -225,7 +235,8 @@ def seq_bounds(q_len, q_start, num_kv_heads, group, splits, num_cus=0, dtype="bf
     q_start = np.asarray(q_start, np.int64)
     if stream_applies(q_len, group, dtype, num_kv_splits):
         return [np.array(b, np.int64).reshape(-1, 2)
-                for b in stream_bounds(np.zeros_like(q_start), q_start + q_len, q_len, num_kv_heads, num_cus)]
+                for b in stream_bounds(np.zeros_like(q_start), q_start + q_len, q_len, num_kv_heads, num_cus,
+                                       stream_waves_per_cu(q_len, group))]
     return [partition_bounds(int(q_start[s] + q_len[s]), int(p)) if p else np.zeros((0, 2), np.int64)
             for s, p in enumerate(splits)]
 
@@ -403,7 +414,7 @@ def plan_units(q_len, q_start, block_table, num_kv_heads, group, num_kv_splits=0
     stream = stream_applies(q_len, group, dtype, num_kv_splits, len(groups))
     if stream:
         sb = stream_bounds([u["lo"] for u in units], [u["hi"] for u in units], [u["rows"] for u in units],
-                           num_kv_heads, num_cus)
+                           num_kv_heads, num_cus, stream_waves_per_cu(q_len, group))
         for u, b in zip(units, sb):
             u["splits"], u["bounds"] = len(b), b
     elif num_kv_splits > 0:

@@ -12,10 +12,10 @@ namespace {
 // planner's dispatch order groups tasks by this count.
 constexpr int kWavesPerWg = kWaveTasksPerWg;
 
-// Wave w of the launch runs task w, or, with a slot table (equal-work decode
-// plans, 16-row tasks only), its tasks [slot_begin[w], slot_begin[w + 1]) one
-// after another. (The loop stays out of the larger tiles, whose 64-row
-// variant it pushes into spilling.)
+// Wave w of the launch runs task w, or, with a slot table (equal-work plans
+// of 16- or 32-row tasks), its tasks [slot_begin[w], slot_begin[w + 1]) one
+// after another. (The loop stays out of the 64-row tiles, which it pushes
+// into spilling.)
 // SMODE 0: cached K/V loads, 1: non-temporal, 2: the task's item_stream flag
 // decides (a uniform branch between the two bodies).
 template <int D, int NT, bool TREE, bool CONC, int SMODE>
@@ -34,7 +34,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWavesPerWg + wave;
-  if constexpr (NT != 1) {
+  if constexpr (NT > 2) {
     if (w < a.item_count) run_one<D, NT, TREE, CONC, SMODE>(a, w, lane);
     return;
   }
@@ -57,7 +57,7 @@ void attn_bf16_kernel(AttnArgs a) {
 hipError_t launch_attn_bf16(int head_dim, int class_rows, const AttnArgs& a, bool concurrent, int stream,
                             hipStream_t st) {
   if (a.item_count <= 0) return hipSuccess;
-  const int waves = a.slot_begin && class_rows <= 16 ? a.slot_count : a.item_count;
+  const int waves = a.slot_begin && class_rows <= 32 ? a.slot_count : a.item_count;
   const dim3 grid((waves + kWavesPerWg - 1) / kWavesPerWg), block(64 * kWavesPerWg);
 #define PMATTN_LAUNCH(D, NT, CONC, SMODE)                                                            \
   do {                                                                                              \

@@ -62,6 +62,13 @@ constexpr int64_t kWgTasksPer2CuTree = 3;
 // 0.92, 0.79 ms against 0.78; shared-prompt cascade 0.173, 0.130, 0.127
 // against 0.125 ms).
 constexpr int64_t kStreamWavesPerCu = 3;
+// The same plan serves a batch whose tasks are all 17..32-row wave tasks
+// (verify drafts), with kStreamWavesPerCu32 waves per CU (measured on
+// MI355X, the 32 verify drafts of the mixed-chunk batch alone, % of HBM
+// peak over the step: one task per wave 50.3; equal work at 3 waves per CU
+// 59.5, 4: 61.7-61.9, 6: 53.7, 8: 58.3; double-buffered at one wave per
+// SIMD 58.3).
+constexpr int64_t kStreamWavesPerCu32 = 4;
 constexpr int64_t kStreamMinBlocks = 16;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;
@@ -612,21 +619,23 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       usplits[u] = (int32_t)std::max<int64_t>(1, p);
     }
   }
-  // Equal-work decode (stream) partitions of the decode units: real sequences
-  // whose rows make one 16-row wave task. Laid end to end in unit order, unit
-  // u holds blocks [S_u, S_u + n_u) of the concatenation; cut it into pieces of
-  // L blocks; a unit's partitions are its parts of the pieces it meets, and
-  // piece j of kv head g is the work of one wave.
+  // Equal-work (stream) partitions when every unit is a real sequence whose
+  // rows make one wave task of the same class, 16 rows (decode) or 32 rows
+  // (verify). Laid end to end in unit order, unit u holds blocks
+  // [S_u, S_u + n_u) of the concatenation; cut it into pieces of L blocks; a
+  // unit's partitions are its parts of the pieces it meets, and piece j of kv
+  // head g is the work of one wave.
   std::vector<char>& sunit = S.sunit;
   sunit.assign(U, 0);
-  bool any_stream = false, any_other = V > 0;
+  int stream_cls = -1;
+  bool uniform = V == 0 && !tiles.empty();
   for (const Tile& t : tiles) {
-    const bool dec = t.seq < B && t.cls == 0;
-    sunit[t.seq] = dec;
-    any_stream = any_stream || dec;
-    any_other = any_other || !dec;
+    if (t.seq >= B || t.cls > 1 || (stream_cls >= 0 && t.cls != stream_cls)) uniform = false;
+    if (stream_cls < 0) stream_cls = t.cls;
+    sunit[t.seq] = 1;
   }
-  const bool stream = d->dtype == PMATTN_BF16 && d->num_kv_splits == 0 && any_stream && !any_other;
+  const bool stream = d->dtype == PMATTN_BF16 && d->num_kv_splits == 0 && uniform;
+  if (!stream) std::fill(sunit.begin(), sunit.end(), 0);
   std::vector<int64_t>& stream_start = S.stream_start;
   stream_start.assign(U, 0);
   int64_t stream_len = 0, stream_pieces = 0;
@@ -637,7 +646,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       if (sunit[u]) total += (unit_hi(u) - unit_lo(u) + kBlock - 1) / kBlock;
     }
     const int64_t cus = d->num_cus > 0 ? d->num_cus : 256;
-    const int64_t per_head = std::max<int64_t>(1, cus * kStreamWavesPerCu / hkv);
+    const int64_t per_head = std::max<int64_t>(1, cus * (stream_cls == 0 ? kStreamWavesPerCu : kStreamWavesPerCu32) / hkv);
     stream_len = std::max(kStreamMinBlocks, (total + per_head - 1) / per_head);
     stream_pieces = (total + stream_len - 1) / stream_len;
     for (int u = 0; u < U; ++u) {
@@ -1082,7 +1091,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       nstream += item_stream[at] = rstream[cd.range];
     };
     uint32_t nout = 0;
-    if (stream && c == 0) {
+    if (stream && c == stream_cls) {
       // Slot (g, j) is the run of tasks of kv head g inside piece j, in unit
       // order (each unit's partition p lies in piece start_u / len + p;
       // partitions start at piece boundaries or at the unit's first key, so

@@ -32,6 +32,11 @@ def _batch_cases():
         "decode-equal-work-long-and-short": (dict(hq=8, hkv=2, d=128),
                                              [S(q_len=1, seq_len=n) for n in (20000, 3, 17, 700, 1)], 0),
         "decode-equal-work-d64": (dict(hq=16, hkv=4, d=64), [S(q_len=1, seq_len=n) for n in (5000, 40, 333)], 0),
+        # equal-work plans of 32-row (verify) tasks: a long draft context cut
+        # into many pieces beside short ones; G = 8 at d = 64 (24 rows)
+        "verify-equal-work-long-and-short": (dict(hq=8, hkv=2, d=128),
+                                             [S(q_len=5, seq_len=n) for n in (12000, 6, 40, 700, 5)], 0),
+        "verify-equal-work-g8-d64": (dict(hq=16, hkv=2, d=64), [S(q_len=3, seq_len=n) for n in (3000, 50, 333)], 0),
         "prefill-unaligned": (dict(hq=8, hkv=2, d=128), [S(q_len=37, seq_len=42, q_start=5), S(q_len=100, seq_len=100),
                                                          S(q_len=64, seq_len=264, q_start=200)], 0),
         "prefill-d64-split2": (dict(hq=4, hkv=1, d=64), [S(q_len=70, seq_len=90, q_start=20), S(q_len=16, seq_len=16)], 2),

@@ -180,6 +180,32 @@ def test_equal_work_only_for_pure_auto_split_bf16_decode():
         assert make_plan(b).tables()["slot_begin"].size == 0
     b = wl.custom([dict(q_len=1, seq_len=n) for n in (300, 17, 1000)], hq=8, hkv=2, d=128, values=False)
     assert make_plan(b).tables()["slot_begin"].size > 0
+    # verify drafts alone (20 rows: the 32-row class) get the plan too
+    b = wl.custom([dict(q_len=5, seq_len=n) for n in (300, 17, 1000)], hq=8, hkv=2, d=128, values=False)
+    assert make_plan(b).tables()["slot_begin"].size > 0
+
+
+def test_equal_work_verify_slots():
+    """A batch of verify drafts only (32-row tasks): 4 waves per CU, each a
+    run of pieces of L blocks of one kv head, like the decode plan."""
+    rng = np.random.default_rng(3)
+    b = wl.custom([dict(q_len=5, seq_len=int(n)) for n in rng.integers(6, 4000, 32)], hq=32, hkv=8, d=128,
+                  seed=4, values=False)
+    t = make_plan(b).tables()
+    assert t["class_rows"].tolist() == [32]
+    sb, it = t["slot_begin"], t["items"]
+    nblk = -(-(np.asarray(b.q_start) + np.asarray(b.q_len)) // 16)
+    start = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    total = int(nblk.sum())
+    L = max(16, -(-total // max(1, 256 * 4 // b.num_kv_heads)))
+    assert sb.size - 1 == b.num_kv_heads * -(-total // L)
+    for w in range(sb.size - 1):
+        tk = it[sb[w]:sb[w + 1]]
+        assert len(set(tk[:, 1].tolist())) == 1
+        a = start[tk[:, 0]] + tk[:, 5] // 16
+        e = start[tk[:, 0]] + -(-tk[:, 6] // 16)
+        assert (a[1:] == e[:-1]).all() and a[0] % L == 0 and (e[-1] % L == 0 or e[-1] == total)
+    check_plan(b, make_plan(b))
 
 
 def test_dispatch_order_with_few_kv_heads_is_a_permutation():
