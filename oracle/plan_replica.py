@@ -27,7 +27,7 @@ MAX_WAVE_ROWS = 64
 MAX_TASK_ROWS = 128
 CLASS_ROWS = (16, 32, 64, 128)
 TASKS_PER_CU = 32
-WG_TASKS_PER_2CU = 2       # 1 workgroup task per CU ...
+WG_TASKS_PER_2CU = 3       # 1.5 workgroup tasks per CU ...
 WG_TASKS_PER_2CU_TREE = 3  # ... 1.5 when the plan holds a token tree
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
@@ -193,7 +193,7 @@ def num_splits(q_len, q_start, num_kv_heads, group, num_kv_splits=0, num_cus=0, 
     sequence with rows. Automatic: a task over n blocks costs n * (2 + rows/16)
     block units. Wave tasks (<= 64 rows) and workgroup tasks (128 rows) are
     balanced separately: each kind's quantum is its total cost over
-    (CUs x 32) wave tasks or (CUs x 1) workgroup tasks (CUs x 1.5 when
+    (CUs x 32) wave tasks or (CUs x 1.5) workgroup tasks (the same when
     ``tree``: some sequence is a token tree), at least 48 units; a
     sequence gets ceil(cost of its largest tile / its kind's quantum)
     partitions, at most 64 and at most its number of blocks."""

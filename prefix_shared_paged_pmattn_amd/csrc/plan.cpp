@@ -39,17 +39,16 @@ std::atomic<uint64_t> g_next_plan_id{1};
 // K/V stream of each block, the rows/16 term for its MFMA column tiles.
 int64_t unit_cost(int cls) { return 2 + kClassRows[cls] / 16; }
 // Automatic splitting aims at this many wave tasks per compute unit, and at
-// 1.5 workgroup tasks per compute unit (measured on MI355X against 1, 2 and 4:
-// fewer, longer workgroup tasks write fewer partials; 1.5 was 14% faster
-// than 4 on the shared-prompt cascade and 5% on tree verify, 1.5% slower on
-// the mixed batch) ...
+// 1.5 workgroup tasks per compute unit: fewer, longer workgroup tasks write
+// fewer partials, more of them shorten the tail. Measured on MI355X, step
+// time at 1 / 1.5 / 2 per CU: shared-prompt cascade (one kernel for its
+// virtual tiles and member decode tasks) 0.0983 / 0.0935 / 0.0959 ms, mixed
+// chunk batch 0.600 / 0.600 / 0.600 ms, token-tree verify 0.1569 /
+// 0.1514-0.1521 / 0.1488-0.1526 ms (3 and 4 per CU: 0.168 ms).
 constexpr int64_t kTasksPerCu = 32;
-constexpr int64_t kWgTasksPer2Cu = 2;
-// ... and 1.5 per CU when the plan holds token trees: their workgroup kernel
-// runs at 2 waves per SIMD instead of 3, and measured on MI355X the
-// token-tree workload took 0.161-0.163 ms at 1.5 per CU against 0.170-0.172
-// at 1, while the shared-prompt cascade took 0.1035-0.1038 ms at 1 against
-// 0.1084-0.1089 at 1.5 (mixed batch equal).
+constexpr int64_t kWgTasksPer2Cu = 3;
+// (token trees, whose workgroup kernel runs at 2 waves per SIMD instead of
+// 3, take the same count)
 constexpr int64_t kWgTasksPer2CuTree = 3;
 // Equal-work decode: a plan whose tasks are all 16-row wave tasks (decode
 // rows) with automatic splits gives each of kStreamWavesPerCu waves per CU an
