@@ -10,7 +10,7 @@
 // * or a bundle of four wave tasks of up to 32 rows (decode rows, verify
 //   drafts): each wave streams its own task's K/V into registers
 //   (task_wave.h; 32-row tasks in 16-key chunks to fit the registers).
-// Both bodies fit the same budget, 168 registers and 37 KiB of LDS, so three
+// Both bodies fit the same budget, 168 registers and 48 KiB of LDS, so three
 // workgroups of either kind share a CU. The planner interleaves the two kinds
 // in cost proportion within each XCD's share of the table; the dispatcher
 // hands entries to CUs in table order, so every CU holds both kinds while
@@ -27,7 +27,7 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_mixed_kernel(MixedArgs m) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[Cfg<D>::LDS_ELEMS];
   const AttnArgs& a = m.a;
   if ((int)blockIdx.x >= m.entries) return;  // uniform over the workgroup
   const int entry = ((cint_p)m.table)[blockIdx.x];

@@ -9,7 +9,7 @@ namespace {
 template <int D, bool TREE, int WAVES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES, WAVES)))
 void attn_prefill_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Cfg<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[Cfg<D>::LDS_ELEMS];
   if ((int)blockIdx.x >= a.item_count) return;  // uniform over the workgroup
   const pmattn_work_item it = load_item(a.items, blockIdx.x);
   wg_task<D, TREE>(a, it, a.q_row, lds);

@@ -9,9 +9,11 @@
 //
 // * 4 waves x 32 rows. All four share the kv head, so each 32-key chunk of
 //   K and V is gathered through the block table once per workgroup into LDS
-//   (double-buffered, one barrier per chunk) and read by every wave from
-//   there: the K/V concatenation the XY-Serve referee report blames for the
-//   baseline's prefix-reuse losses never happens.
+//   and read by every wave from there: the K/V concatenation the XY-Serve
+//   referee report blames for the baseline's prefix-reuse losses never
+//   happens. The gather is a three-stage ring of LDS-destination buffer
+//   loads: chunk c + 2 is in flight while chunk c is computed, one barrier per
+//   chunk, and no register or LDS-store instruction carries the data.
 // * S^T = K . Q^T and O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16. Each lane
 //   owns one query row (l % 32) and 16 keys of every 32-key score tile. The
 //   keys are permuted inside a tile (bits 2 and 3 of the slot swapped) so that
@@ -27,9 +29,9 @@
 //   v_permlane32_swap, the 16-score max eight v_maximum3.
 // * Row-wise causal masks ("Editorial extensions"): chunks wholly visible to
 //   every row of the task take an unmasked path (Figure 11, mask-aware
-//   computation); V lanes of keys past the task's end are zeroed when the chunk
-//   is staged, so pool slots no row can see may hold NaN.
-// * Occupancy is a template parameter: three waves per SIMD (168 VGPRs, 37
+//   computation); V slots of keys past the task's end are zeroed in LDS once
+//   that chunk has landed, so pool slots no row can see may hold NaN.
+// * Occupancy is a template parameter: three waves per SIMD (168 VGPRs, 48
 //   KiB of LDS per workgroup), so that LDS latency and one wave's softmax
 //   VALU hide behind the other waves' MFMA; two for token trees (whose masks
 //   spill at three). Beside one-wave tasks of the same plan the kernel keeps
@@ -37,12 +39,11 @@
 //   Measured: few-shot prefill 907 vs 813 TFLOP/s (3 vs 2), tree verify 2
 //   waves 19% faster. 64-key chunks at 2 waves were 3% slower than 32-key
 //   ones.
-// * The register staging of the next chunk uses clang vector types: with
-//   HIP's uint4 the copies are memcpys of a union, the staging array stays
-//   in private memory and the backend moves it to LDS, so every chunk's loads
-//   were waited for right after issue (15% of the few-shot time). Its loads
-//   are buffer loads with a scalar (block, kv head) base and one 32-bit lane
-//   offset shared by K and V: no 64-bit address arithmetic per chunk.
+// * Staging measured on MI355X (one session, few-shot prefill): the earlier
+//   register staging (global -> registers -> LDS, one chunk ahead) took 20%
+//   of the kernel's time (1.156 ms against 0.937 ms in a timing copy that
+//   skipped it; 1.022 ms skipping only its global loads). The LDS ring made
+//   the kernel 1.037 ms and the mixed batch 0.571 ms instead of 0.593-0.613.
 #pragma once
 
 #include <type_traits>
@@ -64,41 +65,19 @@ constexpr int kVAhead = 2;
 
 template <int D>
 struct Cfg {
-  static constexpr int CHUNK = 32;            // keys per iteration (CHUNK/16 blocks)
+  static constexpr int CHUNK = 32;            // keys per iteration (two blocks)
   static constexpr int NBLK = CHUNK / 16;
-  static constexpr int NTILE = CHUNK / 32;        // 32-key score tiles per chunk
   static constexpr int KSTEPS = D / 16;       // QK k-steps of 16 channels
   static constexpr int DT = D / 32;           // 32-channel output tiles
-  static constexpr int KROW = D + 8;          // LDS K row (bf16), +16 B pad: conflict-free reads
-  static constexpr int VROW = CHUNK + 8;      // LDS V row (bf16), +16 B pad
-  static constexpr int K_ELEMS = CHUNK * KROW;
-  static constexpr int STAGE = K_ELEMS + D * VROW;
-  static constexpr int PIECES = D * CHUNK / 2048;  // 16-byte pieces per thread for K (and for V)
+  static constexpr int BLK = 16 * D;          // elements of one (block, kv head) slice
+  static constexpr int K_ELEMS = NBLK * BLK;  // K of one chunk; V follows
+  static constexpr int STAGE = 2 * K_ELEMS;
+  static constexpr int NSTAGE = 3;            // chunks c, c + 1 and c + 2 in flight
+  static constexpr int LDS_ELEMS = NSTAGE * STAGE;
+  static constexpr int PB = 2 * BLK / 1024;   // 1 KiB pieces per slice
+  static constexpr int LOADS = NBLK * PB / 4; // 1 KiB loads of K (and of V) per wave and chunk
+  static constexpr int VMEM_PER_CHUNK = 2 * LOADS;
 };
-
-
-// Global -> register staging of one chunk (CHUNK / 16 blocks): thread `tid`
-// carries PIECES 16-byte pieces of K and of V; consecutive threads read
-// consecutive 16-byte pieces of a block, so every wave load is 1 KiB
-// contiguous.
-// (clang vector types, not HIP's uint4: copies of the latter are memcpys of a
-// union that keep the array in private memory, which the backend then moves
-// to LDS.)
-template <int D>
-struct Stage {
-  u32x4 k[Cfg<D>::PIECES];
-  u32x4 v[Cfg<D>::PIECES];
-};
-
-// blk[b] for a per-thread b, as selects (a dynamic index would put blk in
-// private memory)
-template <int N>
-__device__ __forceinline__ int pick(const int (&blk)[N], int b) {
-  int r = blk[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) r = b == i ? blk[i] : r;
-  return r;
-}
 
 // Buffer resource over one (block, kv head) slice of a pool: 16 tokens x D
 // channels of bf16; reads past its end return 0.
@@ -107,26 +86,54 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t* sli
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(slice), (short)0, 32 * D, 0x00020000);
 }
 
+// One wave load of 16 bytes per lane from a buffer into LDS: lane i's bytes
+// land at dst + 16 i (dst wave-uniform).
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint16_t* dst, uint32_t voff) {
+  typedef __attribute__((address_space(3))) void* lds_t;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t)dst, 16, voff, 0, 0, 0);
+}
+
+// Issues the loads of one chunk (two blocks of K and of V) straight into an
+// LDS stage (buffer loads with the LDS flag: no registers, no LDS stores).
+// A wave load moves 1 KiB of one slice and writes it to 1 KiB of LDS in lane
+// order, so the stage keeps the pool's block layouts: K grouped
+// [D/8][16][8] (the QK operand of 16 consecutive keys is 256 contiguous
+// bytes: no bank conflicts), V channel-major [D][16] with the two 16-byte
+// halves of a channel's 32 bytes swapped on odd groups of eight channels
+// (the lane filling LDS slot L reads global slot L ^ ((L >> 4) & 1)), so
+// that the PV operand reads of 16 channels fall on distinct banks.
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restrict__ kpool,
-                                           const uint16_t* __restrict__ vpool, const int (&blk)[Cfg<D>::NBLK],
-                                           int kvh, int hkv, int tid) {
-  constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;  // 16-byte pieces per block
-  static_assert(PER_BLOCK % 64 == 0, "a wave's pieces lie in one block");
-  __builtin_assume(tid >= 0 && tid < 256);
+__device__ __forceinline__ void stage_issue(uint16_t* stage, const uint16_t* __restrict__ kpool,
+                                            const uint16_t* __restrict__ vpool, const int (&blk)[Cfg<D>::NBLK],
+                                            int kvh, int hkv, int wave, int lane) {
+  constexpr int PB = Cfg<D>::PB, BLK = Cfg<D>::BLK;
+  static_assert(Cfg<D>::NBLK == 2 && PB * 2 % 4 == 0, "whole wave loads per chunk");
 #pragma unroll
-  for (int u = 0; u < P; ++u) {
-    const int q = tid + 256 * u;
-    // A wave's pieces all lie in one block (a scalar base), and the lane's
-    // byte offset in it, 16 * (q % PER_BLOCK), is the same for K (grouped
-    // [D/8][16][8]: channel group r / 16, token r % 16) and for V ([D][16]:
-    // channel r / 2, half r % 2).
-    const int b = __builtin_amdgcn_readfirstlane(q / PER_BLOCK);
-    const int64_t base = ((int64_t)pick(blk, b) * hkv + kvh) * 16 * D;
-    const uint32_t off = 16u * (uint32_t)(q % PER_BLOCK);
-    st.k[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(block_rsrc<D>(kpool + base), off, 0, 0));
-    st.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(block_rsrc<D>(vpool + base), off, 0, 0));
+  for (int u = 0; u < Cfg<D>::LOADS; ++u) {
+    const int gp = wave + 4 * u;  // wave-uniform
+    const int b = gp / PB, p = gp % PB;
+    const int64_t base = ((int64_t)(b ? blk[1] : blk[0]) * hkv + kvh) * 16 * D;
+    const uint32_t koff = 1024u * p + 16u * lane;
+    const uint32_t voff = 1024u * p + 16u * (lane ^ ((lane >> 4) & 1));
+    lds_load16(block_rsrc<D>(kpool + base), stage + b * BLK + 512 * p, koff);
+    lds_load16(block_rsrc<D>(vpool + base), stage + Cfg<D>::K_ELEMS + b * BLK + 512 * p, voff);
   }
+}
+
+// Waits until at most N of this wave's vector memory operations are in
+// flight (vmcnt; expcnt and lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that orders LDS accesses in the compiler but, unlike
+// __syncthreads, does not wait for the LDS loads still in flight.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Keeps the enclosing uniform branch a real branch: the compiler may not
@@ -134,33 +141,28 @@ __device__ __forceinline__ void stage_load(Stage<D>& st, const uint16_t* __restr
 // code runs only when its condition holds.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
 
-// Register -> LDS. In the chunk that holds the task's end, V pieces of keys
-// >= kv_end are zeroed first (chunks past the last block re-read the last
-// block; their keys are >= kv_end as well).
+// In the chunk that holds the task's end, zeroes the V slots of keys >=
+// kv_end in the landed stage (chunks past the last block re-read the last
+// block; their keys are >= kv_end as well), so that pool slots no row can
+// see may hold NaN: their weights are 0, and 0 * NaN would still be NaN.
 template <int D>
-__device__ __forceinline__ void stage_store(uint16_t* lds, Stage<D>& st, int c0, int kv_end, int tid) {
-  constexpr int P = Cfg<D>::PIECES, PER_BLOCK = 2 * D;
-  uint16_t* kl = lds;
-  uint16_t* vl = lds + Cfg<D>::K_ELEMS;
-  if (c0 + Cfg<D>::CHUNK > kv_end) {
-    keep_branch();
+__device__ __forceinline__ void zero_tail_v(uint16_t* stage, int c0, int kv_end, int tid) {
+  constexpr int SLOTS = 2 * Cfg<D>::BLK / 8, PER_BLK = Cfg<D>::BLK / 8;
+  uint16_t* vl = stage + Cfg<D>::K_ELEMS;
 #pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int q = tid + 256 * u;
-      const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-      const int nv = kv_end - (c0 + 16 * b + 8 * (r % 2));  // keys of this piece below kv_end
-      st.v[u].x &= (0 < nv ? 0xFFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
-      st.v[u].y &= (2 < nv ? 0xFFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
-      st.v[u].z &= (4 < nv ? 0xFFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u);
-      st.v[u].w &= (6 < nv ? 0xFFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u);
+  for (int s0 = 0; s0 < SLOTS; s0 += 256) {
+    const int sl = s0 + tid;
+    const int b = sl / PER_BLK, ws = sl % PER_BLK, ch = ws >> 1;
+    const int half = (ws & 1) ^ ((ch >> 3) & 1);
+    const int nv = kv_end - (c0 + 16 * b + 8 * half);  // keys of this slot below kv_end
+    if (nv < 8) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(vl + 8 * sl);
+      v.x &= (0 < nv ? 0xFFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u);
+      v.y &= (2 < nv ? 0xFFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u);
+      v.z &= (4 < nv ? 0xFFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u);
+      v.w &= (6 < nv ? 0xFFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u);
+      *reinterpret_cast<u32x4*>(vl + 8 * sl) = v;
     }
-  }
-#pragma unroll
-  for (int u = 0; u < P; ++u) {
-    const int q = tid + 256 * u;
-    const int b = q / PER_BLOCK, r = q % PER_BLOCK;
-    *reinterpret_cast<u32x4*>(kl + (16 * b + r % 16) * Cfg<D>::KROW + 8 * (r / 16)) = st.k[u];
-    *reinterpret_cast<u32x4*>(vl + (r / 2) * Cfg<D>::VROW + 16 * b + 8 * (r % 2)) = st.v[u];
   }
 }
 
@@ -197,24 +199,27 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
                                              bool mask, int lim, float sl2, int i32, int h,
                                              uint64_t rel, int dpos) {
   constexpr int KSTEPS = D / 16, DT = D / 32;
+  constexpr int BLK = Cfg<D>::BLK;
   const uint16_t* kl = lds;
   const uint16_t* vl = lds + Cfg<D>::K_ELEMS;
-  // A-operand row i32 holds key kappa(i32): slot bits 2 and 3 swapped
+  // A-operand row i32 holds key kappa(i32): slot bits 2 and 3 swapped. Its
+  // channels (D/2)h + 8st .. + 7 are channel group (D/16)h + st of the key's
+  // grouped K block: 16 bytes at group * 256 + token * 16.
   const int kap = (i32 & ~12) | ((i32 & 4) << 1) | ((i32 & 8) >> 1);
   f32x16 s = {};
-  const uint16_t* kr = kl + (32 * kt + kap) * Cfg<D>::KROW + (D / 2) * h;
+  const uint16_t* kr = kl + (kap >> 4) * BLK + (kap & 15) * 8 + (D / 16) * h * 128;
   // K operands rotate through kKAhead registers, each read that many MFMAs
   // before its use; the scheduling barriers pin the order (left alone, the
   // scheduler sinks every read next to its MFMA and waits out the LDS
   // latency each time)
   bf16x8 kq[kKAhead];
 #pragma unroll
-  for (int st = 0; st < kKAhead && st < KSTEPS; ++st) kq[st] = ld16(kr + 8 * st);
+  for (int st = 0; st < kKAhead && st < KSTEPS; ++st) kq[st] = ld16(kr + 128 * st);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < KSTEPS; ++st) {
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st % kKAhead], qop[st], s, 0, 0, 0);
-    if (st + kKAhead < KSTEPS) kq[st % kKAhead] = ld16(kr + 8 * (st + kKAhead));
+    if (st + kKAhead < KSTEPS) kq[st % kKAhead] = ld16(kr + 128 * (st + kKAhead));
     __builtin_amdgcn_sched_barrier(0);
   }
   if (mask) {
@@ -262,11 +267,13 @@ __device__ __forceinline__ void compute_tile(const uint16_t* lds, int kt, const 
   l_part += ps;
   const bf16x8 pb0 = __builtin_convertvector(p0, bf16x8);
   const bf16x8 pb1 = __builtin_convertvector(p1, bf16x8);
-  // V operands likewise, kVAhead deep: operand j (tile j / 2, keys 16 (j % 2)
-  // onwards) is read kVAhead MFMAs before its use
-  const uint16_t* vb = vl + i32 * Cfg<D>::VROW + 32 * kt + 8 * h;
+  // V operands likewise, kVAhead deep: operand j is keys 16 (j % 2) + 8h ..
+  // + 7 (block j % 2, tokens 8h ..) of channel 32 (j / 2) + i32, the 16-byte
+  // half h of the channel's 32 bytes, stored swapped on odd groups of eight
+  // channels; read kVAhead MFMAs before its use
+  const uint16_t* vb = vl + i32 * 16 + 8 * (h ^ ((i32 >> 3) & 1));
   constexpr int NV = 2 * DT;
-  auto vaddr = [&](int j) { return vb + (32 * (j >> 1)) * Cfg<D>::VROW + 16 * (j & 1); };
+  auto vaddr = [&](int j) { return vb + (j & 1) * BLK + (j >> 1) * 512; };
   bf16x8 vq[kVAhead];
 #pragma unroll
   for (int j = 0; j < kVAhead && j < NV; ++j) vq[j] = ld16(vaddr(j));
@@ -284,16 +291,14 @@ __device__ __forceinline__ void wg_chunk(const uint16_t* lds, const bf16x8 (&qop
                                               f32x16 (&o)[D / 32], RowRef& rr, float& l_part,
                                               bool mask, int lim, float sl2, int i32, int h,
                                               uint64_t rel, int dpos) {
-#pragma unroll
-  for (int kt = 0; kt < Cfg<D>::NTILE; ++kt)
-    compute_tile<D, TREE>(lds, kt, qop, o, rr, l_part, mask, lim, sl2, i32, h, rel, dpos);
+  compute_tile<D, TREE>(lds, 0, qop, o, rr, l_part, mask, lim, sl2, i32, h, rel, dpos);
 }
 
 // One task on the calling workgroup (all 256 threads call it, with the same
-// item). lds: 2 * Cfg<D>::STAGE elements of LDS, 16-byte aligned. q_row: null,
+// item). lds: Cfg<D>::LDS_ELEMS elements of LDS, 16-byte aligned. q_row: null,
 // or the table naming each task row's query row (virtual rows of cascade
-// tasks). Ends with every wave past the task's last barrier; the LDS may be
-// reused at once.
+// tasks). Waves may still read the LDS when they return: a caller reusing it
+// must meet at a barrier first.
 template <int D, bool TREE>
 __device__ __forceinline__ void wg_task(const AttnArgs& a, const pmattn_work_item& it, const int32_t* q_row,
                                         uint16_t* lds) {
@@ -350,37 +355,50 @@ __device__ __forceinline__ void wg_task(const AttnArgs& a, const pmattn_work_ite
     for (int b = 0; b < NBLK; ++b) blk[b] = bt_row[min(bi + b, last_blk)];
   };
 
-  Stage<D> stg;
+  // Chunk c lands in LDS stage c % 3. Step c waits for its own loads (chunk
+  // c + 1's may still be in flight), meets the other waves at a barrier
+  // (chunk c is then complete, and every wave is done with chunk c - 1), and
+  // issues chunk c + 2 into the stage chunk c - 1 left before computing.
+  constexpr int STAGE = Cfg<D>::STAGE;
   int blk[NBLK];
   int c0 = it.kv_begin;
-  chunk_blocks(c0, blk);
-  stage_load<D>(stg, kpool, vpool, blk, kvh, hkv, tid);
-  stage_store<D>(lds, stg, c0, kv_end, tid);
-  __syncthreads();
-  // one chunk out of LDS buffer B (0 or 1), staging the next into the other;
-  // the loop runs them in pairs, so every LDS address takes the buffer as an
-  // immediate offset instead of VALU work per chunk (measured on MI355X, one
-  // session: few-shot prefill +1.0-1.3%, token-tree verify +3-5%)
+  if (nch > 0) {
+    chunk_blocks(c0, blk);
+    stage_issue<D>(lds, kpool, vpool, blk, kvh, hkv, wave, lane);
+  }
+  if (nch > 1) {
+    chunk_blocks(c0 + CHUNK, blk);
+    stage_issue<D>(lds + STAGE, kpool, vpool, blk, kvh, hkv, wave, lane);
+  }
+  // the loop runs the three stages in turn, so every LDS address takes its
+  // stage as an immediate offset
   auto step = [&](auto buf, int c) {
     constexpr int B = decltype(buf)::value;
-    const bool more = c + 1 < nch;
-    if (more) {
-      chunk_blocks(c0 + CHUNK, blk);
-      stage_load<D>(stg, kpool, vpool, blk, kvh, hkv, tid);
+    if (c + 1 < nch) vm_wait<Cfg<D>::VMEM_PER_CHUNK>();
+    else vm_wait<0>();
+    stage_barrier();
+    if (c + 2 < nch) {
+      chunk_blocks(c0 + 2 * CHUNK, blk);
+      stage_issue<D>(lds + ((B + 2) % 3) * STAGE, kpool, vpool, blk, kvh, hkv, wave, lane);
     }
     issue_barrier();
+    if (c0 + CHUNK > kv_end) {
+      keep_branch();
+      zero_tail_v<D>(lds + B * STAGE, c0, kv_end, tid);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the zeroes are written
+      stage_barrier();
+    }
     // a chunk every row of the task sees whole needs no mask; in a token tree
     // that excludes the 64 keys before the task's first row
     const bool mask = c0 + CHUNK - 1 > min_pos - (TREE ? 64 : 0) || c0 + CHUNK > kv_end;
     if (wave_rows)
-      wg_chunk<D, TREE>(lds + B * Cfg<D>::STAGE, qop, o, rr, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
-    if (more) stage_store<D>(lds + (1 - B) * Cfg<D>::STAGE, stg, c0 + CHUNK, kv_end, tid);
-    __syncthreads();
+      wg_chunk<D, TREE>(lds + B * STAGE, qop, o, rr, l_part, mask, row_lim - c0, sl2, i32, h, rel, pos - c0);
     c0 += CHUNK;
   };
-  for (int c = 0; c < nch; c += 2) {
+  for (int c = 0; c < nch; c += 3) {
     step(std::integral_constant<int, 0>{}, c);
     if (c + 1 < nch) step(std::integral_constant<int, 1>{}, c + 1);
+    if (c + 2 < nch) step(std::integral_constant<int, 2>{}, c + 2);
   }
 
   // epilogue: lane (i32, h) owns channels 32t + 8q + 4h + (0..3) of its row
