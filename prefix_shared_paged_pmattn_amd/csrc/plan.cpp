@@ -75,8 +75,10 @@ constexpr int kMaxAutoSplits = 64;
 // Mixed-batch kernel: estimated duration per KV block (1/100 us) of a tile
 // of more than 64 rows, of a smaller workgroup task and of a 16-row wave task,
 // measured per table entry on MI355X (mixed-chunk workload, one session:
-// 0.72, 0.98 and 1.45 us)
-constexpr int64_t kMixTileBlockCost = 72;
+// 0.72, 0.98 and 1.45 us). With the LDS ring of the workgroup body the tiles
+// got faster; 0.56 for them measured best (0.573 against 0.577 ms per step,
+// 0.64: 0.575, 0.80: 0.573-0.577).
+constexpr int64_t kMixTileBlockCost = 56;
 constexpr int64_t kMixSmallTaskBlockCost = 98;
 constexpr int64_t kMixWaveBlockCost = 145;
 // ... and of a 17..32-row wave task (16-key chunks: twice the round trips
