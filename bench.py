@@ -49,10 +49,16 @@ def log(*a):
 
 # Workload -> (committed rocprofv3 counter summary, sources of the dominant
 # kernel and of the planner that shapes its work)
+_WAVE_SRC = ("attn_bf16.hip", "task_wave.h", "task_common.h", "plan.cpp")
+_WG_SRC = ("attn_prefill.hip", "task_wg.h", "task_common.h", "plan.cpp")
+_MIXED_SRC = ("attn_mixed.hip", "task_wave.h", "task_wg.h", "task_common.h", "plan.cpp")
 _TASK_KERNEL = {
-    2: ("attn_bf16_decode_64seq.md", ("attn_bf16.hip", "task_wave.h", "task_common.h", "plan.cpp")),
-    4: ("attn_mixed_chunk_144seq.md", ("attn_mixed.hip", "task_wave.h", "task_wg.h", "task_common.h",
-                                       "plan.cpp")),
+    2: ("attn_bf16_decode_64seq.md", _WAVE_SRC),
+    3: ("attn_prefill_fewshot_256x128.md", _WG_SRC),
+    4: ("attn_mixed_chunk_144seq.md", _MIXED_SRC),
+    5: ("attn_bf16_long_decode_8x32k.md", _WAVE_SRC),
+    6: ("attn_prefill_tree_verify_64x32.md", _WG_SRC),
+    7: ("cascade_shared_prompt_decode_128x8k.md", _MIXED_SRC),
 }
 
 
