@@ -72,18 +72,17 @@ constexpr int64_t kStreamMinBlocks = 16;
 // ... but never cuts a task below this many block units.
 constexpr int64_t kMinQuantum = 48;
 constexpr int kMaxAutoSplits = 64;
-// Mixed-batch kernel: estimated duration per KV block (1/100 us) of a tile
-// of more than 64 rows, of a smaller workgroup task and of a 16-row wave task,
-// measured per table entry on MI355X (mixed-chunk workload, one session:
-// 0.72, 0.98 and 1.45 us). With the LDS ring of the workgroup body the tiles
-// got faster; 0.56 for them measured best (0.573 against 0.577 ms per step,
-// 0.64: 0.575, 0.80: 0.573-0.577).
-constexpr int64_t kMixTileBlockCost = 56;
-constexpr int64_t kMixSmallTaskBlockCost = 98;
-constexpr int64_t kMixWaveBlockCost = 145;
-// ... and of a 17..32-row wave task (16-key chunks: twice the round trips
-// per key of a 16-row task; measured 3.36 us)
-constexpr int64_t kMixWave32BlockCost = 336;
+// Mixed-batch kernel: each stream of the table is consumed in proportion to
+// its own total of KV blocks (a bundle counts its longest task), so that the
+// streams end together. The stream of 17..32-row wave bundles runs this much
+// ahead (percent of its total): its smallest entries still last longer than
+// the other streams' last ones (16-key chunks; measured on MI355X per table
+// entry, mixed-chunk batch: about 3.9 us per block against 1.55 for 16-row
+// tasks and 0.67 for prefill tiles).
+constexpr int64_t kMixVerifyLead = 110;
+// (Measured on MI355X, mixed-chunk batch, one session, three runs each: lead
+// 100: 0.575 ms per step, 110: 0.568, 120: 0.569, 130: 0.571; leading the
+// 16-row bundles as well, 104 or 108, or letting them lag, 96 or 92: slower.)
 // Shader engines per XCD, which receive an XCD's workgroups in turn.
 constexpr int kSeRoundRobin = 4;
 // Automatic cascade: a shared run becomes a group only with this many members
@@ -1231,15 +1230,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
   // waves) or a bundle of four wave tasks (one per wave, each streaming its
   // own K/V). Per XCD (kv head g on XCD g, as for the class order, so that
   // readers of a block meet in one L2), both kinds are taken largest first and
-  // interleaved in proportion to their estimated cost, so that every CU holds
+  // interleaved in proportion to their KV blocks, so that every CU holds
   // some of each while they run (decode streams HBM beside MFMA-bound prefill
   // tiles; POD-Attention, XY-Serve review reference list) and both kinds end
   // together. Bundles hold four wave tasks of neighbouring cost.
   if (P.mixed) {
-    // estimated duration (1/100 us) in this kernel, per KV block: see
-    // kMix*BlockCost (a bundle lasts as long as its longest task)
-    static constexpr int64_t per_block[4] = {kMixTileBlockCost, kMixSmallTaskBlockCost, kMixWaveBlockCost,
-                                             kMixWave32BlockCost};
     auto nblk_of = [&](uint32_t i) { return (items[i].kv_end - items[i].kv_begin + kBlock - 1) / kBlock; };
     int64_t casc_from = 0;  // cascade classes come after the plain ones
     for (int c = 0; c < kNumClasses; ++c) casc_from += cls_items[c];
@@ -1336,7 +1331,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
         MixEntry* st = streams[k].data();
         if (k < 2) {
           for (size_t j = 0; j < m; ++j)
-            st[j] = MixEntry{v[j].nblk * per_block[k], 4 * v[j].item + 2 * is_cascade(v[j].item)};
+            st[j] = MixEntry{v[j].nblk, 4 * v[j].item + 2 * is_cascade(v[j].item)};
           continue;
         }
         // bundles of four wave tasks of neighbouring cost
@@ -1344,7 +1339,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           int32_t* slot = mix_bundles + (size_t)nbund * kWaveTasksPerWg;
           for (size_t q = j; q < j + kWaveTasksPerWg; ++q)
             slot[q - j] = q < m ? 2 * v[q].item + is_cascade(v[q].item) : -1;
-          st[j / kWaveTasksPerWg] = MixEntry{v[j].nblk * per_block[k], 4 * nbund + 1};  // the bundle's longest task
+          st[j / kWaveTasksPerWg] = MixEntry{v[j].nblk, 4 * nbund + 1};  // the bundle's longest task
           ++nbund;
         }
       }
@@ -1360,8 +1355,11 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
       lb[x] = cat.size();
       int64_t tot[4] = {0, 0, 0, 0}, used[4] = {0, 0, 0, 0};
       size_t h[4] = {0, 0, 0, 0};
-      for (int k = 0; k < 4; ++k)
+      for (int k = 0; k < 4; ++k) {
         for (const MixEntry& en : streams[k]) tot[k] += en.cost;
+        tot[k] *= k == 3 ? kMixVerifyLead : 100;
+        for (MixEntry& en : streams[k]) en.cost *= 100;
+      }
       // the share a stream has used, as a double: exact for the comparisons
       // while every total stays below 2^26 (two different shares then differ
       // by more than the rounding of either); larger totals compare exactly
