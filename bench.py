@@ -447,7 +447,9 @@ def main():
         """Plan (host time: median of 20) and time K steps; the workload's
         summary with its rate against its own bound."""
         plan_times = []
+        p = None
         for _ in range(20):
+            p = None  # the previous plan is released outside the timed region
             t0 = time.perf_counter()
             p = make_plan_for(b)
             plan_times.append(time.perf_counter() - t0)
