@@ -518,6 +518,9 @@ def main():
             f"({res['cpu_baseline']['sample']})")
         res["cpu_baseline"]["per_core"] = per_core_oracle()
         log(f"[bench] oracle at one thread: {res['cpu_baseline']['per_core']}")
+        if res["cpu_baseline"]["unit"] == res["unit"]:
+            # the GPU step's rate over the oracle's, in the same unit
+            res["cpu_baseline"]["gpu_ratio"] = res["value"] / res["cpu_baseline"]["value"]
     del t, p
     torch.cuda.empty_cache()
     if not args.no_configs:
