@@ -61,6 +61,13 @@ def _batch_cases():
         "prefill-wg-sparse-waves": (dict(hq=8, hkv=1, d=128), [S(q_len=17, seq_len=300, q_start=283),
                                                                  S(q_len=33, seq_len=33)], 0),
         "prefill-wg-d64-exact": (dict(hq=4, hkv=1, d=64), [S(q_len=64, seq_len=100, q_start=36)], 2),
+        # workgroup tasks of 1 to 5 chunks of 32 keys (the LDS ring's first
+        # and last steps), ending on and just past chunk edges, at both head
+        # dims, and with partitions that start inside the ring's reach
+        "prefill-wg-ring-lengths": (dict(hq=8, hkv=2, d=128), [S(q_len=40, seq_len=n, q_start=n - 40)
+                                                                for n in (40, 64, 65, 96, 97, 128, 129, 160)], 0),
+        "prefill-wg-ring-d64-splits": (dict(hq=8, hkv=2, d=64), [S(q_len=36, seq_len=n, q_start=n - 36)
+                                                                  for n in (36, 95, 161, 224)], 3),
         # wave and workgroup tasks in one plan (run concurrently on two streams)
         "mixed-classes": (dict(hq=8, hkv=2, d=128), [S(q_len=50, seq_len=300, q_start=250), S(q_len=1, seq_len=700),
                                                      S(q_len=5, seq_len=405), S(q_len=1, seq_len=33),
