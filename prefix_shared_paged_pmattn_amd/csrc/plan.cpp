@@ -224,7 +224,8 @@ struct VSeq {
   int32_t lo, hi, table_seq, row_begin, rows;
 };
 
-// A mixed-table stream entry: its estimated duration and table code.
+// A mixed-table stream entry: its weight (KV blocks; a bundle's longest task)
+// and table code.
 struct MixEntry {
   int64_t cost;
   int32_t e;
@@ -1343,7 +1344,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           ++nbund;
         }
       }
-      // Interleave in proportion to estimated duration (next comes the
+      // Interleave in proportion to KV blocks (next comes the
       // stream that has used the smallest share of its own total), in
       // groups of kSeRoundRobin entries of one stream and neighbouring cost.
       // Within an XCD the hardware deals workgroups to its shader engines
