@@ -1182,14 +1182,44 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
         std::vector<uint32_t>& srt = S.slot_key;
         srt.resize(nr);
         for (uint32_t k = 0; k < nr; ++k) srt[k] = rlist[order[k]];
-        deal(qb, qe, per_wg, [&](int x, size_t e) {
-          const uint32_t r = srt[e - qb[x]];
-          if (P.mixed) qi[e] = QItem{(int32_t)(pos + nout), ranges[r].nblk};
-          const Cand cd{r, (uint16_t)x, (uint16_t)x};
-          if (direct) emit(pos + nout, cd);
-          else outc[nout] = cd;
-          ++nout;
-        });
+        if (direct) {
+          // (emit, with the tables it reads held in locals: the stores into
+          // the image cannot alias them)
+          const pmattn_work_item* __restrict__ rt = rtask.data();
+          const Range* __restrict__ rg = ranges.data();
+          const char* __restrict__ rs = rstream.data();
+          const uint32_t* __restrict__ sr = srt.data();
+          pmattn_work_item* __restrict__ out = items + pos;
+          int32_t* __restrict__ ost = item_stream + pos;
+          const bool mixed = P.mixed;
+          auto put = [&](int x, size_t e, uint32_t r) {
+            pmattn_work_item it = rt[r];
+            it.kv_head = x;
+            if (it.part >= 0) it.part += x * rg[r].step;
+            out[nout] = it;
+            const int32_t st = rs[r];
+            ost[nout] = st;
+            nstream += st;
+            if (mixed) qi[e] = QItem{(int32_t)(pos + nout), rg[r].nblk};
+            ++nout;
+          };
+          if (nr % per_wg == 0) {
+            // the deal of equal queues in whole workgroups: round i gives
+            // every XCD in turn its queue's i-th workgroup of tasks
+            for (uint32_t i0 = 0; i0 < nr; i0 += per_wg)
+              for (int x = 0; x < kXcds; ++x)
+                for (uint32_t i = i0; i < i0 + per_wg; ++i) put(x, qb[x] + i, sr[i]);
+          } else {
+            deal(qb, qe, per_wg, [&](int x, size_t e) { put(x, e, sr[e - qb[x]]); });
+          }
+        } else {
+          deal(qb, qe, per_wg, [&](int x, size_t e) {
+            const uint32_t r = srt[e - qb[x]];
+            if (P.mixed) qi[e] = QItem{(int32_t)(pos + nout), ranges[r].nblk};
+            outc[nout] = Cand{r, (uint16_t)x, (uint16_t)x};
+            ++nout;
+          });
+        }
       } else {
         queue.resize(n);
         for (uint32_t a = 0, e; a < nr; a = e) {
