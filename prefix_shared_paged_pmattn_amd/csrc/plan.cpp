@@ -144,12 +144,21 @@ void counting_order(const uint32_t* key, uint32_t n, size_t nkeys, std::vector<u
 // each entry's queue and its index in the common array, in dispatch order.
 template <typename Emit>
 void deal(const size_t* beg, const size_t* end, int per_wg, Emit&& emit) {
-  size_t head[kXcds], total = 0, done = 0;
+  size_t head[kXcds], total = 0, done = 0, least = std::numeric_limits<size_t>::max();
   for (int x = 0; x < kXcds; ++x) {
     head[x] = beg[x];
     total += end[x] - beg[x];
+    least = std::min(least, end[x] - beg[x]);
   }
-  for (size_t slot = 0; done < total; ++slot) {
+  // rounds in which every XCD still has a whole workgroup of tasks: slot s
+  // takes per_wg tasks of XCD s % kXcds, no top-up (the general loop below
+  // does the same, one slot at a time)
+  const size_t rounds = least / (size_t)per_wg;
+  for (size_t r = 0; r < rounds; ++r)
+    for (int x = 0; x < kXcds; ++x)
+      for (int k = 0; k < per_wg; ++k) emit(x, head[x]++);
+  done = rounds * (size_t)per_wg * kXcds;
+  for (size_t slot = rounds * kXcds; done < total; ++slot) {
     int x = (int)(slot % kXcds);
     for (size_t take = std::min<size_t>(per_wg, total - done); take > 0;) {
       if (head[x] == end[x]) {
@@ -1203,15 +1212,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
             if (mixed) qi[e] = QItem{(int32_t)(pos + nout), rg[r].nblk};
             ++nout;
           };
-          if (nr % per_wg == 0) {
-            // the deal of equal queues in whole workgroups: round i gives
-            // every XCD in turn its queue's i-th workgroup of tasks
-            for (uint32_t i0 = 0; i0 < nr; i0 += per_wg)
-              for (int x = 0; x < kXcds; ++x)
-                for (uint32_t i = i0; i < i0 + per_wg; ++i) put(x, qb[x] + i, sr[i]);
-          } else {
-            deal(qb, qe, per_wg, [&](int x, size_t e) { put(x, e, sr[e - qb[x]]); });
-          }
+          deal(qb, qe, per_wg, [&](int x, size_t e) { put(x, e, sr[e - qb[x]]); });
         } else {
           deal(qb, qe, per_wg, [&](int x, size_t e) {
             const uint32_t r = srt[e - qb[x]];
