@@ -1004,12 +1004,13 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           rstream[st] = 0;
           m.state = kMultiBit | (seq_of_range(st) == who ? who : kSeqMulti);
         };
+        Mark* __restrict__ mk = marks.data();
         if (active.size() == 1) {
           const uint32_t rid = active[0];
           const int32_t tile = ranges[rid].tile;
           bool shared = false;
           for (int32_t j = p; j < q; ++j) {
-            Mark& m = marks[row[j]];
+            Mark& m = mk[row[j]];
             if (m.gen != gen) {
               m = Mark{gen, rid};
               continue;
@@ -1026,7 +1027,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           if (shared) rstream[rid] = 0;
         } else {
           for (int32_t j = p; j < q; ++j) {
-            Mark& m = marks[row[j]];
+            Mark& m = mk[row[j]];
             if (m.gen != gen) {
               m = Mark{gen, kMultiBit | who};
               continue;
