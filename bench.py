@@ -48,10 +48,10 @@ def log(*a):
 
 
 # Workload -> (committed rocprofv3 counter summary, sources of the dominant
-# kernel and of the planner that shapes its work)
-_WAVE_SRC = ("attn_bf16.hip", "task_wave.h", "task_common.h", "plan.cpp")
-_WG_SRC = ("attn_prefill.hip", "task_wg.h", "task_common.h", "plan.cpp")
-_MIXED_SRC = ("attn_mixed.hip", "task_wave.h", "task_wg.h", "task_common.h", "plan.cpp")
+# kernel). The work the kernel is given is pinned by the plan's tables.
+_WAVE_SRC = ("attn_bf16.hip", "task_wave.h", "task_common.h")
+_WG_SRC = ("attn_prefill.hip", "task_wg.h", "task_common.h")
+_MIXED_SRC = ("attn_mixed.hip", "task_wave.h", "task_wg.h", "task_common.h")
 _TASK_KERNEL = {
     2: ("attn_bf16_decode_64seq.md", _WAVE_SRC),
     3: ("attn_prefill_fewshot_256x128.md", _WG_SRC),
@@ -72,11 +72,26 @@ def kernel_source_hash(files):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config_idx):
+def plan_tables_hash(tabs):
+    """First 16 hex digits of the sha256 over the tables that define a plan's
+    kernel work: tasks, their streaming flags, merge rows, classes, the
+    equal-work slots and the mixed-batch table."""
+    import hashlib
+    h = hashlib.sha256()
+    for k in ("items", "item_stream", "merge_rows", "class_rows", "class_begin", "class_stream",
+              "slot_begin", "mix_table", "mix_bundles"):
+        v = tabs.get(k)
+        h.update(k.encode())
+        if v is not None:
+            h.update(np.ascontiguousarray(v).tobytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config_idx, tabs):
     """HBM bytes per launch of the tasks kernel from the committed rocprofv3
     counter summary (FETCH_SIZE and WRITE_SIZE, calibrated by a 1 GiB copy),
-    or None when there is none for this workload or the kernel's sources have
-    changed since the counters were taken."""
+    or None when there is none for this workload, or the kernel's sources or
+    the plan's tables differ from those the counters were taken with."""
     prof = _TASK_KERNEL.get(config_idx)
     if prof is None:
         return None
@@ -85,8 +100,10 @@ def measured_traffic(config_idx):
         sha = kernel_source_hash(prof[1])
     except OSError:
         return None
-    fields = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(("traffic_bytes", "kernel_source")))
-    if fields.get("kernel_source_sha256_16") != sha or "traffic_bytes_per_launch" not in fields:
+    fields = dict(l.split(": ", 1) for l in text.splitlines()
+                  if l.startswith(("traffic_bytes", "kernel_source", "plan_tables")))
+    if (fields.get("kernel_source_sha256_16") != sha or fields.get("plan_tables_sha256_16") != plan_tables_hash(tabs)
+            or "traffic_bytes_per_launch" not in fields):
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -479,7 +496,7 @@ def main():
         plain = (args.num_kv_splits is None and not args.num_cus and not args.work_shuffle_seed
                  and args.cascade == 2)
         roof = dict(bound=bound, achieved=achieved, peak=peak, unit=unit, frac=achieved / peak,
-                    traffic=measured_traffic(idx) if plain else None)
+                    traffic=measured_traffic(idx, tabs) if plain else None)
         res = dict(workload=b.name, ms_per_step=ms_step, tasks_ms=ms_task, merge_ms=statistics.mean(t_merge),
                    value=value, unit=unit, roofline=roof, frac_step=value / peak,
                    gbs=work["bytes"] / (ms_step * 1e-3) / 1e9, tflops=work["flop"] / (ms_step * 1e-3) / 1e12,
