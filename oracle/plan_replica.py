@@ -28,7 +28,7 @@ MAX_TASK_ROWS = 128
 CLASS_ROWS = (16, 32, 64, 128)
 TASKS_PER_CU = 32
 WG_TASKS_PER_2CU = 3       # 1.5 workgroup tasks per CU ...
-WG_TASKS_PER_2CU_TREE = 3  # ... 1.5 when the plan holds a token tree
+WG_TASKS_PER_2CU_TREE = 4  # ... 2 when the plan holds a token tree
 MIN_QUANTUM = 48
 MAX_AUTO_SPLITS = 64
 STREAM_WAVES_PER_CU = 3     # equal-work plans of 16-row tasks ...

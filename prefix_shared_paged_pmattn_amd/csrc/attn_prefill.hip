@@ -21,7 +21,7 @@ namespace {
 template <int D>
 void launch_d(const AttnArgs& a, hipStream_t st) {
   const dim3 grid(a.item_count), block(256);
-  if (a.row_mask) hipLaunchKernelGGL((attn_prefill_kernel<D, true, 2>), grid, block, 0, st, a);
+  if (a.row_mask) hipLaunchKernelGGL((attn_prefill_kernel<D, true, 3>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((attn_prefill_kernel<D, false, 3>), grid, block, 0, st, a);
 }
 }  // namespace

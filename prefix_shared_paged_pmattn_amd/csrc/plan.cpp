@@ -43,13 +43,15 @@ int64_t unit_cost(int cls) { return 2 + kClassRows[cls] / 16; }
 // fewer partials, more of them shorten the tail. Measured on MI355X, step
 // time at 1 / 1.5 / 2 per CU: shared-prompt cascade (one kernel for its
 // virtual tiles and member decode tasks) 0.0983 / 0.0935 / 0.0959 ms, mixed
-// chunk batch 0.600 / 0.600 / 0.600 ms, token-tree verify 0.1569 /
-// 0.1514-0.1521 / 0.1488-0.1526 ms (3 and 4 per CU: 0.168 ms).
+// chunk batch 0.600 / 0.600 / 0.600 ms.
 constexpr int64_t kTasksPerCu = 32;
 constexpr int64_t kWgTasksPer2Cu = 3;
-// (token trees, whose workgroup kernel runs at 2 waves per SIMD instead of
-// 3, take the same count)
-constexpr int64_t kWgTasksPer2CuTree = 3;
+// Token trees (no one-wave tasks beside them, and more rows visible per key
+// than a prefill tile's diagonal) take 2 per CU: measured on MI355X, token-tree
+// verify at 3 waves per SIMD, step ms at 1.5 / 2 / 3 per CU: 0.1497-0.1563 / 0.1489-0.1516 /
+// 0.1622-0.1633 (three sessions; the tasks pass 0.1358-0.1386 ms at 2 against
+// 0.1418-0.1466 at 1.5, the merge 3 us longer).
+constexpr int64_t kWgTasksPer2CuTree = 4;
 // Equal-work decode: a plan whose tasks are all 16-row wave tasks (decode
 // rows) with automatic splits gives each of kStreamWavesPerCu waves per CU an
 // equal run of KV blocks of one kv head, never shorter than kStreamMinBlocks.
@@ -1359,6 +1361,18 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           tmp.assign(v, v + m);
           for (size_t j = 0; j < m; ++j) v[j] = tmp[gord[j]];
           for (size_t j = 0; j < m; ++j) gid[items[v[j].item].seq] = -1;
+          // Within a sequence, tiles of equal cost by first key: the row tiles
+          // of one KV partition (a cascade prompt's virtual tiles, the tiles of
+          // one prefill chunk) start together and share its keys in the L2.
+          for (size_t j = 0, e; j < m; j = e) {
+            const int32_t s = items[v[j].item].seq;
+            for (e = j + 1; e < m && items[v[e].item].seq == s && v[e].nblk == v[j].nblk; ++e) {
+            }
+            if (e - j > 2)
+              std::stable_sort(v + j, v + e, [&](const QItem& x, const QItem& y) {
+                return items[x.item].kv_begin < items[y.item].kv_begin;
+              });
+          }
         }
         streams[k].resize(k < 2 ? m : (m + kWaveTasksPerWg - 1) / kWaveTasksPerWg);
         MixEntry* st = streams[k].data();

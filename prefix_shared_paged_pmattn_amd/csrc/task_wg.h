@@ -33,12 +33,16 @@
 //   that chunk has landed, so pool slots no row can see may hold NaN.
 // * Occupancy is a template parameter: three waves per SIMD (168 VGPRs, 48
 //   KiB of LDS per workgroup), so that LDS latency and one wave's softmax
-//   VALU hide behind the other waves' MFMA; two for token trees (whose masks
-//   spill at three). Beside one-wave tasks of the same plan the kernel keeps
-//   three, and those tasks are built to fit the same register share.
-//   Measured: few-shot prefill 907 vs 813 TFLOP/s (3 vs 2), tree verify 2
-//   waves 19% faster. 64-key chunks at 2 waves were 3% slower than 32-key
-//   ones.
+//   VALU hide behind the other waves' MFMA. Beside one-wave tasks of the
+//   same plan the kernel keeps three, and those tasks are built to fit the
+//   same register share. Measured: few-shot prefill 907 vs 813 TFLOP/s (3 vs
+//   2). Token trees run at three as well: with the LDS ring their mask code
+//   fits 168 registers but for one value parked in scratch across the chunk
+//   loop (one store before it, one load after), and run as fast as at two
+//   waves with the same plan and 3.5% faster with more, shorter tasks (with
+//   register staging, before the ring, their masks spilled inside the loop
+//   and two waves were 19% faster). 64-key
+//   chunks at 2 waves were 3% slower than 32-key ones.
 // * Staging measured on MI355X (one session, few-shot prefill): the earlier
 //   register staging (global -> registers -> LDS, one chunk ahead) took 20%
 //   of the kernel's time (1.156 ms against 0.937 ms in a timing copy that
