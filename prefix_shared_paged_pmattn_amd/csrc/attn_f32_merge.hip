@@ -91,7 +91,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// The group kernel (below) takes its partials kGroupBatch at a time; the
+// launcher gives it every merge of at most kGroupBatch partials per output,
+// and any merge whose outputs average at most kGroupMeanParts.
 constexpr int kGroupBatch = 8;
+constexpr int kGroupMeanParts = 12;
 
 // Log-sum-exp merge of partial results (Flash-Decoding, reference list of the
 // XY-Serve pith review): out = sum_p w_p O_p / sum_p w_p with
@@ -318,8 +322,12 @@ hipError_t launch_merge(int head_dim, int out_dtype, const MergeArgs& a, hipStre
   const bool bf = out_dtype == PMATTN_BF16;
   // Measured on MI355X: the group kernel takes 20 us where the wave kernel
   // takes 47 (54k outputs of 1-3 partials); with tens of partials per output
-  // the wave kernel's lane-parallel lse loads win (25 vs 22 us).
-  if (a.max_parts <= kGroupBatch) {
+  // the wave kernel's lane-parallel lse loads win (25 vs 22 us). In between,
+  // the mean count decides: 8,192 outputs of 2-17 partials (mean 9.1) merge
+  // in 14.5-14.8 us by groups against 16.5 by waves; 4,096 of 13-16 listed
+  // partials (mean 14.8) in 12.1-12.3 against 11.2-11.9, and 512 of 16 in 8.2
+  // against 7.4.
+  if (a.max_parts <= kGroupBatch || a.total_parts <= (int64_t)kGroupMeanParts * a.count) {
     const dim3 grid((a.count + 15) / 16), block(256);
     if (head_dim == 128) {
       if (bf) hipLaunchKernelGGL((merge_group_kernel<128, true>), grid, block, 0, st, a);

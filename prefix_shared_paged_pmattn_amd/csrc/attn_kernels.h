@@ -63,6 +63,7 @@ struct MergeArgs {
   int32_t implicit_parts;        // implicit layout: P
   int32_t implicit_rows;         // implicit layout: rows
   int32_t max_parts;             // largest partial count of any output (kernel choice)
+  int64_t total_parts;           // partials over all outputs (kernel choice)
 };
 
 struct AppendArgs {

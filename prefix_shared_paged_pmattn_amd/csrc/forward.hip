@@ -183,6 +183,7 @@ pmattn_status run_merge(pmattn_plan_t plan, void* out, float* lse, void* workspa
   m.implicit_parts = 0;
   m.implicit_rows = 0;
   m.max_parts = P.merge_max_parts;
+  m.total_parts = P.merge_total_parts;
   hipError_t e = launch_merge(P.head_dim, P.dtype, m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return PMATTN_OK;
@@ -293,6 +294,7 @@ pmattn_status pmattn_merge_lse(int32_t num_parts, int32_t num_rows, int32_t num_
   m.implicit_parts = num_parts;
   m.implicit_rows = num_rows;
   m.max_parts = num_parts;
+  m.total_parts = (int64_t)num_parts * m.count;
   hipError_t e = launch_merge(head_dim, out_dtype, m, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return PMATTN_OK;

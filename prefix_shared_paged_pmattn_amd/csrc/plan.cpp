@@ -856,6 +856,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
     listed.clear();
     int64_t nm = 0;
     P.merge_max_parts = 0;
+    P.merge_total_parts = 0;
     for (const Tile& t : tiles) {
       if (!t.k) continue;
       const int u = t.seq;
@@ -869,7 +870,10 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
             for (int i = 0; i < G; ++i, ++m)
               merge[nm++] = pmattn_merge_row{(int32_t)(rec_base + m), trows, t.k, t.row0 + tok, g * G + i};
       }
-      if (!lst && t.k > 1) P.merge_max_parts = std::max(P.merge_max_parts, t.k);
+      if (!lst && t.k > 1) {
+        P.merge_max_parts = std::max(P.merge_max_parts, t.k);
+        P.merge_total_parts += (int64_t)t.k * trows * hkv;
+      }
     }
     if (n_member_rows > 0) {
       // key of (member row, q head): member_slot * Hq + head; each listed
@@ -887,6 +891,7 @@ static pmattn_status build_plan(const pmattn_plan_desc* d, Plan& P) {
           for (int i = 0; i < G; ++i) c[i] += lb.parts;
         }
       for (size_t k = 0; k < keys; ++k) start[k + 1] += start[k];
+      P.merge_total_parts += start[keys];
       std::vector<int32_t>& fill = S.rec_fill;
       fill.assign(start.begin(), start.end() - 1);
       for (const Listed& lb : listed)

@@ -61,6 +61,7 @@ struct Plan {
   // kernel reads the per-task flags, item_stream)
   std::vector<int32_t> class_stream;
   int32_t merge_max_parts = 0;  // largest nparts of any merge row
+  int64_t merge_total_parts = 0;  // sum of nparts over the merge rows
   int32_t slot_class = -1;      // the class slot_begin belongs to
   int32_t num_records = 0;
   // Mixed-batch kernel (bf16 plans without token trees holding both 16-row
