@@ -291,7 +291,7 @@ def test_empty_plan_launches_nothing():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("P", [2, 5, 8, 9, 100])  # group kernel up to 8 partials, wave kernel above
+@pytest.mark.parametrize("P", [2, 5, 8, 9, 12, 13, 100])  # group kernel up to 12 partials (one batch up to 8), wave kernel above
 def test_merge_lse_standalone(d, out_dtype, P):
     import torch
     rng = np.random.Generator(np.random.PCG64(d + P))
