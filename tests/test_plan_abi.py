@@ -581,6 +581,26 @@ def test_mixed_table_covers_every_item_once(cfg, cascade):
     _check_mixed_table(t)
 
 
+def test_mixed_table_tiles_of_one_partition_together():
+    """Shared-prompt cascade: on each XCD (table position mod 8) the virtual
+    tiles of one prompt partition sit side by side, partitions in key order, so
+    that the tiles reading the same keys start together."""
+    b = wl.config(7, values=False)
+    t = make_plan(b, cascade=2).tables()
+    items, table = t["items"], t["mix_table"]
+    for x in range(8):
+        wg = [items[e >> 2] for e in table[x::8] if not e & 1]
+        assert len(wg) > 8
+        keys = [(int(it[0]), int(it[6] - it[5]), int(it[5])) for it in wg]  # (seq, keys, first key)
+        for a, c in zip(keys, keys[1:]):
+            if a[:2] == c[:2]:
+                assert a[2] <= c[2]
+        # the first partition's tiles lead: the same first key, different row tiles
+        first = [it for it in wg if int(it[5]) == int(wg[0][5]) and int(it[6]) == int(wg[0][6])]
+        assert len(first) >= 2 and len({int(it[2]) for it in first}) == len(first)
+        assert all(int(it[5]) == int(wg[0][5]) for it in wg[:len(first)])
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_mixed_table_random_batches(seed):
     rng = np.random.Generator(np.random.PCG64(400 + seed))
